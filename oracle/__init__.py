@@ -1,0 +1,6 @@
+"""CPU oracle of the ODA decode step (test infrastructure only).
+
+Only tests/, __graft_entry__.smoke() and the cpu_baseline leg of bench.py may
+import this package.  The product path never does.
+"""
+from .oda_oracle import *  # noqa: F401,F403

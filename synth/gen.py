@@ -1,0 +1,378 @@
+"""Seeded synthetic inputs for the On-Demand Attention decode step.
+
+This module is the one source of inputs shared by the CPU oracle and the HIP
+path.  It holds none of the method's arithmetic: it only turns
+(seed, tag, logical index) into bf16 / float values, and describes the shapes
+of the synthetic workloads (lengths, needle positions, head-weight init,
+forced flags, paged block tables).
+
+Generator G
+-----------
+* ``splitmix64`` is Vigna's public-domain mixer (the SplitMix64 output
+  function): add the golden gamma 0x9E3779B97F4A7C15, then two xor-shift /
+  multiply rounds (constants 0xBF58476D1CE4E5B9, 0x94D049BB133111EB) and a
+  final xor-shift.
+* Stream key: ``key = splitmix64(seed * 256 + tag)``.
+* One 64-bit hash feeds two values: ``h = splitmix64(key + (idx >> 1))`` and
+  value ``idx`` takes the 32-bit half ``(h >> (32 * (idx & 1))) & 0xFFFFFFFF``.
+* bf16 value of a 32-bit word w: ``x = sum of its four bytes - 510`` (an
+  integer in [-510, 510]; mean 0, variance 4 * (256**2 - 1) / 12 = 21845),
+  ``v = float32(x) * VALUE_SCALE`` with ``VALUE_SCALE = float32(1/sqrt(21845))``
+  (one IEEE multiply, no fused op), then round-to-nearest-even to bf16.
+  The result has unit variance and support of about +-3.45.
+* Uniform doubles (head weights, lengths, Bernoulli draws) use the whole hash:
+  ``u = (splitmix64(key + idx) >> 11) * 2**-53``.
+
+The device-side fill kernels in ``synth/csrc/fill.hip`` implement the same
+definition and are checked against this file bit for bit.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_U64 = np.uint64
+GAMMA = 0x9E3779B97F4A7C15
+MIX1 = 0xBF58476D1CE4E5B9
+MIX2 = 0x94D049BB133111EB
+MASK64 = (1 << 64) - 1
+
+VALUE_SCALE = np.float32(1.0 / math.sqrt(21845.0))  # 0x3BDDB4E6 bit pattern below
+assert VALUE_SCALE.view(np.uint32) == np.uint32(1004385350)
+
+# Stream tags.
+TAG_K, TAG_V = 1, 2            # KV cache contents
+TAG_QL, TAG_QF = 3, 4          # per-step attention queries, local / full branch
+TAG_KL, TAG_VL = 5, 6          # per-step staged current k, v (local branch)
+TAG_KF, TAG_VF = 7, 8          # per-step staged current k, v (full branch)
+TAG_E, TAG_H0 = 9, 10          # current-token embedding, initial previous hidden state
+TAG_NEEDLE = 11                # needle sign patterns
+TAG_HEAD = 12                  # recall-head weights
+TAG_LEN = 13                   # ragged context lengths
+TAG_BERN = 14                  # Bernoulli forced flags
+TAG_SHUF = 15                  # paged block shuffle
+
+MAX_B = 32          # logical batch stride of the index space
+POS_BITS = 18       # logical position stride 2**18
+NEEDLE_SCALE_BITS = np.uint16(0x3FC0)  # bf16 of +1.5
+NEEDLE_NEG_BITS = np.uint16(0xBFC0)    # bf16 of -1.5
+
+
+# --------------------------------------------------------------------------
+# generator core
+# --------------------------------------------------------------------------
+def splitmix64(z: np.ndarray) -> np.ndarray:
+    """SplitMix64 output function on a uint64 array (wrapping arithmetic)."""
+    z = np.asarray(z, dtype=_U64)
+    with np.errstate(over="ignore"):
+        z = z + _U64(GAMMA)
+        z = (z ^ (z >> _U64(30))) * _U64(MIX1)
+        z = (z ^ (z >> _U64(27))) * _U64(MIX2)
+    return z ^ (z >> _U64(31))
+
+
+def splitmix64_int(z: int) -> int:
+    z = (z + GAMMA) & MASK64
+    z = ((z ^ (z >> 30)) * MIX1) & MASK64
+    z = ((z ^ (z >> 27)) * MIX2) & MASK64
+    return z ^ (z >> 31)
+
+
+def stream_key(seed: int, tag: int) -> int:
+    return splitmix64_int((seed * 256 + tag) & MASK64)
+
+
+def hash_at(seed: int, tag: int, idx) -> np.ndarray:
+    key = _U64(stream_key(seed, tag))
+    idx = np.asarray(idx, dtype=_U64)
+    with np.errstate(over="ignore"):
+        return splitmix64(key + idx)
+
+
+def word32_at(seed: int, tag: int, idx) -> np.ndarray:
+    idx = np.asarray(idx, dtype=_U64)
+    h = hash_at(seed, tag, idx >> _U64(1))
+    shift = (idx & _U64(1)) * _U64(32)
+    return ((h >> shift) & _U64(0xFFFFFFFF)).astype(np.uint32)
+
+
+def f32_to_bf16_rne(v: np.ndarray) -> np.ndarray:
+    """Round finite float32 values to bf16 bits, nearest-even."""
+    u = np.asarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    bias = _U64(0x7FFF) + ((u >> _U64(16)) & _U64(1))
+    return ((u + bias) >> _U64(16)).astype(np.uint16)
+
+
+def bf16_at(seed: int, tag: int, idx) -> np.ndarray:
+    """bf16 bits of G(seed, tag, idx) for an array of logical indices."""
+    w = word32_at(seed, tag, idx)
+    x = ((w & 0xFF) + ((w >> 8) & 0xFF) + ((w >> 16) & 0xFF) + (w >> 24)).astype(np.int32) - 510
+    v = x.astype(np.float32) * VALUE_SCALE
+    return f32_to_bf16_rne(v)
+
+
+def uniform_at(seed: int, tag: int, idx) -> np.ndarray:
+    h = hash_at(seed, tag, idx)
+    return (h >> _U64(11)).astype(np.float64) * (2.0 ** -53)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+# --------------------------------------------------------------------------
+# workloads
+# --------------------------------------------------------------------------
+@dataclasses.dataclass
+class Workload:
+    """Shape and structure of one synthetic decode workload.
+
+    ``t0[b]`` is the committed length of sequence b before the first routed
+    step; step j (0-based) decodes the token at 0-based position t0[b] + j.
+    """
+    name: str
+    layers: int
+    hq: int
+    hkv: int
+    head_dim: int
+    batch: int
+    t0: np.ndarray
+    steps: int
+    seed: int
+    head_seed: int
+    layout: str = "contig"           # "contig" | "paged"
+    block_size: int = 16
+    needles: Tuple[int, ...] = ()
+    sink: int = 4
+    window: int = 2048
+    rate: Optional[float] = None     # target full-branch rate when theta is tuned
+    theta: float = 0.0               # threshold when not tuned
+    bernoulli_odd: Optional[float] = None  # odd sequences forced by Bernoulli(p)
+    t_cap_slack: int = 256
+
+    @property
+    def hidden(self) -> int:
+        return self.hq * self.head_dim
+
+    @property
+    def t_cap(self) -> int:
+        """Per-sequence capacity for the contiguous layout."""
+        return int(np.max(self.t0)) + self.steps + self.t_cap_slack
+
+    def kv_bytes(self) -> int:
+        tok = int(np.sum(self.t0 + self.steps + self.t_cap_slack))
+        return self.layers * tok * self.hkv * self.head_dim * 2 * 2
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+def log_uniform_lengths(seed: int, batch: int, lo: int, hi: int) -> np.ndarray:
+    u = uniform_at(seed, TAG_LEN, np.arange(batch))
+    return np.rint(np.exp(np.log(lo) + u * (np.log(hi) - np.log(lo)))).astype(np.int64)
+
+
+def workloads() -> dict:
+    """The five synthetic workloads, keyed by number (plus "5-4k")."""
+    w = {}
+    w[1] = Workload("tiny-1layer-4k", 1, 16, 8, 128, 1, np.full(1, 4096), 64, seed=1,
+                    head_seed=101, needles=(100, 500, 900), theta=0.0)
+    w[2] = Workload("qwen3-1.7b-16k-b8", 28, 16, 8, 128, 8, np.full(8, 16384), 256, seed=2,
+                    head_seed=102, rate=0.416)
+    w[3] = Workload("qwen3-1.7b-128k-b4", 28, 16, 8, 128, 4, np.full(4, 131072), 128, seed=3,
+                    head_seed=103, needles=(32768, 65536, 98304), rate=0.125)
+    w[4] = Workload("qwen3-8b-64k-b16", 36, 32, 8, 128, 16, np.full(16, 65536), 128, seed=4,
+                    head_seed=104, rate=0.47)
+    w[5] = Workload("ragged-paged-b32", 28, 16, 8, 128, 32,
+                    log_uniform_lengths(5, 32, 4096, 131072), 64, seed=5, head_seed=105,
+                    layout="paged", theta=0.0, bernoulli_odd=0.3, t_cap_slack=16)
+    w["5-4k"] = Workload("paged-4k-b32", 28, 16, 8, 128, 32, np.full(32, 4096), 64, seed=6,
+                         head_seed=106, layout="paged", theta=0.0, t_cap_slack=16)
+    return w
+
+
+# --------------------------------------------------------------------------
+# logical indices
+# --------------------------------------------------------------------------
+def cache_index(l, b, g, p, i, hkv: int, d: int):
+    l, b, g, p, i = (np.asarray(a, dtype=np.uint64) for a in (l, b, g, p, i))
+    return ((((l * _U64(MAX_B) + b) * _U64(hkv) + g) << _U64(POS_BITS)) + p) * _U64(d) + i
+
+
+def step_index(j, l, b, h, i, layers: int, heads: int, d: int):
+    j, l, b, h, i = (np.asarray(a, dtype=np.uint64) for a in (j, l, b, h, i))
+    return ((((j * _U64(layers) + l) * _U64(MAX_B) + b) * _U64(heads) + h) * _U64(d)) + i
+
+
+def emb_index(j, b, i, hidden: int):
+    j, b, i = (np.asarray(a, dtype=np.uint64) for a in (j, b, i))
+    return (j * _U64(MAX_B) + b) * _U64(hidden) + i
+
+
+# --------------------------------------------------------------------------
+# tensors
+# --------------------------------------------------------------------------
+def needle_signs(seed: int, n: int, d: int) -> np.ndarray:
+    """+-1 pattern of needle n (bit 0 of tag-11 words)."""
+    w = word32_at(seed, TAG_NEEDLE, np.arange(n * d, (n + 1) * d))
+    return np.where((w & 1) == 1, 1, -1).astype(np.int8)
+
+
+def needle_bits(seed: int, n: int, d: int) -> np.ndarray:
+    return np.where(needle_signs(seed, n, d) > 0, NEEDLE_SCALE_BITS, NEEDLE_NEG_BITS).astype(np.uint16)
+
+
+def cache_rows(wl: Workload, tag: int, l: int, b: int, g: int, p0: int, p1: int) -> np.ndarray:
+    """bf16 bits [p1-p0][d] of the initial cache (K if tag==TAG_K else V)
+    for logical positions [p0, p1).  Needle rows override K."""
+    d = wl.head_dim
+    p = np.arange(p0, p1, dtype=np.uint64)[:, None]
+    i = np.arange(d, dtype=np.uint64)[None, :]
+    out = bf16_at(wl.seed, tag, cache_index(l, b, g, p, i, wl.hkv, d))
+    if tag == TAG_K:
+        for n, pn in enumerate(wl.needles):
+            if p0 <= pn < p1:
+                out[pn - p0] = needle_bits(wl.seed, n, d)
+    return out
+
+
+def aligned_needle(wl: Workload, j: int) -> Optional[int]:
+    """Needle targeted by every query at step j, or None."""
+    if wl.needles and j % 8 == 0:
+        return (j // 8) % len(wl.needles)
+    return None
+
+
+_STEP_TAGS = {"qL": TAG_QL, "qF": TAG_QF, "kL": TAG_KL, "vL": TAG_VL, "kF": TAG_KF, "vF": TAG_VF}
+_LAYER0_ALIAS = {"qF": "qL", "kF": "kL", "vF": "vL"}
+
+
+def step_tensor(wl: Workload, which: str, j: int, l: int) -> np.ndarray:
+    """bf16 bits [B][H][d] of a per-step input for layer l.
+
+    which: qL / qF (H = hq) or kL / vL / kF / vF (H = hkv).  Layer 0 takes the
+    same values for both branches (same pre-step state and token embedding);
+    at aligned steps every query equals 1.5 * the targeted needle pattern."""
+    if l == 0 and which in _LAYER0_ALIAS:
+        which = _LAYER0_ALIAS[which]
+    heads = wl.hq if which.startswith("q") else wl.hkv
+    d = wl.head_dim
+    b = np.arange(wl.batch, dtype=np.uint64)[:, None, None]
+    h = np.arange(heads, dtype=np.uint64)[None, :, None]
+    i = np.arange(d, dtype=np.uint64)[None, None, :]
+    out = bf16_at(wl.seed, _STEP_TAGS[which], step_index(j, l, b, h, i, wl.layers, heads, d))
+    n = aligned_needle(wl, j)
+    if which.startswith("q") and n is not None:
+        out[:] = needle_bits(wl.seed, n, d)[None, None, :]
+    return out
+
+
+def step_tensor_all_layers(wl: Workload, which: str, j: int) -> np.ndarray:
+    return np.stack([step_tensor(wl, which, j, l) for l in range(wl.layers)])
+
+
+def embedding(wl: Workload, j: int) -> np.ndarray:
+    D = wl.hidden
+    b = np.arange(wl.batch, dtype=np.uint64)[:, None]
+    i = np.arange(D, dtype=np.uint64)[None, :]
+    return bf16_at(wl.seed, TAG_E, emb_index(j, b, i, D))
+
+
+def h_prev0(wl: Workload) -> np.ndarray:
+    D = wl.hidden
+    b = np.arange(wl.batch, dtype=np.uint64)[:, None]
+    i = np.arange(D, dtype=np.uint64)[None, :]
+    return bf16_at(wl.seed, TAG_H0, b * _U64(D) + i)
+
+
+def bernoulli_force(wl: Workload, j: int) -> np.ndarray:
+    """int8 force vector for step j: -1 = decided by the head, 0/1 = forced."""
+    force = np.full(wl.batch, -1, dtype=np.int8)
+    if wl.bernoulli_odd is not None:
+        odd = np.arange(1, wl.batch, 2)
+        u = uniform_at(wl.seed, TAG_BERN, j * MAX_B + odd)
+        force[odd] = (u < wl.bernoulli_odd).astype(np.int8)
+    return force
+
+
+def forced_rate_flags(seed: int, steps: int, batch: int, rate: float) -> np.ndarray:
+    """[steps][B] int8 forced flags with an exact count round(rate*steps*batch),
+    placed by the order of tag-14 uniforms (used for controlled-rate sweeps)."""
+    n = steps * batch
+    k = int(round(rate * n))
+    u = uniform_at(seed, TAG_BERN, np.arange(n) + 7919)
+    order = np.argsort(u, kind="stable")
+    flags = np.zeros(n, dtype=np.int8)
+    flags[order[:k]] = 1
+    return flags.reshape(steps, batch)
+
+
+# --------------------------------------------------------------------------
+# paged layout
+# --------------------------------------------------------------------------
+def paged_block_tables(wl: Workload) -> Tuple[np.ndarray, int]:
+    """Per-sequence block tables [B][MB] int32 over a shuffled physical pool.
+
+    Each sequence owns ceil((t0 + steps + slack) / block) blocks; the physical
+    ids are a seeded permutation of the pool, so logical neighbours are
+    scattered.  Unused table entries hold -1."""
+    bs = wl.block_size
+    need = [(int(t) + wl.steps + wl.t_cap_slack + bs - 1) // bs for t in wl.t0]
+    nb = int(sum(need))
+    mb = int(max(need))
+    perm = np.argsort(hash_at(wl.seed, TAG_SHUF, np.arange(nb)), kind="stable").astype(np.int32)
+    tables = np.full((wl.batch, mb), -1, dtype=np.int32)
+    at = 0
+    for b, n in enumerate(need):
+        tables[b, :n] = perm[at:at + n]
+        at += n
+    return tables, nb
+
+
+# --------------------------------------------------------------------------
+# recall-head weights (fp32 blob)
+# --------------------------------------------------------------------------
+def head_tensor_shapes(hidden: int, tower: int = 1024, ffn: int = 2048) -> Sequence[Tuple[str, tuple, str]]:
+    """(name, shape, init) of each packed tensor, in blob order.
+
+    init: "xavier" (uniform +-sqrt(6/(fan_in+fan_out))), "zero" (bias) or
+    "one" (norm gain)."""
+    t, f, D = tower, ffn, hidden
+    out = []
+    for s in ("H", "E", "L"):
+        out += [(f"gamma_{s}", (D,), "one"), (f"W_{s}", (t, D), "xavier"), (f"c_{s}", (t,), "zero")]
+    out += [("W_I", (t, 9 * t), "xavier"), ("c_I", (t,), "zero")]
+    for k in (1, 2):
+        out += [(f"gamma_{k}", (t,), "one"), (f"Wg_{k}", (f, t), "xavier"),
+                (f"Wu_{k}", (f, t), "xavier"), (f"Wd_{k}", (t, f), "xavier")]
+    out += [("gamma_o", (t,), "one"), ("w_o", (1, t), "xavier"), ("c_o", (1,), "zero")]
+    return out
+
+
+def head_blob(hidden: int, seed: int, perturb: bool = False, tower: int = 1024,
+              ffn: int = 2048) -> np.ndarray:
+    """Packed fp32 recall-head parameters, Xavier-uniform init (gain 1).
+
+    With ``perturb`` the biases are drawn U(-0.1, 0.1) and the norm gains
+    1 + U(-0.1, 0.1) instead of 0 / 1, so parity runs exercise every term."""
+    shapes = head_tensor_shapes(hidden, tower, ffn)
+    total = sum(int(np.prod(s)) for _, s, _ in shapes)
+    u = uniform_at(seed, TAG_HEAD, np.arange(total))
+    blob = np.empty(total, dtype=np.float32)
+    at = 0
+    for name, shape, init in shapes:
+        n = int(np.prod(shape))
+        uu = u[at:at + n]
+        if init == "xavier":
+            fan_out, fan_in = shape
+            bound = math.sqrt(6.0 / (fan_in + fan_out))
+            blob[at:at + n] = ((2.0 * uu - 1.0) * bound).astype(np.float32)
+        elif init == "zero":
+            blob[at:at + n] = ((2.0 * uu - 1.0) * 0.1).astype(np.float32) if perturb else 0.0
+        else:
+            blob[at:at + n] = (1.0 + (2.0 * uu - 1.0) * 0.1).astype(np.float32) if perturb else 1.0
+        at += n
+    return blob
