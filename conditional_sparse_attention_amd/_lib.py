@@ -1,0 +1,195 @@
+"""ctypes binding of liboda (include/oda.h).
+
+Argument marshalling only: every function takes torch tensors (or None for a
+nullable pointer), passes their device pointers and the current HIP stream
+to the C entry point of the same name, and raises OdaError on a non-zero
+status.  All work runs in the library's HIP kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboda.so")
+
+ODA_OK = 0
+ODA_E_NULL, ODA_E_DIMS, ODA_E_UNSUPPORTED, ODA_E_WORKSPACE, ODA_E_LAYER, ODA_E_LAUNCH = -1, -2, -3, -4, -5, -6
+ODA_KV_CONTIG, ODA_KV_PAGED = 0, 1
+ODA_ERR_CAPACITY, ODA_ERR_BLOCK = 1, 2
+ODA_HEAD_NTENSORS = 22
+ODA_FULL_MIN_CHUNK = 1024
+ODA_FULL_MAX_SPLITS = 32
+
+EXPORTED = (
+    "oda_abi_version", "oda_status_str", "oda_head_param_count", "oda_head_offsets",
+    "oda_workspace_bytes", "oda_workspace_worklist_offset", "oda_workspace_init",
+    "oda_local_ranges", "oda_local_attn", "oda_recall_score", "oda_full_attn_if", "oda_commit",
+)
+
+
+class OdaError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        self.status = status
+        super().__init__(f"{fn} failed: {status} ({status_str(status)})")
+
+
+class oda_dims(ctypes.Structure):
+    _fields_ = [
+        ("num_layers", ctypes.c_int32), ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("hidden", ctypes.c_int32),
+        ("sink", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("kv_layout", ctypes.c_int32), ("block_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("t_cap", ctypes.c_int64), ("num_blocks", ctypes.c_int64),
+    ]
+
+
+class oda_kv(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("block_tables", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m conditional_sparse_attention_amd.build` (no fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+        dp, kp = ctypes.POINTER(oda_dims), ctypes.POINTER(oda_kv)
+        sig = {
+            "oda_abi_version": (ctypes.c_int, []),
+            "oda_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+            "oda_head_param_count": (i64, [i32]),
+            "oda_head_offsets": (ctypes.c_int, [i32, ctypes.POINTER(i64)]),
+            "oda_workspace_bytes": (sz, [dp]),
+            "oda_workspace_worklist_offset": (sz, [dp]),
+            "oda_workspace_init": (ctypes.c_int, [dp, vp, sz, vp]),
+            "oda_local_ranges": (ctypes.c_int, [dp, vp, vp, vp]),
+            "oda_local_attn": (ctypes.c_int, [dp, i32, kp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "oda_recall_score": (ctypes.c_int, [dp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, sz, vp]),
+            "oda_full_attn_if": (ctypes.c_int, [dp, i32, kp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "oda_commit": (ctypes.c_int, [dp, kp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().oda_status_str(int(status)).decode()
+
+
+def _check(status: int, fn: str) -> None:
+    if status != ODA_OK:
+        raise OdaError(status, fn)
+
+
+def _p(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("device tensor required")
+    if not t.is_contiguous():
+        raise ValueError("contiguous tensor required")
+    return t.data_ptr()
+
+
+def _s(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _bytes(ws: torch.Tensor) -> int:
+    return ws.numel() * ws.element_size()
+
+
+# ---------------------------------------------------------------------------
+# struct helpers
+# ---------------------------------------------------------------------------
+def make_dims(num_layers: int, batch: int, num_q_heads: int, num_kv_heads: int, *, head_dim: int = 128,
+              sink: int = 4, window: int = 2048, kv_layout: int = ODA_KV_CONTIG, t_cap: int = 0,
+              block_size: int = 16, max_blocks_per_seq: int = 0, num_blocks: int = 0) -> oda_dims:
+    return oda_dims(num_layers, batch, num_q_heads, num_kv_heads, head_dim, num_q_heads * head_dim, sink, window,
+                    kv_layout, block_size if kv_layout == ODA_KV_PAGED else 0,
+                    max_blocks_per_seq if kv_layout == ODA_KV_PAGED else 0, 0,
+                    t_cap if kv_layout == ODA_KV_CONTIG else 0,
+                    num_blocks if kv_layout == ODA_KV_PAGED else 0)
+
+
+def make_kv(k: torch.Tensor, v: torch.Tensor, block_tables: Optional[torch.Tensor] = None) -> oda_kv:
+    return oda_kv(_p(k), _p(v), _p(block_tables))
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+def oda_abi_version() -> int:
+    return lib().oda_abi_version()
+
+
+def oda_head_param_count(hidden: int) -> int:
+    return int(lib().oda_head_param_count(hidden))
+
+
+def oda_head_offsets(hidden: int):
+    arr = (ctypes.c_int64 * (ODA_HEAD_NTENSORS + 1))()
+    _check(lib().oda_head_offsets(hidden, arr), "oda_head_offsets")
+    return [int(x) for x in arr]
+
+
+def oda_workspace_bytes(dims: oda_dims) -> int:
+    n = int(lib().oda_workspace_bytes(ctypes.byref(dims)))
+    if n == 0:
+        raise OdaError(ODA_E_DIMS, "oda_workspace_bytes")
+    return n
+
+
+def oda_workspace_worklist_offset(dims: oda_dims) -> int:
+    return int(lib().oda_workspace_worklist_offset(ctypes.byref(dims)))
+
+
+def oda_workspace_init(dims, ws, stream=None) -> None:
+    _check(lib().oda_workspace_init(ctypes.byref(dims), _p(ws), _bytes(ws), _s(stream)), "oda_workspace_init")
+
+
+def oda_local_ranges(dims, pos, ranges, stream=None) -> None:
+    _check(lib().oda_local_ranges(ctypes.byref(dims), _p(pos), _p(ranges), _s(stream)), "oda_local_ranges")
+
+
+def oda_local_attn(dims, layer, kv: oda_kv, pos, q, k_cur, v_cur, out, lse, ws, stream=None) -> None:
+    _check(lib().oda_local_attn(ctypes.byref(dims), layer, ctypes.byref(kv), _p(pos), _p(q), _p(k_cur), _p(v_cur),
+                                _p(out), _p(lse), _p(ws), _bytes(ws), _s(stream)), "oda_local_attn")
+
+
+def oda_recall_score(dims, head_w, h_prev, emb, h_local, theta, force, pos, score, flag, ws, stream=None) -> None:
+    _check(lib().oda_recall_score(ctypes.byref(dims), _p(head_w), _p(h_prev), _p(emb), _p(h_local),
+                                  ctypes.c_float(theta), _p(force), _p(pos), _p(score), _p(flag), _p(ws),
+                                  _bytes(ws), _s(stream)), "oda_recall_score")
+
+
+def oda_full_attn_if(dims, layer, kv: oda_kv, pos, q, k_cur, v_cur, out, lse, ws, stream=None) -> None:
+    _check(lib().oda_full_attn_if(ctypes.byref(dims), layer, ctypes.byref(kv), _p(pos), _p(q), _p(k_cur),
+                                  _p(v_cur), _p(out), _p(lse), _p(ws), _bytes(ws), _s(stream)), "oda_full_attn_if")
+
+
+def oda_commit(dims, kv: oda_kv, pos, flag, k_cur_L, v_cur_L, k_cur_F, v_cur_F, out_last_L, out_last_F, h_prev, ws,
+               stream=None) -> None:
+    _check(lib().oda_commit(ctypes.byref(dims), ctypes.byref(kv), _p(pos), _p(flag), _p(k_cur_L), _p(v_cur_L),
+                            _p(k_cur_F), _p(v_cur_F), _p(out_last_L), _p(out_last_F), _p(h_prev), _p(ws),
+                            _bytes(ws), _s(stream)), "oda_commit")

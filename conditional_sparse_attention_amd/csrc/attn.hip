@@ -1,0 +1,539 @@
+// Split-K GQA decode attention over an index set, for gfx950.
+//
+// Computes o = softmax(q K~[S]^T / sqrt(d)) V~[S] for every query head of a
+// KV group  [On-Demand Attention notes §2.1, equation for o_t], where K~, V~
+// are the committed cache rows followed by the branch's staged current row,
+// and S is either the local set S^L (sink + window, §2.1) or the full set
+// S^F = [0, t).
+//
+// Work unit: (sequence b, KV head g, split) -- a contiguous run of the index
+// set.  One workgroup of NW waves processes a unit:
+//   * lane layout: a 256-byte bf16 row (d = 128) is read by 16 lanes with one
+//     16-byte load each, so one wave instruction reads 4 whole rows (1 KB,
+//     fully coalesced); each lane handles 8 dims of its row;
+//   * q.k uses v_dot2_f32_bf16 on the raw bf16 pairs, and the 16 partial dot
+//     products of a row are summed with four DPP row operations
+//     (quad_perm x2, row_half_mirror, row_mirror), which leave the bit-same
+//     sum in all 16 lanes;
+//   * online softmax in the log2 domain (scores pre-multiplied by
+//     log2(e)/sqrt(d)), fp32 running max / sum / accumulator per row group,
+//     one rescale per block of UNROLL rows;
+//   * the 4 row groups of a wave merge through cross-lane shuffles, the NW
+//     waves through LDS.
+// A unit that covers its whole (b, g) writes the output directly; otherwise
+// it stores a partial (acc[128], m, l) and takes a ticket; the last unit of a
+// (b, g) merges all partials in split order (deterministic: no float
+// atomics) and resets the ticket.
+//
+// The local kernel runs on a grid (split, g, b).  The full kernel runs on a
+// fixed persistent grid whose workgroups walk the device-side work list
+// written by the recall-score step, so the host never learns which
+// sequences were flagged.
+#include "oda_internal.h"
+
+namespace oda {
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// row blocks per lane per iteration: 4 (16 rows per wave) for G <= 2; 2 for
+// G = 4, which keeps four query heads' state in registers
+template <int G>
+struct Unroll {
+  static constexpr int value = G >= 4 ? 2 : 4;
+};
+constexpr int kLocalWaves = 4;    // local kernel: 256 threads
+// full kernel: 1024 threads (16 waves) for G <= 2; 768 (12 waves, a larger
+// register budget) for G = 4
+template <int G>
+struct FullWaves {
+  static constexpr int value = G >= 4 ? 12 : 16;
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row receives the same bits.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_mov<0x141>(x);  // row_half_mirror
+  x += dpp_mov<0x140>(x);  // row_mirror
+  return x;
+}
+
+__device__ __forceinline__ float dot8_bf16(const uint4 a, const uint4 b) {
+  float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x),
+                                            __builtin_bit_cast(bf16x2_t, b.x), 0.0f, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y),
+                                      __builtin_bit_cast(bf16x2_t, b.y), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z),
+                                      __builtin_bit_cast(bf16x2_t, b.z), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w),
+                                      __builtin_bit_cast(bf16x2_t, b.w), s, false);
+  return s;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+constexpr float kNegBig = -1.0e30f;
+
+template <int G>
+struct State {
+  float m[G];
+  float l[G];
+  float acc[G][8];
+};
+
+// Address of cache row p of (b, g); for the paged layout a block-table
+// entry outside the pool marks the row invalid (ok=false) and returns a
+// safe address.
+template <bool PAGED>
+__device__ __forceinline__ size_t row_index(const AttnParams& P, int b, int g, int p, bool& ok) {
+  if (!PAGED) {
+    return ((size_t)(b * P.Hkv + g) * (size_t)P.t_cap + (size_t)p);
+  } else {
+    int32_t blk = P.tables[(size_t)b * P.max_blocks + (p >> P.log2_block)];
+    if (blk < 0 || (int64_t)blk >= P.num_blocks) {
+      ok = false;
+      blk = 0;
+    }
+    return ((((size_t)blk * P.Hkv + g) << P.log2_block) | (size_t)(p & ((1 << P.log2_block) - 1)));
+  }
+}
+
+template <int G, int kUnroll = Unroll<G>::value>
+__device__ __forceinline__ void block_update(const uint4 (&qv)[G], State<G>& st, const uint4 (&kk)[kUnroll],
+                                             const uint4 (&vv)[kUnroll], const bool (&ok)[kUnroll],
+                                             float scale) {
+  // scores of the kUnroll rows of this lane's row group, log2 domain
+  float s[kUnroll][G];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float x = row16_sum(dot8_bf16(qv[h], kk[u])) * scale;
+      s[u][h] = ok[u] ? x : -INFINITY;
+    }
+  }
+  // one rescale per block; s[][] becomes the unnormalised weights p
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float mx = s[0][h];
+#pragma unroll
+    for (int u = 1; u < kUnroll; ++u) mx = fmaxf(mx, s[u][h]);
+    const float mn = fmaxf(st.m[h], mx);
+    const float alpha = fast_exp2(st.m[h] - mn);
+    st.m[h] = mn;
+    st.l[h] *= alpha;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.acc[h][i] *= alpha;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      s[u][h] = fast_exp2(s[u][h] - mn);
+      st.l[h] += s[u][h];
+    }
+  }
+  // p * v, one row's 8 values converted at a time
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    float vf[8];
+    vf[0] = bf16lo(vv[u].x);
+    vf[1] = bf16hi(vv[u].x);
+    vf[2] = bf16lo(vv[u].y);
+    vf[3] = bf16hi(vv[u].y);
+    vf[4] = bf16lo(vv[u].z);
+    vf[5] = bf16hi(vv[u].z);
+    vf[6] = bf16lo(vv[u].w);
+    vf[7] = bf16hi(vv[u].w);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) st.acc[h][i] = fmaf(s[u][h], vf[i], st.acc[h][i]);
+    }
+  }
+}
+
+// Rows [p_lo, p_hi) of the cache, interleaved over the NW waves in blocks of
+// 4*kUnroll rows.
+template <int G, bool PAGED, int NW>
+__device__ __forceinline__ void cache_rows(const AttnParams& P, const uint4 (&qv)[G], State<G>& st, int b, int g,
+                                           int p_lo, int p_hi, int wave, int r, int c) {
+  constexpr int kUnroll = Unroll<G>::value;
+  constexpr int kWaveRows = 4 * kUnroll;
+  for (int base = p_lo + wave * kWaveRows; base < p_hi; base += NW * kWaveRows) {
+    uint4 kk[kUnroll], vv[kUnroll];
+    bool ok[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int p = base + u * 4 + r;
+      bool valid = p < p_hi;
+      const int pp = valid ? p : p_hi - 1;
+      bool bok = true;
+      const size_t row = row_index<PAGED>(P, b, g, pp, bok);
+      if (PAGED && !bok) {
+        if (valid && c == 0) atomicOr(P.err, ODA_ERR_BLOCK);
+        valid = false;
+      }
+      ok[u] = valid;
+      kk[u] = *reinterpret_cast<const uint4*>(P.K + row * kHeadDim + c * 8);
+      vv[u] = *reinterpret_cast<const uint4*>(P.V + row * kHeadDim + c * 8);
+    }
+    block_update<G>(qv, st, kk, vv, ok, P.scale_log2);
+  }
+}
+
+// The current token: one staged row, handled by wave 0 / row group 0.
+template <int G>
+__device__ __forceinline__ void current_row(const AttnParams& P, const uint4 (&qv)[G], State<G>& st, int b, int g,
+                                            int wave, int r, int c) {
+  constexpr int kUnroll = Unroll<G>::value;
+  if (wave != 0) return;
+  uint4 kk[kUnroll], vv[kUnroll];
+  bool ok[kUnroll];
+  const size_t base = ((size_t)b * P.Hkv + g) * kHeadDim + c * 8;
+  const uint4 kr = *reinterpret_cast<const uint4*>(P.kc + base);
+  const uint4 vr = *reinterpret_cast<const uint4*>(P.vc + base);
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    kk[u] = kr;
+    vv[u] = vr;
+    ok[u] = (u == 0) && (r == 0);
+  }
+  block_update<G>(qv, st, kk, vv, ok, P.scale_log2);
+}
+
+__device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(x, m, 64); }
+
+// Merge the 4 row groups of each wave (shuffles), then the NW waves (LDS).
+// On return, threads idx < G*128 hold (M, L, O) of (head idx/128, dim idx%128)
+// for idx = tid (and tid + NW*64 when G*128 exceeds the block).
+template <int G, int NW>
+__device__ __forceinline__ void wg_merge(State<G>& st, float* lds, int wave, int lane, int c) {
+  float* lacc = lds;                      // [NW][G][128]
+  float* lml = lds + NW * G * kHeadDim;   // [NW][G][2]
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float M = fmaxf(st.m[h], shfl_xor_f(st.m[h], 16));
+    M = fmaxf(M, shfl_xor_f(M, 32));
+    const float sc = fast_exp2(st.m[h] - M);
+    float l = st.l[h] * sc;
+    l += shfl_xor_f(l, 16);
+    l += shfl_xor_f(l, 32);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float a = st.acc[h][i] * sc;
+      a += shfl_xor_f(a, 16);
+      a += shfl_xor_f(a, 32);
+      st.acc[h][i] = a;
+    }
+    if (lane < 16) {
+      float4* dst = reinterpret_cast<float4*>(lacc + ((wave * G + h) * kHeadDim) + c * 8);
+      dst[0] = make_float4(st.acc[h][0], st.acc[h][1], st.acc[h][2], st.acc[h][3]);
+      dst[1] = make_float4(st.acc[h][4], st.acc[h][5], st.acc[h][6], st.acc[h][7]);
+      if (lane == 0) {
+        lml[(wave * G + h) * 2 + 0] = M;
+        lml[(wave * G + h) * 2 + 1] = l;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// After wg_merge: value of (head h, dim dd) merged over the waves.
+template <int G, int NW>
+__device__ __forceinline__ void wg_value(const float* lds, int h, int dd, float& M, float& L, float& O) {
+  const float* lacc = lds;
+  const float* lml = lds + NW * G * kHeadDim;
+  M = kNegBig;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, lml[(w * G + h) * 2]);
+  L = 0.0f;
+  O = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const float sc = fast_exp2(lml[(w * G + h) * 2] - M);
+    L = fmaf(lml[(w * G + h) * 2 + 1], sc, L);
+    O = fmaf(lacc[(w * G + h) * kHeadDim + dd], sc, O);
+  }
+}
+
+__device__ __forceinline__ void write_out(const AttnParams& P, int b, int hq, int dd, float M, float L, float O) {
+  const float v = L > 0.0f ? O / L : 0.0f;
+  P.out[((size_t)b * P.Hq + hq) * kHeadDim + dd] = f32_to_bf16(v);
+  if (P.lse != nullptr && dd == 0) {
+    P.lse[(size_t)b * P.Hq + hq] = L > 0.0f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
+  }
+}
+
+// Final merge of nsplit partials of (b, g) by the last workgroup, in split
+// order.  Kept out of line so its registers do not add to the main loop's.
+template <int G, int NW>
+__device__ __noinline__ void merge_partials(const AttnParams& P, const float* part, int nsplit, int b, int g, float* lds) {
+  constexpr int NT = NW * 64;
+  // stage (m, l) of every (split, head) in LDS
+  float* sm = lds;                       // [nsplit][G]
+  float* sl = lds + nsplit * G;          // [nsplit][G]
+  for (int i = threadIdx.x; i < nsplit * G; i += NT) {
+    const int s = i / G, h = i % G;
+    const float* pp = part + ((size_t)s * G + h) * kPartStride;
+    sm[i] = pp[kHeadDim];
+    sl[i] = pp[kHeadDim + 1];
+  }
+  __syncthreads();
+  // thread -> (head, dim4, split group)
+  constexpr int kLanesPerSplit = G * (kHeadDim / 4);  // (h, d4) pairs
+  constexpr int kGroups = NT / kLanesPerSplit;
+  static_assert(kGroups >= 1, "block too small for the merge");
+  const int tid = threadIdx.x;
+  const int hd = tid % kLanesPerSplit;
+  const int sg = tid / kLanesPerSplit;
+  const int h = hd / (kHeadDim / 4);
+  const int d4 = hd % (kHeadDim / 4);
+  float M = kNegBig;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, sm[s * G + h]);
+  float L = 0.0f;
+  float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (sg < kGroups) {
+#pragma unroll 4
+    for (int s = sg; s < nsplit; s += kGroups) {
+      const float4 a = *reinterpret_cast<const float4*>(part + ((size_t)s * G + h) * kPartStride + d4 * 4);
+      const float w = fast_exp2(sm[s * G + h] - M);
+      L = fmaf(sl[s * G + h], w, L);
+      O.x = fmaf(a.x, w, O.x);
+      O.y = fmaf(a.y, w, O.y);
+      O.z = fmaf(a.z, w, O.z);
+      O.w = fmaf(a.w, w, O.w);
+    }
+  }
+  __syncthreads();
+  // reduce the split groups in fixed order through LDS
+  float* red = lds;  // [kGroups][kLanesPerSplit][5]
+  if (sg < kGroups) {
+    float* r = red + ((size_t)sg * kLanesPerSplit + hd) * 5;
+    r[0] = O.x;
+    r[1] = O.y;
+    r[2] = O.z;
+    r[3] = O.w;
+    r[4] = L;
+  }
+  __syncthreads();
+  if (sg == 0) {
+    float4 Ot = make_float4(0.f, 0.f, 0.f, 0.f);
+    float Lt = 0.0f;
+#pragma unroll 1
+    for (int k = 0; k < kGroups; ++k) {
+      const float* r = red + ((size_t)k * kLanesPerSplit + hd) * 5;
+      Ot.x += r[0];
+      Ot.y += r[1];
+      Ot.z += r[2];
+      Ot.w += r[3];
+      Lt += r[4];
+    }
+    const int hq = g * G + h;
+    write_out(P, b, hq, d4 * 4 + 0, M, Lt, Ot.x);
+    write_out(P, b, hq, d4 * 4 + 1, M, Lt, Ot.y);
+    write_out(P, b, hq, d4 * 4 + 2, M, Lt, Ot.z);
+    write_out(P, b, hq, d4 * 4 + 3, M, Lt, Ot.w);
+  }
+}
+
+// One unit: keys of S with virtual indices [v_lo, v_hi) where S = [0, n0)
+// followed by [s1, t); the last virtual index (n0 + t - s1 - 1) is the
+// current token and is read from staging.
+template <int G, bool PAGED, int NW>
+__device__ void attn_unit(const AttnParams& P, int b, int g, int split, int nsplit, int v_lo, int v_hi,
+                          const LocalSet& S, int32_t* ticket, float* part_bg, float* lds) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int r = lane >> 4;
+  const int c = lane & 15;
+
+  uint4 qv[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    qv[h] = *reinterpret_cast<const uint4*>(P.q + ((size_t)b * P.Hq + g * G + h) * kHeadDim + c * 8);
+
+  State<G> st;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    st.m[h] = kNegBig;
+    st.l[h] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.acc[h][i] = 0.0f;
+  }
+
+  const int n_total = S.size();
+  const bool has_current = (v_hi == n_total);
+  const int v_cache_hi = has_current ? v_hi - 1 : v_hi;
+  // first range [0, n0) -> positions equal virtual indices
+  if (v_lo < S.n0) {
+    const int hi = v_cache_hi < S.n0 ? v_cache_hi : S.n0;
+    if (hi > v_lo) cache_rows<G, PAGED, NW>(P, qv, st, b, g, v_lo, hi, wave, r, c);
+  }
+  // second range: virtual n0 + k  ->  position s1 + k
+  {
+    const int lo = v_lo > S.n0 ? v_lo : S.n0;
+    if (v_cache_hi > lo) cache_rows<G, PAGED, NW>(P, qv, st, b, g, S.s1 + (lo - S.n0), S.s1 + (v_cache_hi - S.n0), wave, r, c);
+  }
+  if (has_current) current_row<G>(P, qv, st, b, g, wave, r, c);
+
+  wg_merge<G, NW>(st, lds, wave, lane, c);
+
+  constexpr int NT = NW * 64;
+  if (nsplit == 1) {
+    for (int idx = tid; idx < G * kHeadDim; idx += NT) {
+      const int h = idx / kHeadDim, dd = idx % kHeadDim;
+      float M, L, O;
+      wg_value<G, NW>(lds, h, dd, M, L, O);
+      write_out(P, b, g * G + h, dd, M, L, O);
+    }
+    __syncthreads();
+    return;
+  }
+  // store this split's partial
+  for (int idx = tid; idx < G * kHeadDim; idx += NT) {
+    const int h = idx / kHeadDim, dd = idx % kHeadDim;
+    float M, L, O;
+    wg_value<G, NW>(lds, h, dd, M, L, O);
+    float* pp = part_bg + ((size_t)split * G + h) * kPartStride;
+    pp[dd] = O;
+    if (dd == 0) {
+      pp[kHeadDim] = M;
+      pp[kHeadDim + 1] = L;
+    }
+  }
+  __threadfence();
+  __syncthreads();
+  __shared__ int s_last;
+  if (tid == 0) {
+    const int prev = atomicAdd(ticket, 1);
+    s_last = (prev == nsplit - 1);
+  }
+  __syncthreads();
+  if (s_last) {
+    __threadfence();
+    merge_partials<G, NW>(P, part_bg, nsplit, b, g, lds);
+    if (tid == 0) atomicExch(ticket, 0);
+  }
+  __syncthreads();
+}
+
+template <int G, int NW>
+constexpr int lds_floats() {
+  // wg_merge needs NW*G*(128+2) floats; merge_partials needs 2*nsplit*G
+  // (nsplit <= 32) for the (m, l) staging, then NW*64*5 for the group reduce.
+  constexpr int a = NW * G * (kHeadDim + 2);
+  constexpr int b = 5 * NW * 64;
+  constexpr int c = 2 * (kFullMaxSplits > kLocalMaxSplits ? kFullMaxSplits : kLocalMaxSplits) * G;
+  return a > b ? (a > c ? a : c) : (b > c ? b : c);
+}
+
+template <int G, bool PAGED>
+__global__ void __launch_bounds__(kLocalWaves * 64) k_attn_local(AttnParams P) {
+  constexpr int NW = kLocalWaves;
+  __shared__ float lds[lds_floats<G, NW>()];
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int pos = P.pos[b];
+  const int t = pos + 1;
+  if (pos < 0 || (int64_t)t > P.t_max) {
+    if (split == 0 && g == 0 && threadIdx.x == 0) atomicOr(P.err, ODA_ERR_CAPACITY);
+    return;
+  }
+  const LocalSet S = local_set(t, P.sink, P.window);
+  const int n = S.size();
+  int ns = (n + kLocalMinChunk - 1) / kLocalMinChunk;
+  ns = ns < kLocalMaxSplits ? ns : kLocalMaxSplits;
+  const int chunk = (n + ns - 1) / ns;
+  if (split >= ns) return;
+  const int v_lo = split * chunk;
+  const int v_hi = (v_lo + chunk) < n ? v_lo + chunk : n;
+  float* part_bg = P.part + ((size_t)(b * P.Hkv + g) * kLocalMaxSplits) * G * kPartStride;
+  attn_unit<G, PAGED, NW>(P, b, g, split, ns, v_lo, v_hi, S, P.tickets + b * P.Hkv + g, part_bg, lds);
+}
+
+template <int G, bool PAGED>
+__global__ void __launch_bounds__(FullWaves<G>::value * 64) k_attn_full(AttnParams P) {
+  constexpr int NW = FullWaves<G>::value;
+  __shared__ float lds[lds_floats<G, NW>()];
+  int count = P.worklist[0];
+  count = count < 0 ? 0 : (count > P.B * kFullMaxSplits ? P.B * kFullMaxSplits : count);
+  const int units = count * P.Hkv;
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const int item = P.worklist[1 + u / P.Hkv];
+    const int g = u % P.Hkv;
+    const int b = item >> 20;
+    const int split = item & 0xFFFFF;
+    if (b < 0 || b >= P.B) continue;
+    const int pos = P.pos[b];
+    const int t = pos + 1;
+    if (pos < 0 || (int64_t)t > P.t_max) {
+      if (split == 0 && g == 0 && threadIdx.x == 0) atomicOr(P.err, ODA_ERR_CAPACITY);
+      continue;
+    }
+    const int ns = full_nsplit(t);
+    if (split >= ns) continue;
+    const int chunk = (t + ns - 1) / ns;
+    const int v_lo = split * chunk;
+    const int v_hi = (v_lo + chunk) < t ? v_lo + chunk : t;
+    LocalSet S;
+    S.n0 = t;
+    S.s1 = t;
+    S.t = t;
+    float* part_bg = P.part + ((size_t)(b * P.Hkv + g) * kFullMaxSplits) * G * kPartStride;
+    attn_unit<G, PAGED, NW>(P, b, g, split, ns, v_lo, v_hi, S, P.tickets + b * P.Hkv + g, part_bg, lds);
+  }
+}
+
+template <int G, bool PAGED>
+int launch_local_t(const AttnParams& p, hipStream_t s) {
+  dim3 grid(kLocalMaxSplits, p.Hkv, p.B);
+  hipLaunchKernelGGL((k_attn_local<G, PAGED>), grid, dim3(kLocalWaves * 64), 0, s, p);
+  return hipGetLastError() == hipSuccess ? ODA_OK : ODA_E_LAUNCH;
+}
+
+int full_grid(const AttnParams& p) {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  const long units_max = (long)p.B * p.Hkv * kFullMaxSplits;
+  long grid = cus[dev];
+  return (int)(units_max < grid ? units_max : grid);
+}
+
+template <int G, bool PAGED>
+int launch_full_t(const AttnParams& p, hipStream_t s) {
+  dim3 grid(full_grid(p));
+  hipLaunchKernelGGL((k_attn_full<G, PAGED>), grid, dim3(FullWaves<G>::value * 64), 0, s, p);
+  return hipGetLastError() == hipSuccess ? ODA_OK : ODA_E_LAUNCH;
+}
+
+}  // namespace
+
+int launch_local_attn(const AttnParams& p, int G, bool paged, hipStream_t s) {
+  switch (G) {
+    case 1: return paged ? launch_local_t<1, true>(p, s) : launch_local_t<1, false>(p, s);
+    case 2: return paged ? launch_local_t<2, true>(p, s) : launch_local_t<2, false>(p, s);
+    case 4: return paged ? launch_local_t<4, true>(p, s) : launch_local_t<4, false>(p, s);
+    default: return ODA_E_UNSUPPORTED;
+  }
+}
+
+int launch_full_attn(const AttnParams& p, int G, bool paged, hipStream_t s) {
+  switch (G) {
+    case 1: return paged ? launch_full_t<1, true>(p, s) : launch_full_t<1, false>(p, s);
+    case 2: return paged ? launch_full_t<2, true>(p, s) : launch_full_t<2, false>(p, s);
+    case 4: return paged ? launch_full_t<4, true>(p, s) : launch_full_t<4, false>(p, s);
+    default: return ODA_E_UNSUPPORTED;
+  }
+}
+
+}  // namespace oda

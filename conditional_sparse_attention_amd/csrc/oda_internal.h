@@ -1,0 +1,179 @@
+// Internal declarations of liboda: workspace layout, launch parameter
+// blocks and small device helpers shared by the kernels.  Written for gfx950
+// (CDNA4): 64-wide wavefronts, DPP row operations, v_dot2_f32_bf16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "oda.h"
+
+namespace oda {
+
+constexpr int kHeadDim = 128;
+constexpr int kMaxBatch = 32;
+constexpr int kLocalMaxSplits = 8;     // splits of one (sequence, KV head) in the local branch
+constexpr int kLocalMinChunk = 64;     // fewer keys than this per split is not worth a split
+constexpr int kPartStride = 132;       // floats per partial: acc[128], m, l, 2 pad (16-B aligned)
+constexpr int kTower = ODA_HEAD_TOWER;
+constexpr int kFfn = ODA_HEAD_FFN;
+constexpr int kFullMinChunk = ODA_FULL_MIN_CHUNK;
+constexpr int kFullMaxSplits = ODA_FULL_MAX_SPLITS;
+
+// ---------------------------------------------------------------------------
+// workspace layout (byte offsets, each region 256-B aligned)
+// ---------------------------------------------------------------------------
+struct WsLayout {
+  size_t header;       // int32[64]: [0] error bits
+  size_t worklist;     // int32 count, then int32 items[B * kFullMaxSplits]
+  size_t tick_local;   // int32[B * Hkv]
+  size_t tick_full;    // int32[B * Hkv]
+  size_t tick_commit;  // int32[B]
+  size_t part_local;   // float[B * Hkv * kLocalMaxSplits * G * kPartStride]
+  size_t part_full;    // float[B * Hkv * kFullMaxSplits * G * kPartStride]
+  size_t head;         // float: towers[3][B][T], u[B][T], hdn[B][F], u1[B][T], u2[B][T]
+  size_t total;
+  int64_t t_max;            // capacity of one sequence in positions
+};
+
+// Split count of the full branch for a sequence of t keys.
+__device__ __host__ __forceinline__ int full_nsplit(int t) {
+  int n = (t + kFullMinChunk - 1) / kFullMinChunk;
+  return n < kFullMaxSplits ? n : kFullMaxSplits;
+}
+
+bool dims_valid(const oda_dims* d, int* status);
+WsLayout ws_layout(const oda_dims* d);
+
+// head activation sub-regions (float offsets inside WsLayout::head)
+struct HeadWs {
+  float* towers;  // [3][B][T]  (a, b, c)
+  float* u0;      // [B][T]
+  float* hdn;     // [B][F]
+  float* u1;      // [B][T]
+  float* u2;      // [B][T]
+};
+inline HeadWs head_ws(void* ws, const WsLayout& L, int B) {
+  float* base = reinterpret_cast<float*>(static_cast<char*>(ws) + L.head);
+  HeadWs h;
+  h.towers = base;
+  h.u0 = h.towers + 3 * B * kTower;
+  h.hdn = h.u0 + B * kTower;
+  h.u1 = h.hdn + B * kFfn;
+  h.u2 = h.u1 + B * kTower;
+  return h;
+}
+inline size_t head_ws_floats(int B) { return (size_t)B * (3 * kTower + kTower + kFfn + 2 * kTower); }
+
+// ---------------------------------------------------------------------------
+// attention launch parameters
+// ---------------------------------------------------------------------------
+struct AttnParams {
+  const uint16_t* K;  // layer base of the cache
+  const uint16_t* V;
+  const int32_t* tables;
+  int64_t t_cap;      // contiguous: row stride per (b, g)
+  int64_t num_blocks;
+  int32_t max_blocks;
+  int32_t log2_block;
+  const int32_t* pos;
+  const uint16_t* q;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  uint16_t* out;
+  float* lse;
+  float* part;
+  int32_t* tickets;
+  int32_t* err;
+  const int32_t* worklist;  // count at [0], items from [1]
+  int32_t B, Hq, Hkv, sink, window;
+  int64_t t_max;
+  float scale_log2;         // log2(e) / sqrt(d)
+};
+
+int launch_local_attn(const AttnParams& p, int G, bool paged, hipStream_t s);
+int launch_full_attn(const AttnParams& p, int G, bool paged, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// recall head launch parameters
+// ---------------------------------------------------------------------------
+struct HeadParams {
+  const float* w;          // packed blob
+  const int64_t* offs;     // unused on device; host-side offsets
+  const uint16_t* h_prev;
+  const uint16_t* emb;
+  const uint16_t* h_local;
+  float theta;
+  const int8_t* force;
+  const int32_t* pos;
+  float* score;
+  uint8_t* flag;
+  int32_t* worklist;
+  int32_t B, D;
+  HeadWs act;
+};
+int launch_recall_head(const HeadParams& p, const int64_t* offs, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// commit / ranges / init
+// ---------------------------------------------------------------------------
+struct CommitParams {
+  uint16_t* K;
+  uint16_t* V;
+  const int32_t* tables;
+  int64_t t_cap, num_blocks, layer_stride;  // elements per layer of the cache
+  int32_t max_blocks, log2_block;
+  int32_t* pos;
+  const uint8_t* flag;
+  const uint16_t *kL, *vL, *kF, *vF;
+  const uint16_t *oL, *oF;
+  uint16_t* h_prev;
+  int32_t* tickets;
+  int32_t* err;
+  int32_t L, B, Hkv, D;
+  int64_t t_max;
+};
+int launch_commit(const CommitParams& p, hipStream_t s);
+int launch_ranges(const int32_t* pos, int32_t* ranges, int B, int sink, int window, hipStream_t s);
+int launch_fill_zero(int32_t* p, size_t n, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// round-to-nearest-even fp32 -> bf16 (NaN kept quiet)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Local index set S^L of a sequence whose current 0-based position is t-1:
+// [0, n0) followed by [s1, t) (s1 >= n0); n0 == t when the parts touch.
+struct LocalSet {
+  int32_t n0;   // length of the first range [0, n0)
+  int32_t s1;   // start of the second range
+  int32_t t;    // end of the second range (exclusive) = current position + 1
+  __device__ __host__ int32_t size() const { return n0 + (t - s1); }
+};
+__device__ __host__ __forceinline__ LocalSet local_set(int32_t t, int32_t sink, int32_t window) {
+  LocalSet r;
+  int32_t a1 = sink < t ? sink : t;
+  int32_t b0 = t - window > 0 ? t - window : 0;
+  if (b0 <= a1) {
+    r.n0 = t;
+    r.s1 = t;
+  } else {
+    r.n0 = a1;
+    r.s1 = b0;
+  }
+  r.t = t;
+  return r;
+}
+
+}  // namespace oda

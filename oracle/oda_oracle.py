@@ -271,15 +271,14 @@ def branch_rule(q: float, theta: float = THETA_DEFAULT, force: int = -1) -> int:
 # ---------------------------------------------------------------------------
 # work list for the conditional full branch
 # ---------------------------------------------------------------------------
-def full_worklist(flags: Sequence[int], pos: Sequence[int], chunk: int) -> List[Tuple[int, int]]:
-    """Ordered (sequence, split) items of the full branch: for every flagged
-    sequence b in ascending order, splits 0..ceil(t_b/chunk)-1 of its full
-    index set, t_b = pos_b + 1."""
+def full_worklist(flags: Sequence[int], nsplit: Sequence[int]) -> List[Tuple[int, int]]:
+    """Compacted work list of the conditional full branch: for every flagged
+    sequence b in ascending order, its splits 0..nsplit[b]-1.  (How many
+    splits a sequence is cut into is a kernel policy, passed in.)"""
     items: List[Tuple[int, int]] = []
     for b, f in enumerate(flags):
         if f:
-            t = int(pos[b]) + 1
-            for s in range(-(-t // chunk)):
+            for s in range(int(nsplit[b])):
                 items.append((b, s))
     return items
 

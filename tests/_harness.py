@@ -1,0 +1,254 @@
+"""Test harness: device buffers for a synthetic workload, and a reference
+replay of decode steps against the CPU oracle.
+
+Replay protocol (after the pages' own consistency check, which replays the
+same routing policy and compares outputs, actions and committed state): the
+GPU trajectory drives.  Each step the oracle recomputes, from the same
+inputs, every local output, the recall score from the GPU's h_prev / emb /
+local output, the branch decision, every full output of the flagged
+sequences, and the commit with the GPU's flags, and compares:
+  * attention outputs   |gpu - oracle| <= 1e-2 + 1e-2 |oracle|
+  * recall scores       |gpu - oracle| <= 1e-4 (1 + |oracle|)
+  * flags               bit-exact unless |q_oracle - theta| < 1e-3
+  * cache slot, h_prev, pos   bit-exact.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import synth
+from oracle import (branch_rule, decode_attention, full_index_set, local_index_set, recall_score,
+                    unpack_head)
+import conditional_sparse_attention_amd as C
+from conditional_sparse_attention_amd.step import StepBuffers, StepPlan
+
+ATOL = RTOL = 1e-2
+SCORE_TOL = 1e-4
+TIE_BAND = 1e-3
+DEV = "cuda"
+
+
+def to_dev_u16(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV)
+
+
+def from_dev_u16(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
+def assert_close_bf16(gpu_bits: np.ndarray, ref: np.ndarray, what: str) -> None:
+    g = synth.bf16_bits_to_f32(gpu_bits).astype(np.float64)
+    err = np.abs(g - ref)
+    bad = err > ATOL + RTOL * np.abs(ref)
+    if np.any(bad):
+        i = np.unravel_index(np.argmax(err - (ATOL + RTOL * np.abs(ref))), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; worst at {i}: "
+                             f"gpu {g[i]} oracle {ref[i]}")
+
+
+class Problem:
+    """Device state of a workload: cache, step buffers, workspace, plan."""
+
+    def __init__(self, wl: synth.Workload, *, theta: float = 0.0, head_perturb: bool = False,
+                 device_fill: bool = False, lse: bool = True, host_cache: bool = True):
+        self.wl = wl
+        L, B, Hq, Hkv, d = wl.layers, wl.batch, wl.hq, wl.hkv, wl.head_dim
+        self.paged = wl.layout == "paged"
+        if self.paged:
+            tables, nb = synth.paged_block_tables(wl)
+            self.tables_np, self.num_blocks = tables, nb
+            self.dims = C.make_dims(L, B, Hq, Hkv, kv_layout=C.ODA_KV_PAGED, block_size=wl.block_size,
+                                    max_blocks_per_seq=tables.shape[1], num_blocks=nb,
+                                    sink=wl.sink, window=wl.window)
+            shape = (L, nb, Hkv, wl.block_size, d)
+            self.tables = torch.from_numpy(tables).to(DEV)
+        else:
+            self.tables_np, self.tables = None, None
+            self.dims = C.make_dims(L, B, Hq, Hkv, t_cap=wl.t_cap, sink=wl.sink, window=wl.window)
+            shape = (L, B, Hkv, wl.t_cap, d)
+        self.K = torch.zeros(shape, dtype=torch.int16, device=DEV)
+        self.V = torch.zeros(shape, dtype=torch.int16, device=DEV)
+        self.t0_dev = torch.from_numpy(wl.t0.astype(np.int32)).to(DEV)
+        # host copy of the logical cache [L][B][Hkv][T][d] (small workloads only)
+        self.host = None
+        if host_cache:
+            T = int(np.max(wl.t0)) + wl.steps
+            self.host = {tag: np.zeros((L, B, Hkv, T, d), dtype=np.uint16) for tag in (synth.TAG_K, synth.TAG_V)}
+            for tag in (synth.TAG_K, synth.TAG_V):
+                for l in range(L):
+                    for b in range(B):
+                        for g in range(Hkv):
+                            self.host[tag][l, b, g, :wl.t0[b]] = synth.cache_rows(wl, tag, l, b, g, 0, int(wl.t0[b]))
+        if device_fill or not host_cache:
+            import synth.device as sd
+            for tag, buf in ((synth.TAG_K, self.K), (synth.TAG_V, self.V)):
+                sd.fill_cache(buf, wl, tag, self.t0_dev, tables=self.tables, num_blocks=getattr(self, "num_blocks", 0))
+        else:
+            self._upload_cache()
+        self.kv = C.make_kv(self.K, self.V, self.tables)
+        nbytes = C.oda_workspace_bytes(self.dims)
+        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+        C.oda_workspace_init(self.dims, self.ws)
+        self.blob = synth.head_blob(wl.hidden, wl.head_seed, perturb=head_perturb)
+        self.head_P = None
+        D = wl.hidden
+        self.bufs = StepBuffers(
+            pos=self.t0_dev.clone(),
+            qL=torch.zeros((L, B, Hq, d), dtype=torch.int16, device=DEV),
+            kL=torch.zeros((L, B, Hkv, d), dtype=torch.int16, device=DEV),
+            vL=torch.zeros((L, B, Hkv, d), dtype=torch.int16, device=DEV),
+            qF=torch.zeros((L, B, Hq, d), dtype=torch.int16, device=DEV),
+            kF=torch.zeros((L, B, Hkv, d), dtype=torch.int16, device=DEV),
+            vF=torch.zeros((L, B, Hkv, d), dtype=torch.int16, device=DEV),
+            emb=torch.zeros((B, D), dtype=torch.int16, device=DEV),
+            h_prev=to_dev_u16(synth.h_prev0(wl)),
+            head_w=torch.from_numpy(self.blob).to(DEV),
+            oL=torch.zeros((L, B, Hq, d), dtype=torch.int16, device=DEV),
+            oF=torch.zeros((L, B, Hq, d), dtype=torch.int16, device=DEV),
+            score=torch.zeros(B, dtype=torch.float32, device=DEV),
+            flag=torch.zeros(B, dtype=torch.uint8, device=DEV),
+            force=torch.full((B,), -1, dtype=torch.int8, device=DEV),
+            lseL=torch.zeros((L, B, Hq), dtype=torch.float32, device=DEV) if lse else None,
+            lseF=torch.zeros((L, B, Hq), dtype=torch.float32, device=DEV) if lse else None,
+        )
+        self.plan = StepPlan(self.dims, self.kv, self.ws, self.bufs, theta)
+
+    def _upload_cache(self):
+        wl = self.wl
+        for tag, buf in ((synth.TAG_K, self.K), (synth.TAG_V, self.V)):
+            host = self.host[tag]
+            if not self.paged:
+                arr = np.zeros(tuple(buf.shape), dtype=np.uint16)
+                T = host.shape[3]
+                arr[:, :, :, :T] = host
+                buf.copy_(to_dev_u16(arr))
+            else:
+                arr = np.zeros(tuple(buf.shape), dtype=np.uint16)
+                bs = wl.block_size
+                for b in range(wl.batch):
+                    n = int(wl.t0[b])
+                    for p0 in range(0, n, bs):
+                        blk = self.tables_np[b, p0 // bs]
+                        p1 = min(p0 + bs, n)
+                        arr[:, blk, :, :p1 - p0] = host[:, b, :, p0:p1]
+                buf.copy_(to_dev_u16(arr))
+
+    # ---------------------------------------------------------------- inputs
+    def step_inputs(self, j: int) -> dict:
+        wl = self.wl
+        return {k: synth.step_tensor_all_layers(wl, k, j) for k in ("qL", "kL", "vL", "qF", "kF", "vF")} | \
+            {"emb": synth.embedding(wl, j)}
+
+    def upload_step(self, inp: dict) -> None:
+        for k in ("qL", "kL", "vL", "qF", "kF", "vF"):
+            getattr(self.bufs, k).copy_(to_dev_u16(inp[k]))
+        self.bufs.emb.copy_(to_dev_u16(inp["emb"]))
+
+    def set_force(self, force: np.ndarray) -> None:
+        self.bufs.force.copy_(torch.from_numpy(np.asarray(force, dtype=np.int8)))
+
+    # -------------------------------------------------------------- readback
+    def cache_slot(self, l: int, b: int, p: int):
+        """bf16 bits [2][Hkv][d] (K, V) of logical slot p."""
+        if not self.paged:
+            return (from_dev_u16(self.K[l, b, :, p]), from_dev_u16(self.V[l, b, :, p]))
+        blk = int(self.tables_np[b, p // self.wl.block_size])
+        r = p % self.wl.block_size
+        return (from_dev_u16(self.K[l, blk, :, r]), from_dev_u16(self.V[l, blk, :, r]))
+
+    def ws_error_word(self) -> int:
+        return int(self.ws[:4].view(torch.int32).item())
+
+    def worklist(self):
+        off = C.oda_workspace_worklist_offset(self.dims)
+        w = self.ws[off:].view(torch.int32)
+        n = int(w[0].item())
+        items = w[1:1 + n].cpu().numpy()
+        return [(int(x) >> 20, int(x) & 0xFFFFF) for x in items]
+
+    def head_params(self):
+        if self.head_P is None:
+            self.head_P = unpack_head(self.blob, self.wl.hidden)
+        return self.head_P
+
+
+def full_nsplit(t: int) -> int:
+    """Split policy stated in include/oda.h: min(32, ceil(t / 1024))."""
+    return min(C.ODA_FULL_MAX_SPLITS, -(-t // C.ODA_FULL_MIN_CHUNK))
+
+
+def replay_step(pr: Problem, j: int, *, theta: float, force=None, check_layers=None, check_b=None,
+                stats: dict = None) -> dict:
+    """Run step j on the GPU, then check it against the oracle (small
+    workloads with a host cache).  Returns per-step records."""
+    wl = pr.wl
+    L, B, Hq, Hkv, d = wl.layers, wl.batch, wl.hq, wl.hkv, wl.head_dim
+    inp = pr.step_inputs(j)
+    pr.upload_step(inp)
+    if force is None:
+        force = np.full(B, -1, dtype=np.int8)
+    pr.set_force(force)
+    pr.plan.set_theta(theta)
+    pos_before = pr.bufs.pos.cpu().numpy().copy()
+    h_prev_before = from_dev_u16(pr.bufs.h_prev)
+    sentinel = np.full((L, B, Hq, d), 0x7FC1, dtype=np.uint16)  # NaN pattern: rows left untouched keep it
+    pr.bufs.oF.copy_(to_dev_u16(sentinel))
+    pr.plan.run()
+    torch.cuda.synchronize()
+    oL = from_dev_u16(pr.bufs.oL)
+    oF = from_dev_u16(pr.bufs.oF)
+    score = pr.bufs.score.cpu().numpy()
+    flag = pr.bufs.flag.cpu().numpy()
+    h_prev_after = from_dev_u16(pr.bufs.h_prev)
+    pos_after = pr.bufs.pos.cpu().numpy()
+    lseL = pr.bufs.lseL.cpu().numpy() if pr.bufs.lseL is not None else None
+    assert pr.ws_error_word() == 0, "device error bits set"
+    layers = range(L) if check_layers is None else check_layers
+    bs = range(B) if check_b is None else check_b
+    Kh, Vh = pr.host[synth.TAG_K], pr.host[synth.TAG_V]
+    P = pr.head_params()
+    # ---- local branch
+    for l in layers:
+        for b in bs:
+            p = int(pos_before[b])
+            ref = decode_attention(inp["qL"][l, b], Kh[l, b, :, :p], Vh[l, b, :, :p], inp["kL"][l, b],
+                                   inp["vL"][l, b], local_index_set(p + 1, wl.sink, wl.window))
+            assert_close_bf16(oL[l, b], ref, f"step {j} local l={l} b={b} pos={p}")
+    # ---- score, rule
+    for b in range(B):
+        q = recall_score(P, h_prev_before[b], inp["emb"][b], oL[L - 1, b].reshape(-1))
+        assert abs(float(score[b]) - q) <= SCORE_TOL * (1 + abs(q)), f"step {j} b={b}: score {score[b]} vs {q}"
+        want = branch_rule(q, theta, int(force[b]))
+        if force[b] >= 0 or abs(q - theta) >= TIE_BAND or not np.isfinite(q):
+            assert int(flag[b]) == want, f"step {j} b={b}: flag {flag[b]} vs {want} (q={q}, theta={theta})"
+        if stats is not None:
+            stats.setdefault("q", []).append(q)
+    # ---- work list
+    assert pr.worklist() == [(b, s) for b in range(B) if flag[b] for s in range(full_nsplit(int(pos_before[b]) + 1))]
+    # ---- full branch (flagged rows), untouched rows
+    for b in range(B):
+        if flag[b]:
+            for l in layers:
+                if b not in bs:
+                    continue
+                p = int(pos_before[b])
+                ref = decode_attention(inp["qF"][l, b], Kh[l, b, :, :p], Vh[l, b, :, :p], inp["kF"][l, b],
+                                       inp["vF"][l, b], full_index_set(p + 1))
+                assert_close_bf16(oF[l, b], ref, f"step {j} full l={l} b={b} pos={p}")
+        else:
+            assert np.all(oF[:, b] == 0x7FC1), f"step {j}: full output of unflagged b={b} was written"
+    # ---- commit (GPU flags drive), bit-exact
+    assert np.array_equal(pos_after, pos_before + 1)
+    for b in range(B):
+        p = int(pos_before[b])
+        chosen = "F" if flag[b] else "L"
+        o_last = oF[L - 1, b] if flag[b] else oL[L - 1, b]
+        assert np.array_equal(h_prev_after[b], o_last.reshape(-1)), f"step {j} b={b}: h_prev"
+        for l in range(L):
+            Kh[l, b, :, p] = inp["k" + chosen][l, b]
+            Vh[l, b, :, p] = inp["v" + chosen][l, b]
+            ks, vs = pr.cache_slot(l, b, p)
+            assert np.array_equal(ks, Kh[l, b, :, p]) and np.array_equal(vs, Vh[l, b, :, p]), \
+                f"step {j} l={l} b={b}: committed slot"
+    return {"flag": flag.copy(), "score": score.copy(), "lseL": lseL}

@@ -1,0 +1,83 @@
+"""The C-ABI library loads, exports every symbol include/oda.h declares,
+answers host-only queries, and rejects bad arguments before launching
+anything (these calls return before any device work, so they run on CPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import conditional_sparse_attention_amd as C
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "oda.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(oda_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(C.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = C.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_host_queries():
+    assert C.oda_abi_version() == 1
+    assert C.oda_head_param_count(2048) == 28325889   # the page's head size
+    assert C.oda_head_param_count(0) == -1
+    offs = C.oda_head_offsets(2048)
+    assert offs[-1] == 28325889 and offs[0] == 0 and all(o % 4 == 0 for o in offs[:-1])
+
+
+def test_head_offsets_agree_with_oracle_layout():
+    from oracle import head_layout
+    import numpy as np
+    for D in (2048, 4096):
+        offs = C.oda_head_offsets(D)
+        sizes = [int(np.prod(s)) for _, s in head_layout(D)]
+        assert offs == list(np.concatenate([[0], np.cumsum(sizes)]))
+
+
+def test_workspace_and_dims_validation():
+    ok = C.make_dims(28, 4, 16, 8, t_cap=131072 + 384)
+    assert C.oda_workspace_bytes(ok) > 0
+    bad = [
+        C.make_dims(28, 33, 16, 8, t_cap=100),     # batch > 32
+        C.make_dims(28, 4, 16, 8, head_dim=64, t_cap=100),
+        C.make_dims(28, 4, 16, 6, t_cap=100),      # 16 % 6
+        C.make_dims(28, 4, 64, 8, t_cap=100),      # G = 8 unsupported
+        C.make_dims(0, 4, 16, 8, t_cap=100),
+        C.make_dims(28, 4, 16, 8, t_cap=0),
+        C.make_dims(28, 4, 16, 8, kv_layout=C.ODA_KV_PAGED, block_size=12, max_blocks_per_seq=4, num_blocks=8),
+    ]
+    for d in bad:
+        with pytest.raises(C.OdaError):
+            C.oda_workspace_bytes(d)
+
+
+def test_entry_points_reject_bad_arguments_without_launching():
+    lib = C.lib()
+    d = C.make_dims(2, 2, 16, 8, t_cap=64)
+    kv = C.oda_kv(None, None, None)
+    ws_bytes = C.oda_workspace_bytes(d)
+    dp, kp = ctypes.byref(d), ctypes.byref(kv)
+    assert lib.oda_local_attn(dp, 0, kp, *([None] * 7), ws_bytes, None) == C.ODA_E_NULL
+    assert lib.oda_full_attn_if(dp, 0, kp, *([None] * 7), ws_bytes, None) == C.ODA_E_NULL
+    fake = 0x1000
+    kv2 = C.oda_kv(fake, fake, None)
+    args = (fake,) * 5  # pos, q, k_cur, v_cur, out
+    assert lib.oda_local_attn(dp, 2, ctypes.byref(kv2), *args, None, fake, ws_bytes, None) == C.ODA_E_LAYER
+    assert lib.oda_local_attn(dp, -1, ctypes.byref(kv2), *args, None, fake, ws_bytes, None) == C.ODA_E_LAYER
+    assert lib.oda_local_attn(dp, 0, ctypes.byref(kv2), *args, None, fake, ws_bytes - 1, None) == C.ODA_E_WORKSPACE
+    assert lib.oda_recall_score(dp, *([None] * 4), ctypes.c_float(0), *([None] * 5), ws_bytes, None) == C.ODA_E_NULL
+    assert lib.oda_commit(dp, kp, *([None] * 10), ws_bytes, None) == C.ODA_E_NULL
+    assert lib.oda_workspace_init(dp, None, ws_bytes, None) == C.ODA_E_NULL
+    assert lib.oda_local_ranges(None, fake, fake, None) == C.ODA_E_NULL
+    assert C.status_str(C.ODA_E_WORKSPACE).startswith("workspace")

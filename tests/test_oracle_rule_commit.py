@@ -67,11 +67,12 @@ def test_worklist_brute_force():
         flags = rng.integers(0, 2, size=B)
         pos = rng.integers(0, 5000, size=B)
         chunk = int(rng.choice([64, 256, 1000]))
-        items = full_worklist(flags, pos, chunk)
+        nsplit = [math.ceil((p + 1) / chunk) for p in pos]
+        items = full_worklist(flags, nsplit)
         brute = [(b, s) for b in range(B) for s in range(10000)
                  if flags[b] and s * chunk < pos[b] + 1]
         assert items == brute
-        assert len(items) == sum(int(f) * math.ceil((p + 1) / chunk) for f, p in zip(flags, pos))
+        assert len(items) == sum(int(f) * n for f, n in zip(flags, nsplit))
 
 
 def test_commit_invariants():
