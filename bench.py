@@ -1,0 +1,318 @@
+#!/usr/bin/env python3
+"""Benchmark of the ODA decode step on one MI355X.
+
+Workload (default): Qwen3-1.7B-shaped attention stack -- 28 layers, 16 query
+/ 8 KV heads, head_dim 128 -- batch 4, 131,072-token contiguous bf16 KV
+cache per sequence (60 GB), three planted far needles, random Xavier fp32
+recall head, threshold tuned so that 12.5% of (sequence, step) decisions
+take the full branch.  All inputs are synthetic (seeded generator G, filled
+on the device); the time excludes that fill.
+
+One step = local attention of all 28 layers, recall score + rule + work
+list, conditional full attention of all 28 layers, commit, plus the feed
+kernel that writes the step's synthetic q/k/v/embedding.
+
+Protocol: a calibration pass with theta = +inf (all local) records the
+head's scores and sets theta to the midpoint between the k-th and (k+1)-th
+largest, k = round(0.125 * B * steps); the state is reset; W warm-up steps;
+then the timed region (K steps) is run REPEATS times from the same start
+state and the median is reported (warm throughput).  Each launch of the
+full-attention kernel is bracketed by HIP events on its stream, giving its
+average duration inside the timed region; the algorithmic bytes of a launch
+are t_b * 4096 B (K and V of every key of every flagged sequence, incl. the
+staged current token) summed over the sequences the flags select.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--repeats", type=int, default=3)
+    ap.add_argument("--workload", default="3", help="workload key (default 3: 128K, B=4, 12.5%% recall)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="replay the step as one HIP graph (no per-launch events)")
+    ap.add_argument("--rate-sweep", default="", help="comma list of forced full-branch rates to time as well")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "single-GPU build: this benchmark runs on one GPU only; "
+                                   "multi-GPU runs are not part of it", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import synth
+    import synth.device as sd
+    import conditional_sparse_attention_amd as C
+    from conditional_sparse_attention_amd.step import StepBuffers, StepPlan
+
+    wl_key = int(args.workload) if args.workload.isdigit() else args.workload
+    wl = synth.workloads()[wl_key]
+    if wl.layout != "contig":
+        raise SystemExit("bench supports the contiguous workloads")
+    total_steps_needed = args.steps + max(args.warmup, 0)
+    if args.steps > wl.steps + wl.t_cap_slack:
+        raise SystemExit("too many steps for the cache capacity")
+    dev = "cuda"
+    stream = torch.cuda.Stream()  # a non-default stream, so the step can also be graph-captured
+    with torch.cuda.stream(stream):
+        run(args, wl, stream, torch, synth, sd, C, StepBuffers, StepPlan, dev)
+
+
+def run(args, wl, stream, torch, synth, sd, C, StepBuffers, StepPlan, dev):
+    L, B, Hq, Hkv, d, D = wl.layers, wl.batch, wl.hq, wl.hkv, wl.head_dim, wl.hidden
+    t_setup = time.time()
+    dims = C.make_dims(L, B, Hq, Hkv, t_cap=wl.t_cap, sink=wl.sink, window=wl.window)
+    K = torch.empty((L, B, Hkv, wl.t_cap, d), dtype=torch.int16, device=dev)
+    V = torch.empty_like(K)
+    t0 = torch.from_numpy(wl.t0.astype(np.int32)).to(dev)
+    sd.fill_cache(K, wl, synth.TAG_K, t0)
+    sd.fill_cache(V, wl, synth.TAG_V, t0)
+    kv = C.make_kv(K, V)
+    ws = torch.zeros(C.oda_workspace_bytes(dims), dtype=torch.uint8, device=dev)
+    C.oda_workspace_init(dims, ws)
+    blob = synth.head_blob(D, wl.head_seed)
+    h0 = torch.from_numpy(synth.h_prev0(wl).view(np.int16)).to(dev)
+    z = lambda *s, dt=torch.int16: torch.zeros(s, dtype=dt, device=dev)
+    bufs = StepBuffers(pos=t0.clone(), qL=z(L, B, Hq, d), kL=z(L, B, Hkv, d), vL=z(L, B, Hkv, d),
+                       qF=z(L, B, Hq, d), kF=z(L, B, Hkv, d), vF=z(L, B, Hkv, d), emb=z(B, D), h_prev=h0.clone(),
+                       head_w=torch.from_numpy(blob).to(dev), oL=z(L, B, Hq, d), oF=z(L, B, Hq, d),
+                       score=z(B, dt=torch.float32), flag=z(B, dt=torch.uint8),
+                       force=torch.full((B,), -1, dtype=torch.int8, device=dev))
+    plan = StepPlan(dims, kv, ws, bufs, theta=math.inf, stream=stream)
+    feed = {"qL": bufs.qL, "qF": bufs.qF, "kL": bufs.kL, "vL": bufs.vL, "kF": bufs.kF, "vF": bufs.vF, "e": bufs.emb}
+
+    def reset():
+        bufs.pos.copy_(t0)
+        bufs.h_prev.copy_(h0)
+
+    def step():
+        sd.fill_step(feed, wl, bufs.pos, t0)
+        plan.run()
+
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+
+    # ---- calibration: all-local scores -> theta for the target rate
+    reset()
+    scores = torch.zeros((args.steps, B), dtype=torch.float32, device=dev)
+    for j in range(args.steps):
+        step()
+        scores[j].copy_(bufs.score)
+    torch.cuda.synchronize()
+    sc = np.sort(scores.cpu().numpy().reshape(-1))[::-1]
+    rate = wl.rate if wl.rate is not None else 0.125
+    k = int(round(rate * sc.size))
+    theta = float((sc[k - 1] + sc[k]) / 2) if 0 < k < sc.size else (math.inf if k == 0 else -math.inf)
+    plan.set_theta(theta)
+
+    # ---- warm-up
+    reset()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region(s)
+    flags_hist = torch.zeros((args.steps, B), dtype=torch.uint8, device=dev)
+    pos_hist = torch.zeros((args.steps, B), dtype=torch.int32, device=dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps * L)]
+    graph = None
+    if args.graph:
+        reset()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+        torch.cuda.synchronize()
+
+    run_ms, full_ms, full_bytes = [], [], []
+    for rep in range(args.repeats):
+        reset()
+        torch.cuda.synchronize()
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        t_start.record(stream)
+        if graph is not None:
+            for j in range(args.steps):
+                graph.replay()
+        else:
+            f = plan._lib.oda_full_attn_if
+            for j in range(args.steps):
+                pos_hist[j].copy_(bufs.pos)
+                sd.fill_step(feed, wl, bufs.pos, t0)
+                plan.local()
+                plan.score()
+                for l, a in enumerate(plan.full_args):
+                    e0, e1 = ev[j * L + l]
+                    e0.record(stream)
+                    C.check(f(*a), "oda_full_attn_if")
+                    e1.record(stream)
+                plan.commit()
+                flags_hist[j].copy_(bufs.flag)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        run_ms.append(t_start.elapsed_time(t_end))
+        if graph is None:
+            fl = flags_hist.cpu().numpy().astype(np.int64)
+            ps = pos_hist.cpu().numpy().astype(np.int64)
+            full_bytes.append(float(np.sum(fl * (ps + 1)) * Hkv * d * 2 * 2 * L))
+            full_ms.append(sum(e0.elapsed_time(e1) for e0, e1 in ev))
+    assert int(ws[:4].view(torch.int32).item()) == 0, "device error bits set"
+
+    ms_total = statistics.median(run_ms)
+    ms_step = ms_total / args.steps
+    steps_per_s = 1000.0 / ms_step
+    # realised schedule and KV bytes of the (last) timed run
+    fl = flags_hist.cpu().numpy().astype(np.int64)
+    ps = pos_hist.cpu().numpy().astype(np.int64)
+    realised = float(fl.mean()) if graph is None else None
+    kv_local = 0
+    for b in range(B):
+        for j in range(args.steps):
+            t = int(wl.t0[b]) + j + 1
+            kv_local += min(t, wl.sink + wl.window)
+    kv_bytes_step = (kv_local + (float(np.sum(fl * (ps + 1))) if graph is None else rate * B * args.steps *
+                                 (float(np.mean(wl.t0)) + args.steps / 2))) * Hkv * d * 2 * 2 * L / args.steps
+    out = {
+        "metric": "ODA decode steps/s + KV HBM GB/s (% peak) at 128K ctx, 12.5% recall, 1 GPU",
+        "value": round(steps_per_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded generator, device-filled; random-init Xavier recall head)",
+        "config": {"workload": wl.name, "layers": L, "batch": B, "context": int(wl.t0[0]), "q_heads": Hq,
+                   "kv_heads": Hkv, "head_dim": d, "kv_layout": "contig", "recall_rate_target": rate,
+                   "recall_rate_realised": realised, "theta": theta, "tokens_per_s": round(steps_per_s * B, 1),
+                   "repeats": args.repeats, "timing": "hip-graph" if graph is not None else "eager+events"},
+        "kv_gbs": round(kv_bytes_step / (ms_step * 1e-3) / 1e9, 1),
+        "kv_frac_peak": round(kv_bytes_step / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    if graph is None and full_ms:
+        i = int(np.argsort(run_ms)[len(run_ms) // 2])
+        nlaunch = args.steps * L
+        avg_us = full_ms[i] * 1e3 / nlaunch
+        bytes_per_launch = full_bytes[i] / nlaunch
+        achieved = bytes_per_launch / (avg_us * 1e-6) / 1e9
+        out["roofline"] = {"bound": "hbm", "kernel": "k_attn_full (oda_full_attn_if)", "achieved": round(achieved, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                           "traffic": None, "avg_launch_us": round(avg_us, 2),
+                           "algorithmic_bytes_per_launch": int(bytes_per_launch)}
+    out["setup_s"] = round(setup_s, 1)
+    if args.rate_sweep:
+        out["rate_sweep"] = rate_sweep(args, wl, plan, bufs, step, reset, torch)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, blob, theta, realised if realised is not None else rate)
+    print(json.dumps(out), flush=True)
+
+
+def rate_sweep(args, wl, plan, bufs, step, reset, torch):
+    """Step time at forced full-branch rates (exact counts placed by seeded
+    uniforms), to show step time scaling with the recall rate."""
+    import synth
+    res = []
+    saved = bufs.force.clone()
+    for r in [float(x) for x in args.rate_sweep.split(",") if x]:
+        flags = synth.forced_rate_flags(wl.seed, args.steps, wl.batch, r)
+        fdev = torch.from_numpy(flags).to("cuda")
+        reset()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for j in range(args.steps):
+            bufs.force.copy_(fdev[j])
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        res.append({"rate": r, "ms_per_step": round(e0.elapsed_time(e1) / args.steps, 4)})
+    bufs.force.copy_(saved)
+    x = np.array([q["rate"] for q in res])
+    y = np.array([q["ms_per_step"] for q in res])
+    if len(res) >= 2:
+        slope, icpt = np.polyfit(x, y, 1)
+        pred = slope * x + icpt
+        r2 = 1 - np.sum((y - pred) ** 2) / max(np.sum((y - y.mean()) ** 2), 1e-30)
+        return {"points": res, "fit_ms_per_step": {"slope_per_unit_rate": round(float(slope), 4),
+                                                   "intercept": round(float(icpt), 4), "r2": round(float(r2), 5)}}
+    return {"points": res}
+
+
+def cpu_baseline(wl, blob, theta, rate):
+    """The oracle, untuned, on a bounded sample of the same workload: one
+    layer of local attention for one sequence, the recall head for every
+    sequence, and one layer of full attention for one sequence; scaled to a
+    whole step as 1 / (L * B * t_local + t_head + rate * B * L * t_full)."""
+    import synth
+    import oracle
+    from threadpoolctl import threadpool_info
+    L, B = wl.layers, wl.batch
+    j = 0
+    l = L - 1
+    inp = {k: synth.step_tensor(wl, k, j, l) for k in ("qL", "kL", "vL", "qF", "kF", "vF")}
+    emb = synth.embedding(wl, j)
+    h0 = synth.h_prev0(wl)
+    t0 = int(wl.t0[0])
+    # committed history of sequence 0 (input generation: not timed); the
+    # local branch reads only the sink and window rows of it
+    t = t0
+    lo = max(0, t - wl.window)
+    Kh = np.zeros((wl.hkv, t, wl.head_dim), np.uint16)
+    Vh = np.zeros((wl.hkv, t, wl.head_dim), np.uint16)
+    for g in range(wl.hkv):
+        Kh[g, :wl.sink] = synth.cache_rows(wl, synth.TAG_K, l, 0, g, 0, min(wl.sink, t))
+        Kh[g, lo:] = synth.cache_rows(wl, synth.TAG_K, l, 0, g, lo, t)
+        Vh[g, :wl.sink] = synth.cache_rows(wl, synth.TAG_V, l, 0, g, 0, min(wl.sink, t))
+        Vh[g, lo:] = synth.cache_rows(wl, synth.TAG_V, l, 0, g, lo, t)
+    P = oracle.unpack_head(blob, wl.hidden)
+    c0 = time.perf_counter()
+    oL0 = oracle.decode_attention(inp["qL"][0], Kh, Vh, inp["kL"][0], inp["vL"][0],
+                                  oracle.local_index_set(t + 1, wl.sink, wl.window))
+    t_local = time.perf_counter() - c0
+    c0 = time.perf_counter()
+    for b in range(B):
+        h_loc = oracle.f64_to_bf16(oL0.reshape(-1))
+        q = oracle.recall_score(P, h0[b], emb[b], h_loc)
+        oracle.branch_rule(q, theta)
+    t_head = time.perf_counter() - c0
+    # full history of sequence 0 for the full-branch sample
+    Kf = np.stack([synth.cache_rows(wl, synth.TAG_K, l, 0, g, 0, t0) for g in range(wl.hkv)])
+    Vf = np.stack([synth.cache_rows(wl, synth.TAG_V, l, 0, g, 0, t0) for g in range(wl.hkv)])
+    c0 = time.perf_counter()
+    oracle.decode_attention(inp["qF"][0], Kf, Vf, inp["kF"][0], inp["vF"][0], oracle.full_index_set(t0 + 1))
+    t_full = time.perf_counter() - c0
+    step_s = L * B * t_local + t_head + rate * B * L * t_full
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(1.0 / step_s, 5), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "host_cpus": os.cpu_count(),
+            "sample": (f"step 0, layer {l}: local attention of sequence 0 ({t_local:.2f} s), recall head "
+                       f"of all {B} ({t_head:.2f} s), full attention of sequence 0 over {t0 + 1} keys "
+                       f"({t_full:.2f} s); scaled to {L} layers x {B} sequences and {rate:.3f}*{B} flagged "
+                       f"sequences per step"),
+            "sample_cpu_s": round(t_local + t_head + t_full, 2)}
+
+
+if __name__ == "__main__":
+    main()

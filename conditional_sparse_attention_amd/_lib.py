@@ -92,7 +92,8 @@ def status_str(status: int) -> str:
     return lib().oda_status_str(int(status)).decode()
 
 
-def _check(status: int, fn: str) -> None:
+def check(status: int, fn: str) -> None:
+    """Raise OdaError for a non-zero status returned by the C function `fn`."""
     if status != ODA_OK:
         raise OdaError(status, fn)
 
@@ -149,7 +150,7 @@ def oda_head_param_count(hidden: int) -> int:
 
 def oda_head_offsets(hidden: int):
     arr = (ctypes.c_int64 * (ODA_HEAD_NTENSORS + 1))()
-    _check(lib().oda_head_offsets(hidden, arr), "oda_head_offsets")
+    check(lib().oda_head_offsets(hidden, arr), "oda_head_offsets")
     return [int(x) for x in arr]
 
 
@@ -165,31 +166,31 @@ def oda_workspace_worklist_offset(dims: oda_dims) -> int:
 
 
 def oda_workspace_init(dims, ws, stream=None) -> None:
-    _check(lib().oda_workspace_init(ctypes.byref(dims), _p(ws), _bytes(ws), _s(stream)), "oda_workspace_init")
+    check(lib().oda_workspace_init(ctypes.byref(dims), _p(ws), _bytes(ws), _s(stream)), "oda_workspace_init")
 
 
 def oda_local_ranges(dims, pos, ranges, stream=None) -> None:
-    _check(lib().oda_local_ranges(ctypes.byref(dims), _p(pos), _p(ranges), _s(stream)), "oda_local_ranges")
+    check(lib().oda_local_ranges(ctypes.byref(dims), _p(pos), _p(ranges), _s(stream)), "oda_local_ranges")
 
 
 def oda_local_attn(dims, layer, kv: oda_kv, pos, q, k_cur, v_cur, out, lse, ws, stream=None) -> None:
-    _check(lib().oda_local_attn(ctypes.byref(dims), layer, ctypes.byref(kv), _p(pos), _p(q), _p(k_cur), _p(v_cur),
+    check(lib().oda_local_attn(ctypes.byref(dims), layer, ctypes.byref(kv), _p(pos), _p(q), _p(k_cur), _p(v_cur),
                                 _p(out), _p(lse), _p(ws), _bytes(ws), _s(stream)), "oda_local_attn")
 
 
 def oda_recall_score(dims, head_w, h_prev, emb, h_local, theta, force, pos, score, flag, ws, stream=None) -> None:
-    _check(lib().oda_recall_score(ctypes.byref(dims), _p(head_w), _p(h_prev), _p(emb), _p(h_local),
+    check(lib().oda_recall_score(ctypes.byref(dims), _p(head_w), _p(h_prev), _p(emb), _p(h_local),
                                   ctypes.c_float(theta), _p(force), _p(pos), _p(score), _p(flag), _p(ws),
                                   _bytes(ws), _s(stream)), "oda_recall_score")
 
 
 def oda_full_attn_if(dims, layer, kv: oda_kv, pos, q, k_cur, v_cur, out, lse, ws, stream=None) -> None:
-    _check(lib().oda_full_attn_if(ctypes.byref(dims), layer, ctypes.byref(kv), _p(pos), _p(q), _p(k_cur),
+    check(lib().oda_full_attn_if(ctypes.byref(dims), layer, ctypes.byref(kv), _p(pos), _p(q), _p(k_cur),
                                   _p(v_cur), _p(out), _p(lse), _p(ws), _bytes(ws), _s(stream)), "oda_full_attn_if")
 
 
 def oda_commit(dims, kv: oda_kv, pos, flag, k_cur_L, v_cur_L, k_cur_F, v_cur_F, out_last_L, out_last_F, h_prev, ws,
                stream=None) -> None:
-    _check(lib().oda_commit(ctypes.byref(dims), ctypes.byref(kv), _p(pos), _p(flag), _p(k_cur_L), _p(v_cur_L),
+    check(lib().oda_commit(ctypes.byref(dims), ctypes.byref(kv), _p(pos), _p(flag), _p(k_cur_L), _p(v_cur_L),
                             _p(k_cur_F), _p(v_cur_F), _p(out_last_L), _p(out_last_F), _p(h_prev), _p(ws),
                             _bytes(ws), _s(stream)), "oda_commit")

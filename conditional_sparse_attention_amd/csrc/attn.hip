@@ -35,19 +35,34 @@ namespace oda {
 namespace {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const v4u_t gv4_t;
 
-// row blocks per lane per iteration: 4 (16 rows per wave) for G <= 2; 2 for
-// G = 4, which keeps four query heads' state in registers
+// How splits of one (b, g) hand their partials to the last one:
+//  1 (default): partials are written and read with agent-scope coherent
+//    accesses (no L2 write-back / invalidate); the ticket is taken after the
+//    workgroup's stores have been acknowledged;
+//  0: plain stores and a device-wide fence around the ticket.
+#ifndef ODA_SPLIT_SYNC
+#define ODA_SPLIT_SYNC 1
+#endif
+
+// Row blocks per lane per pipeline stage (a stage is 4*U rows of a wave).
+// Two stages are in flight: the next block's loads are issued before the
+// current block is consumed.
 template <int G>
 struct Unroll {
-  static constexpr int value = G >= 4 ? 2 : 4;
+  static constexpr int value = 2;
 };
 constexpr int kLocalWaves = 4;    // local kernel: 256 threads
 // full kernel: 1024 threads (16 waves) for G <= 2; 768 (12 waves, a larger
 // register budget) for G = 4
+#ifndef ODA_FULL_WAVES_SMALL_G
+#define ODA_FULL_WAVES_SMALL_G 12
+#endif
 template <int G>
 struct FullWaves {
-  static constexpr int value = G >= 4 ? 12 : 16;
+  static constexpr int value = G >= 4 ? 12 : ODA_FULL_WAVES_SMALL_G;
 };
 
 template <int CTRL>
@@ -156,32 +171,72 @@ __device__ __forceinline__ void block_update(const uint4 (&qv)[G], State<G>& st,
   }
 }
 
-// Rows [p_lo, p_hi) of the cache, interleaved over the NW waves in blocks of
-// 4*kUnroll rows.
-template <int G, bool PAGED, int NW>
-__device__ __forceinline__ void cache_rows(const AttnParams& P, const uint4 (&qv)[G], State<G>& st, int b, int g,
-                                           int p_lo, int p_hi, int wave, int r, int c) {
-  constexpr int kUnroll = Unroll<G>::value;
-  constexpr int kWaveRows = 4 * kUnroll;
-  for (int base = p_lo + wave * kWaveRows; base < p_hi; base += NW * kWaveRows) {
-    uint4 kk[kUnroll], vv[kUnroll];
-    bool ok[kUnroll];
+__device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
+  // streamed once: non-temporal global load (keeps L2 / MALL for reused data)
+  const v4u_t x = __builtin_nontemporal_load((gv4_t*)(p));
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
+
+// Loads one pipeline stage: rows base + u*4 + r (u < U) of this lane's row
+// group, clamped to p_hi - 1 and marked invalid beyond it.
+template <bool PAGED, int U>
+__device__ __forceinline__ void load_stage(const AttnParams& P, const uint16_t* Kbg, const uint16_t* Vbg, int b,
+                                           int g, int base, int p_hi, int r, int c, uint4 (&kk)[U], uint4 (&vv)[U],
+                                           bool (&ok)[U]) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int p = base + u * 4 + r;
-      bool valid = p < p_hi;
-      const int pp = valid ? p : p_hi - 1;
+  for (int u = 0; u < U; ++u) {
+    const int p = base + u * 4 + r;
+    bool valid = p < p_hi;
+    const int pp = valid ? p : p_hi - 1;
+    size_t off;
+    if (!PAGED) {
+      off = (size_t)pp * kHeadDim;
+    } else {
       bool bok = true;
-      const size_t row = row_index<PAGED>(P, b, g, pp, bok);
-      if (PAGED && !bok) {
+      off = row_index<true>(P, b, g, pp, bok) * kHeadDim;
+      if (!bok) {
         if (valid && c == 0) atomicOr(P.err, ODA_ERR_BLOCK);
         valid = false;
       }
-      ok[u] = valid;
-      kk[u] = *reinterpret_cast<const uint4*>(P.K + row * kHeadDim + c * 8);
-      vv[u] = *reinterpret_cast<const uint4*>(P.V + row * kHeadDim + c * 8);
     }
-    block_update<G>(qv, st, kk, vv, ok, P.scale_log2);
+    ok[u] = valid;
+    kk[u] = load_stream(Kbg + off + c * 8);
+    vv[u] = load_stream(Vbg + off + c * 8);
+  }
+}
+
+// Rows [p_lo, p_hi) of the cache.  Wave w takes stages starting at
+// p_lo + (k*NW + w) * 4U; two stages are in flight per wave (the loads of
+// the next stage are issued before the current one is consumed).
+template <int G, bool PAGED, int NW>
+__device__ __forceinline__ void cache_rows(const AttnParams& P, const uint4 (&qv)[G], State<G>& st, int b, int g,
+                                           int p_lo, int p_hi, int wave, int r, int c) {
+  constexpr int U = Unroll<G>::value;
+  constexpr int kStage = 4 * U;
+  constexpr int kStride = NW * kStage;
+  const uint16_t* Kbg = P.K;
+  const uint16_t* Vbg = P.V;
+  if (!PAGED) {
+    const size_t bg = ((size_t)b * P.Hkv + g) * (size_t)P.t_cap * kHeadDim;
+    Kbg += bg;
+    Vbg += bg;
+  }
+  int base = p_lo + wave * kStage;
+  if (base >= p_hi) return;
+  uint4 k0[U], v0[U], k1[U], v1[U];
+  bool o0[U], o1[U];
+  load_stage<PAGED, U>(P, Kbg, Vbg, b, g, base, p_hi, r, c, k0, v0, o0);
+  while (true) {
+    int nxt = base + kStride;
+    if (nxt < p_hi) load_stage<PAGED, U>(P, Kbg, Vbg, b, g, nxt, p_hi, r, c, k1, v1, o1);
+    block_update<G, U>(qv, st, k0, v0, o0, P.scale_log2);
+    if (nxt >= p_hi) break;
+    base = nxt;
+    nxt = base + kStride;
+    if (nxt < p_hi) load_stage<PAGED, U>(P, Kbg, Vbg, b, g, nxt, p_hi, r, c, k0, v0, o0);
+    block_update<G, U>(qv, st, k1, v1, o1, P.scale_log2);
+    if (nxt >= p_hi) break;
+    base = nxt;
   }
 }
 
@@ -206,6 +261,54 @@ __device__ __forceinline__ void current_row(const AttnParams& P, const uint4 (&q
 }
 
 __device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(x, m, 64); }
+
+// Partials cross workgroups (and XCDs, whose L2s are not coherent with each
+// other): store / load them with agent-scope coherent accesses.
+__device__ __forceinline__ void part_store(float* p, float v) {
+#if ODA_SPLIT_SYNC
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#else
+  *p = v;
+#endif
+}
+__device__ __forceinline__ float part_load(const float* p) {
+#if ODA_SPLIT_SYNC
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#else
+  return *p;
+#endif
+}
+
+// Takes the (b, g) ticket after this workgroup's partial is visible;
+// returns true in the workgroup that completes the set.
+__device__ __forceinline__ bool take_ticket(int32_t* ticket, int nsplit) {
+  __shared__ int s_last;
+#if ODA_SPLIT_SYNC
+  // every coherent store of this wave has been acknowledged (gfx9 counts
+  // stores in vmcnt), then all waves meet, then one thread takes the ticket
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
+  __syncthreads();
+  return s_last;
+#else
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(ticket, 1) == nsplit - 1;
+  __syncthreads();
+  if (s_last) __threadfence();
+  return s_last;
+#endif
+}
+
+__device__ __forceinline__ void reset_ticket(int32_t* ticket) {
+#if ODA_SPLIT_SYNC
+  __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#else
+  atomicExch(ticket, 0);
+#endif
+}
 
 // Merge the 4 row groups of each wave (shuffles), then the NW waves (LDS).
 // On return, threads idx < G*128 hold (M, L, O) of (head idx/128, dim idx%128)
@@ -279,8 +382,8 @@ __device__ __noinline__ void merge_partials(const AttnParams& P, const float* pa
   for (int i = threadIdx.x; i < nsplit * G; i += NT) {
     const int s = i / G, h = i % G;
     const float* pp = part + ((size_t)s * G + h) * kPartStride;
-    sm[i] = pp[kHeadDim];
-    sl[i] = pp[kHeadDim + 1];
+    sm[i] = part_load(pp + kHeadDim);
+    sl[i] = part_load(pp + kHeadDim + 1);
   }
   __syncthreads();
   // thread -> (head, dim4, split group)
@@ -299,7 +402,8 @@ __device__ __noinline__ void merge_partials(const AttnParams& P, const float* pa
   if (sg < kGroups) {
 #pragma unroll 4
     for (int s = sg; s < nsplit; s += kGroups) {
-      const float4 a = *reinterpret_cast<const float4*>(part + ((size_t)s * G + h) * kPartStride + d4 * 4);
+      const float* pa = part + ((size_t)s * G + h) * kPartStride + d4 * 4;
+      const float4 a = make_float4(part_load(pa), part_load(pa + 1), part_load(pa + 2), part_load(pa + 3));
       const float w = fast_exp2(sm[s * G + h] - M);
       L = fmaf(sl[s * G + h], w, L);
       O.x = fmaf(a.x, w, O.x);
@@ -400,24 +504,15 @@ __device__ void attn_unit(const AttnParams& P, int b, int g, int split, int nspl
     float M, L, O;
     wg_value<G, NW>(lds, h, dd, M, L, O);
     float* pp = part_bg + ((size_t)split * G + h) * kPartStride;
-    pp[dd] = O;
+    part_store(pp + dd, O);
     if (dd == 0) {
-      pp[kHeadDim] = M;
-      pp[kHeadDim + 1] = L;
+      part_store(pp + kHeadDim, M);
+      part_store(pp + kHeadDim + 1, L);
     }
   }
-  __threadfence();
-  __syncthreads();
-  __shared__ int s_last;
-  if (tid == 0) {
-    const int prev = atomicAdd(ticket, 1);
-    s_last = (prev == nsplit - 1);
-  }
-  __syncthreads();
-  if (s_last) {
-    __threadfence();
+  if (take_ticket(ticket, nsplit)) {
     merge_partials<G, NW>(P, part_bg, nsplit, b, g, lds);
-    if (tid == 0) atomicExch(ticket, 0);
+    if (tid == 0) reset_ticket(ticket);
   }
   __syncthreads();
 }

@@ -13,7 +13,7 @@ namespace oda {
 
 constexpr int kHeadDim = 128;
 constexpr int kMaxBatch = 32;
-constexpr int kLocalMaxSplits = 8;     // splits of one (sequence, KV head) in the local branch
+constexpr int kLocalMaxSplits = 16;    // splits of one (sequence, KV head) in the local branch
 constexpr int kLocalMinChunk = 64;     // fewer keys than this per split is not worth a split
 constexpr int kPartStride = 132;       // floats per partial: acc[128], m, l, 2 pad (16-B aligned)
 constexpr int kTower = ODA_HEAD_TOWER;

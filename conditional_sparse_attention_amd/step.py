@@ -85,18 +85,18 @@ class StepPlan:
     def local(self) -> None:
         f = self._lib.oda_local_attn
         for a in self.local_args:
-            C._check(f(*a), "oda_local_attn")
+            C.check(f(*a), "oda_local_attn")
 
     def score(self) -> None:
-        C._check(self._lib.oda_recall_score(*self.score_args), "oda_recall_score")
+        C.check(self._lib.oda_recall_score(*self.score_args), "oda_recall_score")
 
     def full(self) -> None:
         f = self._lib.oda_full_attn_if
         for a in self.full_args:
-            C._check(f(*a), "oda_full_attn_if")
+            C.check(f(*a), "oda_full_attn_if")
 
     def commit(self) -> None:
-        C._check(self._lib.oda_commit(*self.commit_args), "oda_commit")
+        C.check(self._lib.oda_commit(*self.commit_args), "oda_commit")
 
     def run(self) -> None:
         """One whole decode step on the plan's stream."""

@@ -34,7 +34,7 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 
 __device__ __forceinline__ uint16_t value_of(uint32_t w) {
   const int x = (int)(w & 0xFFu) + (int)((w >> 8) & 0xFFu) + (int)((w >> 16) & 0xFFu) + (int)(w >> 24) - 510;
-  const float scale = __uint_as_float(0x3BDDB4E6u);  // float32(1/sqrt(21845))
+  const float scale = __uint_as_float(0x3BDDB446u);  // float32(1/sqrt(21845))
   return bf16_rne(__fmul_rn((float)x, scale));
 }
 

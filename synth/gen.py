@@ -40,7 +40,7 @@ MIX1 = 0xBF58476D1CE4E5B9
 MIX2 = 0x94D049BB133111EB
 MASK64 = (1 << 64) - 1
 
-VALUE_SCALE = np.float32(1.0 / math.sqrt(21845.0))  # 0x3BDDB4E6 bit pattern below
+VALUE_SCALE = np.float32(1.0 / math.sqrt(21845.0))  # bit pattern 0x3BDDB446
 assert VALUE_SCALE.view(np.uint32) == np.uint32(1004385350)
 
 # Stream tags.

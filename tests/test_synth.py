@@ -53,3 +53,13 @@ def test_block_tables_are_a_permutation():
 def test_forced_rate_flags_exact_count():
     f = synth.forced_rate_flags(3, 128, 4, 0.125)
     assert f.sum() == 64 and f.shape == (128, 4)
+
+
+def test_device_source_uses_the_same_scale_bits():
+    """The device generator hard-codes float32(1/sqrt(21845)); it must be the
+    host constant's bit pattern."""
+    import os
+    import re
+    src = open(os.path.join(os.path.dirname(synth.__file__), "csrc", "fill.hip")).read()
+    m = re.search(r"__uint_as_float\(0x([0-9A-Fa-f]+)u\)", src)
+    assert m and int(m.group(1), 16) == int(synth.VALUE_SCALE.view(np.uint32))
