@@ -47,6 +47,22 @@ typedef __attribute__((address_space(1))) const v4u_t gv4_t;
 #define ODA_SPLIT_SYNC 1
 #endif
 
+#ifndef ODA_LOCAL_DEPTH
+#define ODA_LOCAL_DEPTH 4
+#endif
+#ifndef ODA_FULL_DEPTH
+#define ODA_FULL_DEPTH 2
+#endif
+#ifndef ODA_LOCAL_SPLITS
+#define ODA_LOCAL_SPLITS 16
+#endif
+#ifndef ODA_LOCAL_WAVES
+#define ODA_LOCAL_WAVES 4
+#endif
+#ifndef ODA_FULL_WAVES_SMALL_G
+#define ODA_FULL_WAVES_SMALL_G 12
+#endif
+
 // Row blocks per lane per pipeline stage (a stage is 4*U rows of a wave).
 // Two stages are in flight: the next block's loads are issued before the
 // current block is consumed.
@@ -54,15 +70,18 @@ template <int G>
 struct Unroll {
   static constexpr int value = 2;
 };
-constexpr int kLocalWaves = 4;    // local kernel: 256 threads
-// full kernel: 1024 threads (16 waves) for G <= 2; 768 (12 waves, a larger
-// register budget) for G = 4
-#ifndef ODA_FULL_WAVES_SMALL_G
-#define ODA_FULL_WAVES_SMALL_G 12
-#endif
+constexpr int kLocalWaves = ODA_LOCAL_WAVES;  // local kernel workgroup
+// Full kernel shape per group size: G = 2 (the 16/8-head models) runs 12
+// waves (3 per SIMD) with a 2-stage ring; G = 1 and G = 4 keep more state per
+// lane and run 8 waves with a 4-stage ring, which keeps a similar number of
+// bytes in flight per CU without spilling.
 template <int G>
 struct FullWaves {
-  static constexpr int value = G >= 4 ? 12 : ODA_FULL_WAVES_SMALL_G;
+  static constexpr int value = G == 2 ? ODA_FULL_WAVES_SMALL_G : 8;
+};
+template <int G>
+struct FullDepth {
+  static constexpr int value = G == 2 ? ODA_FULL_DEPTH : 4;
 };
 
 template <int CTRL>
@@ -206,9 +225,9 @@ __device__ __forceinline__ void load_stage(const AttnParams& P, const uint16_t* 
 }
 
 // Rows [p_lo, p_hi) of the cache.  Wave w takes stages starting at
-// p_lo + (k*NW + w) * 4U; two stages are in flight per wave (the loads of
-// the next stage are issued before the current one is consumed).
-template <int G, bool PAGED, int NW>
+// p_lo + (k*NW + w) * 4U.  A ring of DEPTH register stages keeps DEPTH-1
+// stages in flight while one is consumed; its refill is issued right after.
+template <int G, bool PAGED, int NW, int DEPTH>
 __device__ __forceinline__ void cache_rows(const AttnParams& P, const uint4 (&qv)[G], State<G>& st, int b, int g,
                                            int p_lo, int p_hi, int wave, int r, int c) {
   constexpr int U = Unroll<G>::value;
@@ -221,22 +240,28 @@ __device__ __forceinline__ void cache_rows(const AttnParams& P, const uint4 (&qv
     Kbg += bg;
     Vbg += bg;
   }
-  int base = p_lo + wave * kStage;
-  if (base >= p_hi) return;
-  uint4 k0[U], v0[U], k1[U], v1[U];
-  bool o0[U], o1[U];
-  load_stage<PAGED, U>(P, Kbg, Vbg, b, g, base, p_hi, r, c, k0, v0, o0);
-  while (true) {
-    int nxt = base + kStride;
-    if (nxt < p_hi) load_stage<PAGED, U>(P, Kbg, Vbg, b, g, nxt, p_hi, r, c, k1, v1, o1);
-    block_update<G, U>(qv, st, k0, v0, o0, P.scale_log2);
-    if (nxt >= p_hi) break;
-    base = nxt;
-    nxt = base + kStride;
-    if (nxt < p_hi) load_stage<PAGED, U>(P, Kbg, Vbg, b, g, nxt, p_hi, r, c, k0, v0, o0);
-    block_update<G, U>(qv, st, k1, v1, o1, P.scale_log2);
-    if (nxt >= p_hi) break;
-    base = nxt;
+  const int first = p_lo + wave * kStage;
+  if (first >= p_hi) return;
+  uint4 kk[DEPTH][U], vv[DEPTH][U];
+  bool ok[DEPTH][U];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) {
+    const int bs = first + d * kStride;
+    if (bs < p_hi) load_stage<PAGED, U>(P, Kbg, Vbg, b, g, bs, p_hi, r, c, kk[d], vv[d], ok[d]);
+  }
+  int cur = first;
+  bool done = false;
+  while (!done) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      if (!done) {
+        block_update<G, U>(qv, st, kk[d], vv[d], ok[d], P.scale_log2);
+        const int refill = cur + DEPTH * kStride;
+        if (refill < p_hi) load_stage<PAGED, U>(P, Kbg, Vbg, b, g, refill, p_hi, r, c, kk[d], vv[d], ok[d]);
+        cur += kStride;
+        done = cur >= p_hi;
+      }
+    }
   }
 }
 
@@ -371,83 +396,93 @@ __device__ __forceinline__ void write_out(const AttnParams& P, int b, int hq, in
   }
 }
 
-// Final merge of nsplit partials of (b, g) by the last workgroup, in split
-// order.  Kept out of line so its registers do not add to the main loop's.
-template <int G, int NW>
-__device__ __noinline__ void merge_partials(const AttnParams& P, const float* part, int nsplit, int b, int g, float* lds) {
+// Final merge of nsplit (<= MAXS) partials of (b, g) by the last workgroup.
+// Thread (group sg, head h, dims 4*d4..) issues all its coherent loads (m, l,
+// acc of splits sg, sg + groups, ...) in one batch, merges them in split
+// order, and the groups are then merged in group order through LDS, so the
+// result does not depend on timing.
+template <int G, int NW, int MAXS>
+__device__ __forceinline__ void merge_partials(const AttnParams& P, const float* part, int nsplit, int b, int g,
+                                               float* lds) {
   constexpr int NT = NW * 64;
-  // stage (m, l) of every (split, head) in LDS
-  float* sm = lds;                       // [nsplit][G]
-  float* sl = lds + nsplit * G;          // [nsplit][G]
-  for (int i = threadIdx.x; i < nsplit * G; i += NT) {
-    const int s = i / G, h = i % G;
-    const float* pp = part + ((size_t)s * G + h) * kPartStride;
-    sm[i] = part_load(pp + kHeadDim);
-    sl[i] = part_load(pp + kHeadDim + 1);
-  }
-  __syncthreads();
-  // thread -> (head, dim4, split group)
-  constexpr int kLanesPerSplit = G * (kHeadDim / 4);  // (h, d4) pairs
-  constexpr int kGroups = NT / kLanesPerSplit;
-  static_assert(kGroups >= 1, "block too small for the merge");
+  constexpr int kLanes = G * (kHeadDim / 4);  // (h, d4) pairs
+  constexpr int kGroups = NT / kLanes;
+  static_assert(kGroups >= 1 && kGroups * kLanes == NT, "block shape does not fit the merge");
+  constexpr int kPer = (MAXS + kGroups - 1) / kGroups;
   const int tid = threadIdx.x;
-  const int hd = tid % kLanesPerSplit;
-  const int sg = tid / kLanesPerSplit;
+  const int hd = tid % kLanes;
+  const int sg = tid / kLanes;
   const int h = hd / (kHeadDim / 4);
   const int d4 = hd % (kHeadDim / 4);
-  float M = kNegBig;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, sm[s * G + h]);
-  float L = 0.0f;
-  float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (sg < kGroups) {
-#pragma unroll 4
-    for (int s = sg; s < nsplit; s += kGroups) {
-      const float* pa = part + ((size_t)s * G + h) * kPartStride + d4 * 4;
-      const float4 a = make_float4(part_load(pa), part_load(pa + 1), part_load(pa + 2), part_load(pa + 3));
-      const float w = fast_exp2(sm[s * G + h] - M);
-      L = fmaf(sl[s * G + h], w, L);
-      O.x = fmaf(a.x, w, O.x);
-      O.y = fmaf(a.y, w, O.y);
-      O.z = fmaf(a.z, w, O.z);
-      O.w = fmaf(a.w, w, O.w);
+  float m[kPer], l[kPer];
+  float4 a[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int s = sg + k * kGroups;
+    if (s < nsplit) {
+      const float* pp = part + ((size_t)s * G + h) * kPartStride;
+      m[k] = part_load(pp + kHeadDim);
+      l[k] = part_load(pp + kHeadDim + 1);
+      a[k] = make_float4(part_load(pp + d4 * 4), part_load(pp + d4 * 4 + 1), part_load(pp + d4 * 4 + 2),
+                         part_load(pp + d4 * 4 + 3));
+    } else {
+      m[k] = kNegBig;
+      l[k] = 0.0f;
+      a[k] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
+  float M = kNegBig;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) M = fmaxf(M, m[k]);
+  float L = 0.0f;
+  float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const float w = fast_exp2(m[k] - M);
+    L = fmaf(l[k], w, L);
+    O.x = fmaf(a[k].x, w, O.x);
+    O.y = fmaf(a[k].y, w, O.y);
+    O.z = fmaf(a[k].z, w, O.z);
+    O.w = fmaf(a[k].w, w, O.w);
+  }
+  float* red = lds;  // [kGroups][kLanes][6]
   __syncthreads();
-  // reduce the split groups in fixed order through LDS
-  float* red = lds;  // [kGroups][kLanesPerSplit][5]
-  if (sg < kGroups) {
-    float* r = red + ((size_t)sg * kLanesPerSplit + hd) * 5;
-    r[0] = O.x;
-    r[1] = O.y;
-    r[2] = O.z;
-    r[3] = O.w;
-    r[4] = L;
+  {
+    float* r = red + ((size_t)sg * kLanes + hd) * 6;
+    r[0] = M;
+    r[1] = L;
+    r[2] = O.x;
+    r[3] = O.y;
+    r[4] = O.z;
+    r[5] = O.w;
   }
   __syncthreads();
   if (sg == 0) {
-    float4 Ot = make_float4(0.f, 0.f, 0.f, 0.f);
+    float Mt = kNegBig;
+    for (int k = 0; k < kGroups; ++k) Mt = fmaxf(Mt, red[((size_t)k * kLanes + hd) * 6]);
     float Lt = 0.0f;
-#pragma unroll 1
+    float4 Ot = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int k = 0; k < kGroups; ++k) {
-      const float* r = red + ((size_t)k * kLanesPerSplit + hd) * 5;
-      Ot.x += r[0];
-      Ot.y += r[1];
-      Ot.z += r[2];
-      Ot.w += r[3];
-      Lt += r[4];
+      const float* r = red + ((size_t)k * kLanes + hd) * 6;
+      const float w = fast_exp2(r[0] - Mt);
+      Lt = fmaf(r[1], w, Lt);
+      Ot.x = fmaf(r[2], w, Ot.x);
+      Ot.y = fmaf(r[3], w, Ot.y);
+      Ot.z = fmaf(r[4], w, Ot.z);
+      Ot.w = fmaf(r[5], w, Ot.w);
     }
     const int hq = g * G + h;
-    write_out(P, b, hq, d4 * 4 + 0, M, Lt, Ot.x);
-    write_out(P, b, hq, d4 * 4 + 1, M, Lt, Ot.y);
-    write_out(P, b, hq, d4 * 4 + 2, M, Lt, Ot.z);
-    write_out(P, b, hq, d4 * 4 + 3, M, Lt, Ot.w);
+    write_out(P, b, hq, d4 * 4 + 0, Mt, Lt, Ot.x);
+    write_out(P, b, hq, d4 * 4 + 1, Mt, Lt, Ot.y);
+    write_out(P, b, hq, d4 * 4 + 2, Mt, Lt, Ot.z);
+    write_out(P, b, hq, d4 * 4 + 3, Mt, Lt, Ot.w);
   }
 }
 
 // One unit: keys of S with virtual indices [v_lo, v_hi) where S = [0, n0)
 // followed by [s1, t); the last virtual index (n0 + t - s1 - 1) is the
 // current token and is read from staging.
-template <int G, bool PAGED, int NW>
+template <int G, bool PAGED, int NW, int DEPTH, int MAXS>
 __device__ void attn_unit(const AttnParams& P, int b, int g, int split, int nsplit, int v_lo, int v_hi,
                           const LocalSet& S, int32_t* ticket, float* part_bg, float* lds) {
   const int tid = threadIdx.x;
@@ -476,12 +511,12 @@ __device__ void attn_unit(const AttnParams& P, int b, int g, int split, int nspl
   // first range [0, n0) -> positions equal virtual indices
   if (v_lo < S.n0) {
     const int hi = v_cache_hi < S.n0 ? v_cache_hi : S.n0;
-    if (hi > v_lo) cache_rows<G, PAGED, NW>(P, qv, st, b, g, v_lo, hi, wave, r, c);
+    if (hi > v_lo) cache_rows<G, PAGED, NW, DEPTH>(P, qv, st, b, g, v_lo, hi, wave, r, c);
   }
   // second range: virtual n0 + k  ->  position s1 + k
   {
     const int lo = v_lo > S.n0 ? v_lo : S.n0;
-    if (v_cache_hi > lo) cache_rows<G, PAGED, NW>(P, qv, st, b, g, S.s1 + (lo - S.n0), S.s1 + (v_cache_hi - S.n0), wave, r, c);
+    if (v_cache_hi > lo) cache_rows<G, PAGED, NW, DEPTH>(P, qv, st, b, g, S.s1 + (lo - S.n0), S.s1 + (v_cache_hi - S.n0), wave, r, c);
   }
   if (has_current) current_row<G>(P, qv, st, b, g, wave, r, c);
 
@@ -511,7 +546,7 @@ __device__ void attn_unit(const AttnParams& P, int b, int g, int split, int nspl
     }
   }
   if (take_ticket(ticket, nsplit)) {
-    merge_partials<G, NW>(P, part_bg, nsplit, b, g, lds);
+    merge_partials<G, NW, MAXS>(P, part_bg, nsplit, b, g, lds);
     if (tid == 0) reset_ticket(ticket);
   }
   __syncthreads();
@@ -519,12 +554,10 @@ __device__ void attn_unit(const AttnParams& P, int b, int g, int split, int nspl
 
 template <int G, int NW>
 constexpr int lds_floats() {
-  // wg_merge needs NW*G*(128+2) floats; merge_partials needs 2*nsplit*G
-  // (nsplit <= 32) for the (m, l) staging, then NW*64*5 for the group reduce.
+  // wg_merge needs NW*G*(128+2) floats; merge_partials NW*64*6
   constexpr int a = NW * G * (kHeadDim + 2);
-  constexpr int b = 5 * NW * 64;
-  constexpr int c = 2 * (kFullMaxSplits > kLocalMaxSplits ? kFullMaxSplits : kLocalMaxSplits) * G;
-  return a > b ? (a > c ? a : c) : (b > c ? b : c);
+  constexpr int b = 6 * NW * 64;
+  return a > b ? a : b;
 }
 
 template <int G, bool PAGED>
@@ -541,13 +574,13 @@ __global__ void __launch_bounds__(kLocalWaves * 64) k_attn_local(AttnParams P) {
   const LocalSet S = local_set(t, P.sink, P.window);
   const int n = S.size();
   int ns = (n + kLocalMinChunk - 1) / kLocalMinChunk;
-  ns = ns < kLocalMaxSplits ? ns : kLocalMaxSplits;
+  ns = ns < ODA_LOCAL_SPLITS ? ns : ODA_LOCAL_SPLITS;
   const int chunk = (n + ns - 1) / ns;
   if (split >= ns) return;
   const int v_lo = split * chunk;
   const int v_hi = (v_lo + chunk) < n ? v_lo + chunk : n;
   float* part_bg = P.part + ((size_t)(b * P.Hkv + g) * kLocalMaxSplits) * G * kPartStride;
-  attn_unit<G, PAGED, NW>(P, b, g, split, ns, v_lo, v_hi, S, P.tickets + b * P.Hkv + g, part_bg, lds);
+  attn_unit<G, PAGED, NW, ODA_LOCAL_DEPTH, ODA_LOCAL_SPLITS>(P, b, g, split, ns, v_lo, v_hi, S, P.tickets + b * P.Hkv + g, part_bg, lds);
 }
 
 template <int G, bool PAGED>
@@ -579,13 +612,14 @@ __global__ void __launch_bounds__(FullWaves<G>::value * 64) k_attn_full(AttnPara
     S.s1 = t;
     S.t = t;
     float* part_bg = P.part + ((size_t)(b * P.Hkv + g) * kFullMaxSplits) * G * kPartStride;
-    attn_unit<G, PAGED, NW>(P, b, g, split, ns, v_lo, v_hi, S, P.tickets + b * P.Hkv + g, part_bg, lds);
+    attn_unit<G, PAGED, NW, FullDepth<G>::value, kFullMaxSplits>(P, b, g, split, ns, v_lo, v_hi, S, P.tickets + b * P.Hkv + g, part_bg, lds);
   }
 }
 
 template <int G, bool PAGED>
 int launch_local_t(const AttnParams& p, hipStream_t s) {
-  dim3 grid(kLocalMaxSplits, p.Hkv, p.B);
+  static_assert(ODA_LOCAL_SPLITS <= kLocalMaxSplits, "local splits exceed the workspace slots");
+  dim3 grid(ODA_LOCAL_SPLITS, p.Hkv, p.B);
   hipLaunchKernelGGL((k_attn_local<G, PAGED>), grid, dim3(kLocalWaves * 64), 0, s, p);
   return hipGetLastError() == hipSuccess ? ODA_OK : ODA_E_LAUNCH;
 }
