@@ -252,3 +252,117 @@ def replay_step(pr: Problem, j: int, *, theta: float, force=None, check_layers=N
             assert np.array_equal(ks, Kh[l, b, :, p]) and np.array_equal(vs, Vh[l, b, :, p]), \
                 f"step {j} l={l} b={b}: committed slot"
     return {"flag": flag.copy(), "score": score.copy(), "lseL": lseL}
+
+
+class BigProblem:
+    """A workload at full size: cache and per-step inputs filled on the
+    device by the generator, no host copy of the cache.  The oracle checks
+    sampled outputs, regenerating the rows it needs from G plus the slots
+    committed by earlier steps (whose branch the recorded GPU flags give)."""
+
+    def __init__(self, wl: synth.Workload, *, head_perturb: bool = False):
+        import synth.device as sd
+        self.sd = sd
+        self.pr = Problem(wl, head_perturb=head_perturb, host_cache=False, lse=False)
+        self.wl = wl
+        self.flags = []      # GPU flags per step
+        self.feed = {"qL": self.pr.bufs.qL, "qF": self.pr.bufs.qF, "kL": self.pr.bufs.kL, "vL": self.pr.bufs.vL,
+                     "kF": self.pr.bufs.kF, "vF": self.pr.bufs.vF, "e": self.pr.bufs.emb}
+
+    def run_step(self, j: int, theta: float, force) -> dict:
+        pr, wl = self.pr, self.wl
+        L, B, Hq, d = wl.layers, wl.batch, wl.hq, wl.head_dim
+        pos_before = pr.bufs.pos.cpu().numpy().copy()
+        assert np.all(pos_before == wl.t0 + j)
+        self.sd.fill_step(self.feed, wl, pr.bufs.pos, pr.t0_dev)
+        pr.set_force(force)
+        pr.plan.set_theta(theta)
+        h_prev_before = from_dev_u16(pr.bufs.h_prev)
+        pr.bufs.oF.fill_(0x7FC1)
+        pr.plan.run()
+        torch.cuda.synchronize()
+        rec = {"j": j, "pos": pos_before, "h_prev": h_prev_before, "oL": from_dev_u16(pr.bufs.oL),
+               "oF": from_dev_u16(pr.bufs.oF), "score": pr.bufs.score.cpu().numpy().copy(),
+               "flag": pr.bufs.flag.cpu().numpy().copy(), "worklist": pr.worklist(),
+               "h_prev_after": from_dev_u16(pr.bufs.h_prev), "pos_after": pr.bufs.pos.cpu().numpy().copy(),
+               "theta": theta, "force": np.asarray(force)}
+        assert pr.ws_error_word() == 0
+        self.flags.append(rec["flag"])
+        return rec
+
+    def history(self, l: int, b: int, g: int, j: int, rows: np.ndarray):
+        """K, V bits [len(rows)][d] of logical positions `rows` as committed
+        before step j."""
+        wl = self.wl
+        t0 = int(wl.t0[b])
+        K = np.zeros((len(rows), wl.head_dim), np.uint16)
+        V = np.zeros_like(K)
+        old = rows < t0
+        if np.any(old):
+            idx = np.nonzero(old)[0]
+            r = rows[idx]
+            # contiguous runs of positions
+            cuts = np.nonzero(np.diff(r) != 1)[0] + 1
+            for seg_i, seg_r in zip(np.split(idx, cuts), np.split(r, cuts)):
+                lo, hi = int(seg_r[0]), int(seg_r[-1]) + 1
+                K[seg_i] = synth.cache_rows(wl, synth.TAG_K, l, b, g, lo, hi)
+                V[seg_i] = synth.cache_rows(wl, synth.TAG_V, l, b, g, lo, hi)
+        for i in np.nonzero(~old)[0]:
+            jj = int(rows[i]) - t0
+            assert jj < j
+            br = "F" if self.flags[jj][b] else "L"
+            K[i] = synth.step_tensor(wl, "k" + br, jj, l)[b, g]
+            V[i] = synth.step_tensor(wl, "v" + br, jj, l)[b, g]
+        return K, V
+
+    def check(self, rec: dict, samples, full_samples) -> None:
+        """Checks every score / flag / work-list entry / commit of the step,
+        and the attention outputs of the sampled (l, b, g)."""
+        wl, pr = self.wl, self.pr
+        L, B, Hq, Hkv, d = wl.layers, wl.batch, wl.hq, wl.hkv, wl.head_dim
+        G = Hq // Hkv
+        j = rec["j"]
+        P = pr.head_params()
+        emb = synth.embedding(wl, j)
+        flag = rec["flag"]
+        for b in range(B):
+            q = recall_score(P, rec["h_prev"][b], emb[b], rec["oL"][L - 1, b].reshape(-1))
+            assert abs(float(rec["score"][b]) - q) <= SCORE_TOL * (1 + abs(q)), (j, b, rec["score"][b], q)
+            f = int(rec["force"][b])
+            if f >= 0 or abs(q - rec["theta"]) >= TIE_BAND:
+                assert int(flag[b]) == branch_rule(q, rec["theta"], f), (j, b, q)
+        want = [(b, s) for b in range(B) if flag[b] for s in range(full_nsplit(int(rec["pos"][b]) + 1))]
+        assert rec["worklist"] == want
+        for b in range(B):
+            if not flag[b]:
+                assert np.all(rec["oF"][:, b] == 0x7FC1), "unflagged full rows written"
+        # commit, all b, sampled layers
+        assert np.array_equal(rec["pos_after"], rec["pos"] + 1)
+        for b in range(B):
+            o_last = rec["oF"][L - 1, b] if flag[b] else rec["oL"][L - 1, b]
+            assert np.array_equal(rec["h_prev_after"][b], o_last.reshape(-1))
+            p = int(rec["pos"][b])
+            br = "F" if flag[b] else "L"
+            for l in sorted({0, L - 1}):
+                ks, vs = pr.cache_slot(l, b, p)
+                assert np.array_equal(ks, synth.step_tensor(wl, "k" + br, j, l)[b])
+                assert np.array_equal(vs, synth.step_tensor(wl, "v" + br, j, l)[b])
+        # attention outputs
+        for kind, smp in (("L", samples), ("F", full_samples)):
+            for (l, b, g) in smp:
+                if kind == "F" and not flag[b]:
+                    continue
+                p = int(rec["pos"][b])
+                S = local_index_set(p + 1, wl.sink, wl.window) if kind == "L" else full_index_set(p + 1)
+                rows = S[S < p]
+                K, V = self.history(l, b, g, j, rows)
+                Kh = np.zeros((1, p, d), np.uint16)
+                Vh = np.zeros_like(Kh)
+                Kh[0, rows] = K
+                Vh[0, rows] = V
+                qv = synth.step_tensor(wl, "q" + kind, j, l)[b, g * G:(g + 1) * G]
+                kc = synth.step_tensor(wl, "k" + kind, j, l)[b, g:g + 1]
+                vc = synth.step_tensor(wl, "v" + kind, j, l)[b, g:g + 1]
+                ref = decode_attention(qv, Kh, Vh, kc, vc, S)
+                got = (rec["oL"] if kind == "L" else rec["oF"])[l, b, g * G:(g + 1) * G]
+                assert_close_bf16(got, ref, f"{wl.name} step {j} {kind} l={l} b={b} g={g} pos={p}")
