@@ -14,13 +14,16 @@ kernel that writes the step's synthetic q/k/v/embedding.
 
 Protocol: a calibration pass with theta = +inf (all local) records the
 head's scores and sets theta to the midpoint between the k-th and (k+1)-th
-largest, k = round(0.125 * B * steps); the state is reset; W warm-up steps;
-then the timed region (K steps) is run REPEATS times from the same start
-state and the median is reported (warm throughput).  Each launch of the
-full-attention kernel is bracketed by HIP events on its stream, giving its
-average duration inside the timed region; the algorithmic bytes of a launch
-are t_b * 4096 B (K and V of every key of every flagged sequence, incl. the
-staged current token) summed over the sequences the flags select.
+largest, k = round(0.125 * B * steps); the state is reset; W warm-up steps.
+The timed region is K steps replayed from one captured HIP graph (the step
+has no host synchronisation, so it is one graph), run REPEATS times from the
+same start state; the median is the reported warm throughput.  The same K
+steps are then launched one call at a time, the L back-to-back
+full-attention launches of each step bracketed by a pair of HIP events on
+their stream: that gives the dominant kernel's average launch duration and, from the recorded flags and positions, its
+algorithmic bytes per launch, t_b * 4096 B (K and V of every key of every
+flagged sequence, including the staged current token).  Both passes run the
+same kernels on the same inputs, so they follow the same trajectory.
 
 Prints one JSON line.
 """
@@ -47,8 +50,9 @@ def parse():
     ap.add_argument("--repeats", type=int, default=3)
     ap.add_argument("--workload", default="3", help="workload key (default 3: 128K, B=4, 12.5%% recall)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", action="store_true", help="replay the step as one HIP graph (no per-launch events)")
     ap.add_argument("--rate-sweep", default="", help="comma list of forced full-branch rates to time as well")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -130,67 +134,79 @@ def run(args, wl, stream, torch, synth, sd, C, StepBuffers, StepPlan, dev):
         step()
     torch.cuda.synchronize()
 
-    # ---- timed region(s)
-    flags_hist = torch.zeros((args.steps, B), dtype=torch.uint8, device=dev)
-    pos_hist = torch.zeros((args.steps, B), dtype=torch.int32, device=dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps * L)]
-    graph = None
-    if args.graph:
-        reset()
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            step()
-        torch.cuda.synchronize()
-
-    run_ms, full_ms, full_bytes = [], [], []
+    # ---- timed region: K steps replayed from one captured HIP graph, from the
+    # same start state, REPEATS times; the median is the reported throughput
+    reset()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        step()
+    torch.cuda.synchronize()
+    run_ms = []
     for rep in range(args.repeats):
         reset()
         torch.cuda.synchronize()
         t_start = torch.cuda.Event(enable_timing=True)
         t_end = torch.cuda.Event(enable_timing=True)
         t_start.record(stream)
-        if graph is not None:
-            for j in range(args.steps):
-                graph.replay()
-        else:
-            f = plan._lib.oda_full_attn_if
-            for j in range(args.steps):
-                pos_hist[j].copy_(bufs.pos)
-                sd.fill_step(feed, wl, bufs.pos, t0)
-                plan.local()
-                plan.score()
-                for l, a in enumerate(plan.full_args):
-                    e0, e1 = ev[j * L + l]
-                    e0.record(stream)
-                    C.check(f(*a), "oda_full_attn_if")
-                    e1.record(stream)
-                plan.commit()
-                flags_hist[j].copy_(bufs.flag)
+        for j in range(args.steps):
+            graph.replay()
         t_end.record(stream)
         torch.cuda.synchronize()
         run_ms.append(t_start.elapsed_time(t_end))
-        if graph is None:
-            fl = flags_hist.cpu().numpy().astype(np.int64)
-            ps = pos_hist.cpu().numpy().astype(np.int64)
-            full_bytes.append(float(np.sum(fl * (ps + 1)) * Hkv * d * 2 * 2 * L))
-            full_ms.append(sum(e0.elapsed_time(e1) for e0, e1 in ev))
+
+    # ---- the same K steps replayed as three graphs per step (feed + local +
+    # score | the L full-attention launches | commit), with a pair of HIP
+    # events on the stream around the middle graph: the dominant kernel's
+    # average launch duration, free of host launch gaps; the recorded flags
+    # and positions fix its algorithmic bytes
+    reset()
+    torch.cuda.synchronize()
+    g_pre, g_full, g_post = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_pre, stream=stream):
+        sd.fill_step(feed, wl, bufs.pos, t0)
+        plan.local()
+        plan.score()
+    with torch.cuda.graph(g_full, stream=stream):
+        plan.full()
+    with torch.cuda.graph(g_post, stream=stream):
+        plan.commit()
+    flags_hist = torch.zeros((args.steps, B), dtype=torch.uint8, device=dev)
+    pos_hist = torch.zeros((args.steps, B), dtype=torch.int32, device=dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    reset()
+    torch.cuda.synchronize()
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
+    e_start.record(stream)
+    for j in range(args.steps):
+        pos_hist[j].copy_(bufs.pos)
+        g_pre.replay()
+        e0, e1 = ev[j]
+        e0.record(stream)
+        g_full.replay()
+        e1.record(stream)
+        g_post.replay()
+        flags_hist[j].copy_(bufs.flag)
+    e_end.record(stream)
+    torch.cuda.synchronize()
+    split_ms = e_start.elapsed_time(e_end)
+    full_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev)
+    fl = flags_hist.cpu().numpy().astype(np.int64)
+    ps = pos_hist.cpu().numpy().astype(np.int64)
+    full_bytes = float(np.sum(fl * (ps + 1))) * Hkv * d * 2 * 2 * L
     assert int(ws[:4].view(torch.int32).item()) == 0, "device error bits set"
 
     ms_total = statistics.median(run_ms)
     ms_step = ms_total / args.steps
     steps_per_s = 1000.0 / ms_step
-    # realised schedule and KV bytes of the (last) timed run
-    fl = flags_hist.cpu().numpy().astype(np.int64)
-    ps = pos_hist.cpu().numpy().astype(np.int64)
-    realised = float(fl.mean()) if graph is None else None
+    realised = float(fl.mean())
     kv_local = 0
     for b in range(B):
         for j in range(args.steps):
             t = int(wl.t0[b]) + j + 1
             kv_local += min(t, wl.sink + wl.window)
-    kv_bytes_step = (kv_local + (float(np.sum(fl * (ps + 1))) if graph is None else rate * B * args.steps *
-                                 (float(np.mean(wl.t0)) + args.steps / 2))) * Hkv * d * 2 * 2 * L / args.steps
+    kv_bytes_step = (kv_local + float(np.sum(fl * (ps + 1)))) * Hkv * d * 2 * 2 * L / args.steps
     out = {
         "metric": "ODA decode steps/s + KV HBM GB/s (% peak) at 128K ctx, 12.5% recall, 1 GPU",
         "value": round(steps_per_s, 2),
@@ -207,26 +223,64 @@ def run(args, wl, stream, torch, synth, sd, C, StepBuffers, StepPlan, dev):
         "config": {"workload": wl.name, "layers": L, "batch": B, "context": int(wl.t0[0]), "q_heads": Hq,
                    "kv_heads": Hkv, "head_dim": d, "kv_layout": "contig", "recall_rate_target": rate,
                    "recall_rate_realised": realised, "theta": theta, "tokens_per_s": round(steps_per_s * B, 1),
-                   "repeats": args.repeats, "timing": "hip-graph" if graph is not None else "eager+events"},
+                   "repeats": args.repeats, "timing": "hip-graph replay, median of repeats",
+                   "split_graph_steps_per_s": round(1000.0 * args.steps / split_ms, 2)},
         "kv_gbs": round(kv_bytes_step / (ms_step * 1e-3) / 1e9, 1),
         "kv_frac_peak": round(kv_bytes_step / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
     }
-    if graph is None and full_ms:
-        i = int(np.argsort(run_ms)[len(run_ms) // 2])
-        nlaunch = args.steps * L
-        avg_us = full_ms[i] * 1e3 / nlaunch
-        bytes_per_launch = full_bytes[i] / nlaunch
-        achieved = bytes_per_launch / (avg_us * 1e-6) / 1e9
-        out["roofline"] = {"bound": "hbm", "kernel": "k_attn_full (oda_full_attn_if)", "achieved": round(achieved, 1),
-                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                           "traffic": None, "avg_launch_us": round(avg_us, 2),
-                           "algorithmic_bytes_per_launch": int(bytes_per_launch)}
+    nlaunch = args.steps * L
+    avg_us = full_ms * 1e3 / nlaunch
+    bytes_per_launch = full_bytes / nlaunch
+    achieved = bytes_per_launch / (avg_us * 1e-6) / 1e9
+    traffic, traffic_note = measured_traffic(bytes_per_launch)
+    out["roofline"] = {"bound": "hbm", "kernel": "k_attn_full (oda_full_attn_if)", "achieved": round(achieved, 1),
+                       "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                       "traffic": traffic, "traffic_note": traffic_note, "avg_launch_us": round(avg_us, 2),
+                       "algorithmic_bytes_per_launch": int(bytes_per_launch), "launches": nlaunch}
     out["setup_s"] = round(setup_s, 1)
     if args.rate_sweep:
         out["rate_sweep"] = rate_sweep(args, wl, plan, bufs, step, reset, torch)
+    if args.copy_calibration:
+        src = torch.empty(1 << 29, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = 2 * src.numel() * src.element_size()
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, blob, theta, realised if realised is not None else rate)
+        out["cpu_baseline"] = cpu_baseline(wl, blob, theta, realised)
     print(json.dumps(out), flush=True)
+
+
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "k_attn_full_traffic.json")
+KERNEL_SOURCES = ("conditional_sparse_attention_amd/csrc/attn.hip", "conditional_sparse_attention_amd/csrc/oda_internal.h")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(root, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(bytes_per_launch):
+    """HBM bytes per launch of k_attn_full from the committed rocprofv3 PMC
+    measurement (FETCH_SIZE + WRITE_SIZE, each normalised on a 1 GiB copy),
+    as its ratio to the algorithmic bytes of the measured launches times this
+    run's algorithmic bytes per launch; None if the kernel source changed
+    since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None, "no counter measurement"
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None, "kernel changed since the counters were taken"
+    ratio = rec["hbm_bytes_per_launch"] / rec["algorithmic_bytes_per_launch"]
+    return int(ratio * bytes_per_launch), f"PMC ratio {ratio:.5f} of algorithmic bytes ({os.path.basename(TRAFFIC_FILE)})"
 
 
 def rate_sweep(args, wl, plan, bufs, step, reset, torch):

@@ -51,7 +51,7 @@ typedef __attribute__((address_space(1))) const v4u_t gv4_t;
 #define ODA_LOCAL_DEPTH 4
 #endif
 #ifndef ODA_FULL_DEPTH
-#define ODA_FULL_DEPTH 2
+#define ODA_FULL_DEPTH 3
 #endif
 #ifndef ODA_LOCAL_SPLITS
 #define ODA_LOCAL_SPLITS 16
@@ -66,10 +66,12 @@ typedef __attribute__((address_space(1))) const v4u_t gv4_t;
 // Row blocks per lane per pipeline stage (a stage is 4*U rows of a wave).
 // Two stages are in flight: the next block's loads are issued before the
 // current block is consumed.
-template <int G>
-struct Unroll {
-  static constexpr int value = 2;
-};
+#ifndef ODA_LOCAL_U
+#define ODA_LOCAL_U 2
+#endif
+#ifndef ODA_FULL_U
+#define ODA_FULL_U 2
+#endif
 constexpr int kLocalWaves = ODA_LOCAL_WAVES;  // local kernel workgroup
 // Full kernel shape per group size: G = 2 (the 16/8-head models) runs 12
 // waves (3 per SIMD) with a 2-stage ring; G = 1 and G = 4 keep more state per
@@ -138,7 +140,7 @@ __device__ __forceinline__ size_t row_index(const AttnParams& P, int b, int g, i
   }
 }
 
-template <int G, int kUnroll = Unroll<G>::value>
+template <int G, int kUnroll>
 __device__ __forceinline__ void block_update(const uint4 (&qv)[G], State<G>& st, const uint4 (&kk)[kUnroll],
                                              const uint4 (&vv)[kUnroll], const bool (&ok)[kUnroll],
                                              float scale) {
@@ -227,10 +229,9 @@ __device__ __forceinline__ void load_stage(const AttnParams& P, const uint16_t* 
 // Rows [p_lo, p_hi) of the cache.  Wave w takes stages starting at
 // p_lo + (k*NW + w) * 4U.  A ring of DEPTH register stages keeps DEPTH-1
 // stages in flight while one is consumed; its refill is issued right after.
-template <int G, bool PAGED, int NW, int DEPTH>
+template <int G, bool PAGED, int NW, int DEPTH, int U>
 __device__ __forceinline__ void cache_rows(const AttnParams& P, const uint4 (&qv)[G], State<G>& st, int b, int g,
                                            int p_lo, int p_hi, int wave, int r, int c) {
-  constexpr int U = Unroll<G>::value;
   constexpr int kStage = 4 * U;
   constexpr int kStride = NW * kStage;
   const uint16_t* Kbg = P.K;
@@ -269,20 +270,14 @@ __device__ __forceinline__ void cache_rows(const AttnParams& P, const uint4 (&qv
 template <int G>
 __device__ __forceinline__ void current_row(const AttnParams& P, const uint4 (&qv)[G], State<G>& st, int b, int g,
                                             int wave, int r, int c) {
-  constexpr int kUnroll = Unroll<G>::value;
   if (wave != 0) return;
-  uint4 kk[kUnroll], vv[kUnroll];
-  bool ok[kUnroll];
+  uint4 kk[1], vv[1];
+  bool ok[1];
   const size_t base = ((size_t)b * P.Hkv + g) * kHeadDim + c * 8;
-  const uint4 kr = *reinterpret_cast<const uint4*>(P.kc + base);
-  const uint4 vr = *reinterpret_cast<const uint4*>(P.vc + base);
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    kk[u] = kr;
-    vv[u] = vr;
-    ok[u] = (u == 0) && (r == 0);
-  }
-  block_update<G>(qv, st, kk, vv, ok, P.scale_log2);
+  kk[0] = *reinterpret_cast<const uint4*>(P.kc + base);
+  vv[0] = *reinterpret_cast<const uint4*>(P.vc + base);
+  ok[0] = (r == 0);
+  block_update<G, 1>(qv, st, kk, vv, ok, P.scale_log2);
 }
 
 __device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(x, m, 64); }
@@ -482,7 +477,7 @@ __device__ __forceinline__ void merge_partials(const AttnParams& P, const float*
 // One unit: keys of S with virtual indices [v_lo, v_hi) where S = [0, n0)
 // followed by [s1, t); the last virtual index (n0 + t - s1 - 1) is the
 // current token and is read from staging.
-template <int G, bool PAGED, int NW, int DEPTH, int MAXS>
+template <int G, bool PAGED, int NW, int DEPTH, int U, int MAXS>
 __device__ void attn_unit(const AttnParams& P, int b, int g, int split, int nsplit, int v_lo, int v_hi,
                           const LocalSet& S, int32_t* ticket, float* part_bg, float* lds) {
   const int tid = threadIdx.x;
@@ -511,12 +506,12 @@ __device__ void attn_unit(const AttnParams& P, int b, int g, int split, int nspl
   // first range [0, n0) -> positions equal virtual indices
   if (v_lo < S.n0) {
     const int hi = v_cache_hi < S.n0 ? v_cache_hi : S.n0;
-    if (hi > v_lo) cache_rows<G, PAGED, NW, DEPTH>(P, qv, st, b, g, v_lo, hi, wave, r, c);
+    if (hi > v_lo) cache_rows<G, PAGED, NW, DEPTH, U>(P, qv, st, b, g, v_lo, hi, wave, r, c);
   }
   // second range: virtual n0 + k  ->  position s1 + k
   {
     const int lo = v_lo > S.n0 ? v_lo : S.n0;
-    if (v_cache_hi > lo) cache_rows<G, PAGED, NW, DEPTH>(P, qv, st, b, g, S.s1 + (lo - S.n0), S.s1 + (v_cache_hi - S.n0), wave, r, c);
+    if (v_cache_hi > lo) cache_rows<G, PAGED, NW, DEPTH, U>(P, qv, st, b, g, S.s1 + (lo - S.n0), S.s1 + (v_cache_hi - S.n0), wave, r, c);
   }
   if (has_current) current_row<G>(P, qv, st, b, g, wave, r, c);
 
@@ -580,7 +575,7 @@ __global__ void __launch_bounds__(kLocalWaves * 64) k_attn_local(AttnParams P) {
   const int v_lo = split * chunk;
   const int v_hi = (v_lo + chunk) < n ? v_lo + chunk : n;
   float* part_bg = P.part + ((size_t)(b * P.Hkv + g) * kLocalMaxSplits) * G * kPartStride;
-  attn_unit<G, PAGED, NW, ODA_LOCAL_DEPTH, ODA_LOCAL_SPLITS>(P, b, g, split, ns, v_lo, v_hi, S, P.tickets + b * P.Hkv + g, part_bg, lds);
+  attn_unit<G, PAGED, NW, ODA_LOCAL_DEPTH, ODA_LOCAL_U, ODA_LOCAL_SPLITS>(P, b, g, split, ns, v_lo, v_hi, S, P.tickets + b * P.Hkv + g, part_bg, lds);
 }
 
 template <int G, bool PAGED>
@@ -612,7 +607,7 @@ __global__ void __launch_bounds__(FullWaves<G>::value * 64) k_attn_full(AttnPara
     S.s1 = t;
     S.t = t;
     float* part_bg = P.part + ((size_t)(b * P.Hkv + g) * kFullMaxSplits) * G * kPartStride;
-    attn_unit<G, PAGED, NW, FullDepth<G>::value, kFullMaxSplits>(P, b, g, split, ns, v_lo, v_hi, S, P.tickets + b * P.Hkv + g, part_bg, lds);
+    attn_unit<G, PAGED, NW, FullDepth<G>::value, ODA_FULL_U, kFullMaxSplits>(P, b, g, split, ns, v_lo, v_hi, S, P.tickets + b * P.Hkv + g, part_bg, lds);
   }
 }
 
