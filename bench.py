@@ -30,6 +30,7 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -51,6 +52,9 @@ def parse():
     ap.add_argument("--workload", default="3", help="workload key (default 3: 128K, B=4, 12.5%% recall)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rate-sweep", default="", help="comma list of forced full-branch rates to time as well")
+    ap.add_argument("--always-full", action="store_true",
+                    help="also time the always-full baseline: every sequence takes the full branch, no local "
+                         "attention and no recall head (the feed, the work list, the full attention, the commit)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -70,8 +74,8 @@ def main():
 
     wl_key = int(args.workload) if args.workload.isdigit() else args.workload
     wl = synth.workloads()[wl_key]
-    if wl.layout != "contig":
-        raise SystemExit("bench supports the contiguous workloads")
+    if wl.bernoulli_odd is not None:
+        raise SystemExit("the bench runs head-decided schedules; this workload forces per-step flags")
     total_steps_needed = args.steps + max(args.warmup, 0)
     if args.steps > wl.steps + wl.t_cap_slack:
         raise SystemExit("too many steps for the cache capacity")
@@ -84,13 +88,21 @@ def main():
 def run(args, wl, stream, torch, synth, sd, C, StepBuffers, StepPlan, dev):
     L, B, Hq, Hkv, d, D = wl.layers, wl.batch, wl.hq, wl.hkv, wl.head_dim, wl.hidden
     t_setup = time.time()
-    dims = C.make_dims(L, B, Hq, Hkv, t_cap=wl.t_cap, sink=wl.sink, window=wl.window)
-    K = torch.empty((L, B, Hkv, wl.t_cap, d), dtype=torch.int16, device=dev)
-    V = torch.empty_like(K)
     t0 = torch.from_numpy(wl.t0.astype(np.int32)).to(dev)
-    sd.fill_cache(K, wl, synth.TAG_K, t0)
-    sd.fill_cache(V, wl, synth.TAG_V, t0)
-    kv = C.make_kv(K, V)
+    if wl.layout == "paged":
+        tables_np, nblocks = synth.paged_block_tables(wl)
+        tables = torch.from_numpy(tables_np).to(dev)
+        dims = C.make_dims(L, B, Hq, Hkv, kv_layout=C.ODA_KV_PAGED, block_size=wl.block_size,
+                           max_blocks_per_seq=tables_np.shape[1], num_blocks=nblocks, sink=wl.sink, window=wl.window)
+        K = torch.empty((L, nblocks, Hkv, wl.block_size, d), dtype=torch.int16, device=dev)
+    else:
+        tables, nblocks = None, 0
+        dims = C.make_dims(L, B, Hq, Hkv, t_cap=wl.t_cap, sink=wl.sink, window=wl.window)
+        K = torch.empty((L, B, Hkv, wl.t_cap, d), dtype=torch.int16, device=dev)
+    V = torch.empty_like(K)
+    sd.fill_cache(K, wl, synth.TAG_K, t0, tables=tables, num_blocks=nblocks)
+    sd.fill_cache(V, wl, synth.TAG_V, t0, tables=tables, num_blocks=nblocks)
+    kv = C.make_kv(K, V, tables)
     ws = torch.zeros(C.oda_workspace_bytes(dims), dtype=torch.uint8, device=dev)
     C.oda_workspace_init(dims, ws)
     blob = synth.head_blob(D, wl.head_seed)
@@ -123,9 +135,12 @@ def run(args, wl, stream, torch, synth, sd, C, StepBuffers, StepPlan, dev):
         scores[j].copy_(bufs.score)
     torch.cuda.synchronize()
     sc = np.sort(scores.cpu().numpy().reshape(-1))[::-1]
-    rate = wl.rate if wl.rate is not None else 0.125
-    k = int(round(rate * sc.size))
-    theta = float((sc[k - 1] + sc[k]) / 2) if 0 < k < sc.size else (math.inf if k == 0 else -math.inf)
+    rate = wl.rate
+    if rate is not None:
+        k = int(round(rate * sc.size))
+        theta = float((sc[k - 1] + sc[k]) / 2) if 0 < k < sc.size else (math.inf if k == 0 else -math.inf)
+    else:
+        theta = float(wl.theta)
     plan.set_theta(theta)
 
     # ---- warm-up
@@ -207,6 +222,9 @@ def run(args, wl, stream, torch, synth, sd, C, StepBuffers, StepPlan, dev):
             t = int(wl.t0[b]) + j + 1
             kv_local += min(t, wl.sink + wl.window)
     kv_bytes_step = (kv_local + float(np.sum(fl * (ps + 1)))) * Hkv * d * 2 * 2 * L / args.steps
+    always_full = None
+    if args.always_full:
+        always_full = always_full_leg(args, wl, dims, kv, ws, bufs, plan, feed, sd, t0, reset, stream, torch, C)
     out = {
         "metric": "ODA decode steps/s + KV HBM GB/s (% peak) at 128K ctx, 12.5% recall, 1 GPU",
         "value": round(steps_per_s, 2),
@@ -220,8 +238,9 @@ def run(args, wl, stream, torch, synth, sd, C, StepBuffers, StepPlan, dev):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded generator, device-filled; random-init Xavier recall head)",
-        "config": {"workload": wl.name, "layers": L, "batch": B, "context": int(wl.t0[0]), "q_heads": Hq,
-                   "kv_heads": Hkv, "head_dim": d, "kv_layout": "contig", "recall_rate_target": rate,
+        "config": {"workload": wl.name, "layers": L, "batch": B, "context": int(wl.t0[0]) if np.all(wl.t0 == wl.t0[0])
+                   else f"ragged mean {float(np.mean(wl.t0)):.0f}", "q_heads": Hq,
+                   "kv_heads": Hkv, "head_dim": d, "kv_layout": wl.layout, "recall_rate_target": rate,
                    "recall_rate_realised": realised, "theta": theta, "tokens_per_s": round(steps_per_s * B, 1),
                    "repeats": args.repeats, "timing": "hip-graph replay, median of repeats",
                    "split_graph_steps_per_s": round(1000.0 * args.steps / split_ms, 2)},
@@ -237,6 +256,9 @@ def run(args, wl, stream, torch, synth, sd, C, StepBuffers, StepPlan, dev):
                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                        "traffic": traffic, "traffic_note": traffic_note, "avg_launch_us": round(avg_us, 2),
                        "algorithmic_bytes_per_launch": int(bytes_per_launch), "launches": nlaunch}
+    if always_full is not None:
+        out["always_full"] = always_full
+        out["always_full"]["oda_speedup"] = round(steps_per_s / always_full["steps_per_s"], 3)
     out["setup_s"] = round(setup_s, 1)
     if args.rate_sweep:
         out["rate_sweep"] = rate_sweep(args, wl, plan, bufs, step, reset, torch)
@@ -281,6 +303,40 @@ def measured_traffic(bytes_per_launch):
         return None, "kernel changed since the counters were taken"
     ratio = rec["hbm_bytes_per_launch"] / rec["algorithmic_bytes_per_launch"]
     return int(ratio * bytes_per_launch), f"PMC ratio {ratio:.5f} of algorithmic bytes ({os.path.basename(TRAFFIC_FILE)})"
+
+
+def always_full_leg(args, wl, dims, kv, ws, bufs, plan, feed, sd, t0, reset, stream, torch, C):
+    """K steps of the always-full baseline from the same start state, one graph
+    per step, median of the repeats."""
+    flag_all = torch.ones(wl.batch, dtype=torch.uint8, device="cuda")
+    lib = plan._lib
+    dp = ctypes.byref(dims)
+    wsb = ws.numel() * ws.element_size()
+    s = stream.cuda_stream
+    commit_args = list(plan.commit_args)
+    commit_args[3] = flag_all.data_ptr()
+    reset()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        sd.fill_step(feed, wl, bufs.pos, t0)
+        C.check(lib.oda_worklist(dp, flag_all.data_ptr(), bufs.pos.data_ptr(), ws.data_ptr(), wsb, s), "oda_worklist")
+        plan.full()
+        C.check(lib.oda_commit(*commit_args), "oda_commit")
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(args.repeats):
+        reset()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    m = statistics.median(ms) / args.steps
+    return {"steps_per_s": round(1000.0 / m, 2), "ms_per_step": round(m, 4)}
 
 
 def rate_sweep(args, wl, plan, bufs, step, reset, torch):

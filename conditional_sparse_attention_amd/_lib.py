@@ -27,7 +27,7 @@ ODA_FULL_MAX_SPLITS = 32
 EXPORTED = (
     "oda_abi_version", "oda_status_str", "oda_head_param_count", "oda_head_offsets",
     "oda_workspace_bytes", "oda_workspace_worklist_offset", "oda_workspace_init",
-    "oda_local_ranges", "oda_local_attn", "oda_recall_score", "oda_full_attn_if", "oda_commit",
+    "oda_local_ranges", "oda_local_attn", "oda_recall_score", "oda_worklist", "oda_full_attn_if", "oda_commit",
 )
 
 
@@ -77,6 +77,7 @@ def lib() -> ctypes.CDLL:
             "oda_local_ranges": (ctypes.c_int, [dp, vp, vp, vp]),
             "oda_local_attn": (ctypes.c_int, [dp, i32, kp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "oda_recall_score": (ctypes.c_int, [dp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, sz, vp]),
+            "oda_worklist": (ctypes.c_int, [dp, vp, vp, vp, sz, vp]),
             "oda_full_attn_if": (ctypes.c_int, [dp, i32, kp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "oda_commit": (ctypes.c_int, [dp, kp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         }
@@ -182,6 +183,10 @@ def oda_recall_score(dims, head_w, h_prev, emb, h_local, theta, force, pos, scor
     check(lib().oda_recall_score(ctypes.byref(dims), _p(head_w), _p(h_prev), _p(emb), _p(h_local),
                                   ctypes.c_float(theta), _p(force), _p(pos), _p(score), _p(flag), _p(ws),
                                   _bytes(ws), _s(stream)), "oda_recall_score")
+
+
+def oda_worklist(dims, flag, pos, ws, stream=None) -> None:
+    check(lib().oda_worklist(ctypes.byref(dims), _p(flag), _p(pos), _p(ws), _bytes(ws), _s(stream)), "oda_worklist")
 
 
 def oda_full_attn_if(dims, layer, kv: oda_kv, pos, q, k_cur, v_cur, out, lse, ws, stream=None) -> None:

@@ -86,20 +86,6 @@ struct FullDepth {
   static constexpr int value = G == 2 ? ODA_FULL_DEPTH : 4;
 };
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
-}
-
-// Sum over the 16 lanes of a DPP row; every lane of the row receives the same bits.
-__device__ __forceinline__ float row16_sum(float x) {
-  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
-  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
-  x += dpp_mov<0x141>(x);  // row_half_mirror
-  x += dpp_mov<0x140>(x);  // row_mirror
-  return x;
-}
-
 __device__ __forceinline__ float dot8_bf16(const uint4 a, const uint4 b) {
   float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x),
                                             __builtin_bit_cast(bf16x2_t, b.x), 0.0f, false);

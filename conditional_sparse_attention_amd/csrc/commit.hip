@@ -53,13 +53,16 @@ __global__ void __launch_bounds__(kThreads) k_commit(CommitParams P) {
     uint16_t* dst = (which ? P.V : P.K) + dst_layer + row_base + (size_t)g * g_stride + c * 8;
     *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
   }
-  __threadfence();
+  // The ticket only orders this workgroup's read of pos[b] (already
+  // complete: every store above used it) before the last workgroup's
+  // increment.  The copied slots and h_prev are read by later kernels only,
+  // so no device-wide fence is needed.
   __syncthreads();
   __shared__ int s_last;
-  if (threadIdx.x == 0) s_last = (atomicAdd(P.tickets + b, 1) == P.L - 1);
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(P.tickets + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == P.L - 1;
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
   const uint16_t* so = (full ? P.oF : P.oL) + (size_t)b * P.D;
   uint16_t* dh = P.h_prev + (size_t)b * P.D;
   for (int i = threadIdx.x; i < P.D / 8; i += kThreads)
@@ -67,7 +70,7 @@ __global__ void __launch_bounds__(kThreads) k_commit(CommitParams P) {
   __syncthreads();
   if (threadIdx.x == 0) {
     P.pos[b] = p + 1;
-    atomicExch(P.tickets + b, 0);
+    __hip_atomic_store(P.tickets + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

@@ -11,110 +11,101 @@
 //
 // At decode batch sizes every layer is a skinny matrix-vector product that
 // streams its fp32 weights once from HBM (4 bytes per 2*B flops), so the
-// kernels are bandwidth-shaped GEMVs: a workgroup owns 4 output rows, its
-// 256 lanes walk the reduction dimension with 16-byte weight loads, every
-// batch row is accumulated from the same weight registers, and RMSNorm
-// scales are folded in after the dot product (W (gamma*x) / rms(x)), with
-// the sum of squares gathered in the same pass.  The interaction vector is
-// never materialised: each lane forms its 4 elements from the tower outputs
-// on the fly.  Batches above 8 rows are processed in tiles of 8.
+// kernels are bandwidth-shaped GEMVs.  One wave owns R output rows: its 64
+// lanes hold the rows' weights in registers (16-byte loads, all issued at
+// once), then sweep every batch row against them, so the weights are read
+// from HBM exactly once whatever the batch; the batch inputs come from L2.
+// The dot products are reduced inside the wave (DPP row sums + readlane),
+// with no LDS and no barrier.  RMSNorm scales are folded in after the dot
+// product (W (gamma*x) / rms(x)), the sum of squares gathered in the same
+// pass; the interaction vector is formed on the fly from the tower outputs.
 #include "oda_internal.h"
 
 namespace oda {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRows = 4;       // output rows per workgroup
-constexpr int kMaxNB = 8;      // batch rows per tile
+constexpr int kWaves = 4;
 constexpr float kEps = 1e-6f;
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
-  return x;
-}
-
-// Reduce NV per-thread values over the 256-thread block; result in red[0..NV).
-template <int NV>
-__device__ __forceinline__ void block_sum(float (&v)[NV], float* red /* [4][NV] */) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const float s = wave_sum(v[i]);
-    if (lane == 0) red[wave * NV + i] = s;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < NV; i += kThreads) {
-    red[4 * NV + i] = red[i] + red[NV + i] + red[2 * NV + i] + red[3 * NV + i];
-  }
-  __syncthreads();
-}
-
-__device__ __forceinline__ float4 load_bf16x4(const uint16_t* p) {
-  const uint2 w = *reinterpret_cast<const uint2*>(p);
-  return make_float4(bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y));
-}
 __device__ __forceinline__ float dot4(const float4 a, const float4 b) {
   return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
 }
+__device__ __forceinline__ float4 mul4(const float4 a, const float4 b) {
+  return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
+}
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 ldbf4(const uint16_t* p) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  return make_float4(bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y));
+}
 
+// ------------------------------------------------------------------ towers
 struct TowerArgs {
-  const float* w;      // blob
+  const float* w;  // blob
   int64_t off_gamma[3], off_W[3], off_c[3];
-  const uint16_t* x[3];  // h_prev, emb, h_local  [B][D]
+  const uint16_t* x[3];  // h_prev, emb, h_local  [B][D] bf16
   float* out;            // towers [3][B][T]
-  int B, D;
+  int B;
 };
 
-// grid (T / kRows, 3 towers, batch tiles)
-template <int NB>
+// KI = D / 256 float4 per lane per row; R rows per wave; NBM >= B.
+// grid (T / (4R), 3 towers)
+template <int KI, int R, int NBM>
 __global__ void __launch_bounds__(kThreads) k_tower(TowerArgs A) {
-  __shared__ float red[5 * (kRows * NB + NB)];
+  constexpr int D = KI * 256;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int tw = blockIdx.y;
-  const int n0 = blockIdx.x * kRows;
-  const int b0 = blockIdx.z * kMaxNB;
-  const int nb = min(NB, A.B - b0);
-  const float* W = A.w + A.off_W[tw];
-  const float* gamma = A.w + A.off_gamma[tw];
-  const uint16_t* x = A.x[tw] + (size_t)b0 * A.D;
-  float acc[kRows * NB + NB];
+  const int n0 = (blockIdx.x * kWaves + wave) * R;
+  const float* W = A.w + A.off_W[tw] + (size_t)n0 * D + lane * 4;
+  const float* gam = A.w + A.off_gamma[tw] + lane * 4;
+  float4 w[R][KI];
 #pragma unroll
-  for (int i = 0; i < kRows * NB + NB; ++i) acc[i] = 0.0f;
-  for (int k = threadIdx.x * 4; k < A.D; k += kThreads * 4) {
-    float4 w[kRows];
+  for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) w[r] = *reinterpret_cast<const float4*>(W + (size_t)(n0 + r) * A.D + k);
-    const float4 gm = *reinterpret_cast<const float4*>(gamma + k);
+    for (int i = 0; i < KI; ++i) w[r][i] = ld4(W + (size_t)r * D + 256 * i);
+  float4 g[KI];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      if (b < nb) {
-        const float4 xv = load_bf16x4(x + (size_t)b * A.D + k);
-        const float4 in = make_float4(xv.x * gm.x, xv.y * gm.y, xv.z * gm.z, xv.w * gm.w);
+  for (int i = 0; i < KI; ++i) g[i] = ld4(gam + 256 * i);
+  float acc[R][NBM], ss[NBM];
+  const uint16_t* x = A.x[tw] + lane * 4;
 #pragma unroll
-        for (int r = 0; r < kRows; ++r) acc[r * NB + b] += dot4(w[r], in);
-        acc[kRows * NB + b] += dot4(xv, xv);
+  for (int b = 0; b < NBM; ++b) {
+    ss[b] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r][b] = 0.0f;
+    if (b < A.B) {
+#pragma unroll
+      for (int i = 0; i < KI; ++i) {
+        const float4 xv = ldbf4(x + (size_t)b * D + 256 * i);
+        const float4 in = mul4(xv, g[i]);
+        ss[b] += dot4(xv, xv);
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r][b] += dot4(w[r][i], in);
       }
     }
   }
-  block_sum<kRows * NB + NB>(acc, red);
-  const float* tot = red + 4 * (kRows * NB + NB);
-  if (threadIdx.x < kRows * NB) {
-    const int r = threadIdx.x / NB, b = threadIdx.x % NB;
-    if (b < nb) {
-      const float inv = rsqrtf(tot[kRows * NB + b] / (float)A.D + kEps);
-      const float c = A.w[A.off_c[tw] + n0 + r];
-      A.out[((size_t)tw * A.B + b0 + b) * kTower + n0 + r] = silu(tot[r * NB + b] * inv + c);
+  const float* cb = A.w + A.off_c[tw] + n0;
+#pragma unroll
+  for (int b = 0; b < NBM; ++b) {
+    if (b < A.B) {
+      const float inv = rsqrtf(wave_sum64(ss[b]) / (float)D + kEps);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float v = wave_sum64(acc[r][b]);
+        if (lane == 0) A.out[((size_t)tw * A.B + b) * kTower + n0 + r] = silu(v * inv + cb[r]);
+      }
     }
   }
 }
 
+// ------------------------------------------------------------- interaction
 struct InteractArgs {
-  const float* W;      // W_I [T][9T]
-  const float* bias;   // c_I
-  const float* towers; // [3][B][T]
-  float* out;          // u0 [B][T]
+  const float* W;       // W_I [T][9T]
+  const float* bias;    // c_I
+  const float* towers;  // [3][B][T]
+  float* out;           // u0 [B][T]
   int B;
 };
 
@@ -123,65 +114,60 @@ __device__ __forceinline__ float4 seg_value(int seg, const float4 a, const float
     case 0: return a;
     case 1: return b;
     case 2: return c;
-    case 3: return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
-    case 4: return make_float4(a.x * c.x, a.y * c.y, a.z * c.z, a.w * c.w);
-    case 5: return make_float4(b.x * c.x, b.y * c.y, b.z * c.z, b.w * c.w);
+    case 3: return mul4(a, b);
+    case 4: return mul4(a, c);
+    case 5: return mul4(b, c);
     case 6: return make_float4(fabsf(a.x - b.x), fabsf(a.y - b.y), fabsf(a.z - b.z), fabsf(a.w - b.w));
     case 7: return make_float4(fabsf(a.x - c.x), fabsf(a.y - c.y), fabsf(a.z - c.z), fabsf(a.w - c.w));
     default: return make_float4(fabsf(b.x - c.x), fabsf(b.y - c.y), fabsf(b.z - c.z), fabsf(b.w - c.w));
   }
 }
 
-// grid (T / kRows, 1, batch tiles); one loop iteration per interaction segment
-template <int NB>
+// One wave per output row.  The lane's 36 float4 of the 9216-long row are
+// loaded at once (chunk q holds element q*256 + 4*lane of each of the 9
+// segments), so one (a, b, c) float4 per batch row and chunk serves all 9
+// segment values of that chunk.  grid (T / 4)
+template <int NBM>
 __global__ void __launch_bounds__(kThreads) k_interact(InteractArgs A) {
-  __shared__ float red[5 * kRows * NB];
-  const int n0 = blockIdx.x * kRows;
-  const int b0 = blockIdx.z * kMaxNB;
-  const int nb = min(NB, A.B - b0);
-  const float* ta = A.towers + (size_t)b0 * kTower;
-  const float* tb = A.towers + ((size_t)A.B + b0) * kTower;
-  const float* tc = A.towers + ((size_t)2 * A.B + b0) * kTower;
-  const int i4 = threadIdx.x * 4;  // element inside the segment (T = 1024 = 256 lanes * 4)
-  float acc[kRows * NB];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = blockIdx.x * kWaves + wave;
+  const float* W = A.W + (size_t)n * (9 * kTower) + lane * 4;
+  float4 w[4][9];
 #pragma unroll
-  for (int i = 0; i < kRows * NB; ++i) acc[i] = 0.0f;
-  float4 av[NB], bv[NB], cv[NB];
+  for (int q = 0; q < 4; ++q)
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    if (b < nb) {
-      av[b] = *reinterpret_cast<const float4*>(ta + (size_t)b * kTower + i4);
-      bv[b] = *reinterpret_cast<const float4*>(tb + (size_t)b * kTower + i4);
-      cv[b] = *reinterpret_cast<const float4*>(tc + (size_t)b * kTower + i4);
-    } else {
-      av[b] = bv[b] = cv[b] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < 9; ++s) w[q][s] = ld4(W + s * kTower + q * 256);
+  float acc[NBM];
+#pragma unroll
+  for (int b = 0; b < NBM; ++b) {
+    acc[b] = 0.0f;
+    if (b < A.B) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = q * 256 + lane * 4;
+        const float4 av = ld4(A.towers + (size_t)b * kTower + e);
+        const float4 bv = ld4(A.towers + ((size_t)A.B + b) * kTower + e);
+        const float4 cv = ld4(A.towers + ((size_t)2 * A.B + b) * kTower + e);
+#pragma unroll
+        for (int s = 0; s < 9; ++s) acc[b] += dot4(w[q][s], seg_value(s, av, bv, cv));
+      }
     }
   }
-  for (int seg = 0; seg < 9; ++seg) {
-    float4 w[kRows];
+  const float cI = A.bias[n];
 #pragma unroll
-    for (int r = 0; r < kRows; ++r)
-      w[r] = *reinterpret_cast<const float4*>(A.W + (size_t)(n0 + r) * (9 * kTower) + seg * kTower + i4);
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const float4 in = seg_value(seg, av[b], bv[b], cv[b]);
-#pragma unroll
-      for (int r = 0; r < kRows; ++r) acc[r * NB + b] += dot4(w[r], in);
-    }
-  }
-  block_sum<kRows * NB>(acc, red);
-  const float* tot = red + 4 * kRows * NB;
-  if (threadIdx.x < kRows * NB) {
-    const int r = threadIdx.x / NB, b = threadIdx.x % NB;
-    if (b < nb) {
-      const int n = n0 + r;
-      const size_t o = (size_t)(b0 + b) * kTower + n;
-      const float resid = ta[(size_t)b * kTower + n] + tb[(size_t)b * kTower + n] + tc[(size_t)b * kTower + n];
-      A.out[o] = tot[r * NB + b] + A.bias[n] + resid;
+  for (int b = 0; b < NBM; ++b) {
+    if (b < A.B) {
+      const float v = wave_sum64(acc[b]);
+      if (lane == 0) {
+        const float resid = A.towers[(size_t)b * kTower + n] + A.towers[((size_t)A.B + b) * kTower + n] +
+                            A.towers[((size_t)2 * A.B + b) * kTower + n];
+        A.out[(size_t)b * kTower + n] = v + cI + resid;
+      }
     }
   }
 }
 
+// ----------------------------------------------------------- gated FFN
 struct GateUpArgs {
   const float* gamma;  // [T]
   const float* Wg;     // [F][T]
@@ -191,45 +177,53 @@ struct GateUpArgs {
   int B;
 };
 
-// grid (F / (kRows/2), 1, batch tiles): rows n0, n0+1 of both gate and up
-template <int NB>
+// One wave per R (gate, up) row pairs, K = T = 1024 (4 float4 per lane).
+// grid (F / (4R))
+template <int R, int NBM>
 __global__ void __launch_bounds__(kThreads) k_gateup(GateUpArgs A) {
-  constexpr int NP = kRows / 2;  // (gate, up) pairs per block
-  __shared__ float red[5 * (kRows * NB + NB)];
-  const int n0 = blockIdx.x * NP;
-  const int b0 = blockIdx.z * kMaxNB;
-  const int nb = min(NB, A.B - b0);
-  const float* u = A.u + (size_t)b0 * kTower;
-  float acc[kRows * NB + NB];
+  constexpr int KI = kTower / 256;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n0 = (blockIdx.x * kWaves + wave) * R;
+  float4 wg[R][KI], wu[R][KI], g[KI];
 #pragma unroll
-  for (int i = 0; i < kRows * NB + NB; ++i) acc[i] = 0.0f;
-  const int k = threadIdx.x * 4;  // T = 1024 = one pass
-  float4 w[kRows];
+  for (int r = 0; r < R; ++r)
 #pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    w[2 * p] = *reinterpret_cast<const float4*>(A.Wg + (size_t)(n0 + p) * kTower + k);
-    w[2 * p + 1] = *reinterpret_cast<const float4*>(A.Wu + (size_t)(n0 + p) * kTower + k);
-  }
-  const float4 gm = *reinterpret_cast<const float4*>(A.gamma + k);
+    for (int i = 0; i < KI; ++i) {
+      wg[r][i] = ld4(A.Wg + (size_t)(n0 + r) * kTower + 256 * i + lane * 4);
+      wu[r][i] = ld4(A.Wu + (size_t)(n0 + r) * kTower + 256 * i + lane * 4);
+    }
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    if (b < nb) {
-      const float4 xv = *reinterpret_cast<const float4*>(u + (size_t)b * kTower + k);
-      const float4 in = make_float4(xv.x * gm.x, xv.y * gm.y, xv.z * gm.z, xv.w * gm.w);
+  for (int i = 0; i < KI; ++i) g[i] = ld4(A.gamma + 256 * i + lane * 4);
+  float ag[R][NBM], au[R][NBM], ss[NBM];
 #pragma unroll
-      for (int r = 0; r < kRows; ++r) acc[r * NB + b] += dot4(w[r], in);
-      acc[kRows * NB + b] += dot4(xv, xv);
+  for (int b = 0; b < NBM; ++b) {
+    ss[b] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) ag[r][b] = au[r][b] = 0.0f;
+    if (b < A.B) {
+#pragma unroll
+      for (int i = 0; i < KI; ++i) {
+        const float4 xv = ld4(A.u + (size_t)b * kTower + 256 * i + lane * 4);
+        const float4 in = mul4(xv, g[i]);
+        ss[b] += dot4(xv, xv);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          ag[r][b] += dot4(wg[r][i], in);
+          au[r][b] += dot4(wu[r][i], in);
+        }
+      }
     }
   }
-  block_sum<kRows * NB + NB>(acc, red);
-  const float* tot = red + 4 * (kRows * NB + NB);
-  if (threadIdx.x < NP * NB) {
-    const int p = threadIdx.x / NB, b = threadIdx.x % NB;
-    if (b < nb) {
-      const float inv = rsqrtf(tot[kRows * NB + b] / (float)kTower + kEps);
-      const float g = tot[(2 * p) * NB + b] * inv;
-      const float up = tot[(2 * p + 1) * NB + b] * inv;
-      A.hdn[(size_t)(b0 + b) * kFfn + n0 + p] = silu(g) * up;
+#pragma unroll
+  for (int b = 0; b < NBM; ++b) {
+    if (b < A.B) {
+      const float inv = rsqrtf(wave_sum64(ss[b]) / (float)kTower + kEps);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float gv = wave_sum64(ag[r][b]) * inv;
+        const float uv = wave_sum64(au[r][b]) * inv;
+        if (lane == 0) A.hdn[(size_t)b * kFfn + n0 + r] = silu(gv) * uv;
+      }
     }
   }
 }
@@ -242,40 +236,37 @@ struct DownArgs {
   int B;
 };
 
-template <int NB>
+// One wave per output row, K = F = 2048 (8 float4 per lane).  grid (T / 4)
+template <int NBM>
 __global__ void __launch_bounds__(kThreads) k_down(DownArgs A) {
-  __shared__ float red[5 * kRows * NB];
-  const int n0 = blockIdx.x * kRows;
-  const int b0 = blockIdx.z * kMaxNB;
-  const int nb = min(NB, A.B - b0);
-  const float* h = A.hdn + (size_t)b0 * kFfn;
-  float acc[kRows * NB];
+  constexpr int KI = kFfn / 256;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = blockIdx.x * kWaves + wave;
+  float4 w[KI];
 #pragma unroll
-  for (int i = 0; i < kRows * NB; ++i) acc[i] = 0.0f;
-  for (int k = threadIdx.x * 4; k < kFfn; k += kThreads * 4) {
-    float4 w[kRows];
+  for (int i = 0; i < KI; ++i) w[i] = ld4(A.Wd + (size_t)n * kFfn + 256 * i + lane * 4);
+  float acc[NBM];
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) w[r] = *reinterpret_cast<const float4*>(A.Wd + (size_t)(n0 + r) * kFfn + k);
+  for (int b = 0; b < NBM; ++b) {
+    acc[b] = 0.0f;
+    if (b < A.B) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      if (b < nb) {
-        const float4 in = *reinterpret_cast<const float4*>(h + (size_t)b * kFfn + k);
-#pragma unroll
-        for (int r = 0; r < kRows; ++r) acc[r * NB + b] += dot4(w[r], in);
-      }
+      for (int i = 0; i < KI; ++i) acc[b] += dot4(w[i], ld4(A.hdn + (size_t)b * kFfn + 256 * i + lane * 4));
     }
   }
-  block_sum<kRows * NB>(acc, red);
-  const float* tot = red + 4 * kRows * NB;
-  if (threadIdx.x < kRows * NB) {
-    const int r = threadIdx.x / NB, b = threadIdx.x % NB;
-    if (b < nb) {
-      const size_t o = (size_t)(b0 + b) * kTower + n0 + r;
-      A.out[o] = A.u[o] + tot[r * NB + b];
+#pragma unroll
+  for (int b = 0; b < NBM; ++b) {
+    if (b < A.B) {
+      const float v = wave_sum64(acc[b]);
+      if (lane == 0) {
+        const size_t o = (size_t)b * kTower + n;
+        A.out[o] = A.u[o] + v;
+      }
     }
   }
 }
 
+// --------------------------------------------------- output, rule, work list
 struct OutArgs {
   const float* gamma;  // [T]
   const float* w;      // [T]
@@ -286,87 +277,88 @@ struct OutArgs {
   const int32_t* pos;
   float* score;
   uint8_t* flag;
-  int32_t* worklist;   // count, items
+  int32_t* worklist;  // count, items
   int B;
 };
 
-// One block: q for every sequence, the rule, and the work list.
-__global__ void __launch_bounds__(kThreads) k_out_rule(OutArgs A) {
-  __shared__ float red[5 * 2 * kMaxBatch];
-  __shared__ int counts[kMaxBatch];
-  __shared__ int starts[kMaxBatch + 1];
-  const int k = threadIdx.x * 4;
-  const float4 gm = *reinterpret_cast<const float4*>(A.gamma + k);
-  const float4 wv = *reinterpret_cast<const float4*>(A.w + k);
-  const float4 wg = make_float4(wv.x * gm.x, wv.y * gm.y, wv.z * gm.z, wv.w * gm.w);
-  float acc[2 * kMaxBatch];
+// Exclusive scan of the per-sequence split counts (lanes < B of one wave,
+// B <= 32) and the compacted items (b << 20) | split, b ascending.
+__device__ __forceinline__ void write_worklist(int cnt, int lane, int B, int* s_start, const int* s_count,
+                                               int32_t* worklist) {
+  int incl = cnt;
 #pragma unroll
-  for (int b = 0; b < kMaxBatch; ++b) {
-    if (b < A.B) {
-      const float4 x = *reinterpret_cast<const float4*>(A.u + (size_t)b * kTower + k);
-      acc[b] = dot4(wg, x);
-      acc[kMaxBatch + b] = dot4(x, x);
-    } else {
-      acc[b] = 0.0f;
-      acc[kMaxBatch + b] = 0.0f;
-    }
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
   }
-  block_sum<2 * kMaxBatch>(acc, red);
-  const float* tot = red + 4 * 2 * kMaxBatch;
-  if (threadIdx.x < A.B) {
-    const int b = threadIdx.x;
-    const float inv = rsqrtf(tot[kMaxBatch + b] / (float)kTower + kEps);
-    const float q = tot[b] * inv + A.c[0];
-    A.score[b] = q;
-    int f;
-    const int fo = A.force != nullptr ? (int)A.force[b] : -1;
-    if (fo >= 0) {
-      f = fo != 0;
-    } else {
-      f = (q > A.theta) || !isfinite(q);
-    }
-    A.flag[b] = (uint8_t)f;
-    counts[b] = f ? full_nsplit(A.pos[b] + 1) : 0;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int s = 0;
-    for (int b = 0; b < A.B; ++b) {
-      starts[b] = s;
-      s += counts[b];
-    }
-    starts[A.B] = s;
-    A.worklist[0] = s;
-  }
-  __syncthreads();
-  // each sequence writes its own items; lanes stride over (b, split)
-  for (int i = threadIdx.x; i < A.B * kFullMaxSplits; i += kThreads) {
+  if (lane < B) s_start[lane] = incl - cnt;
+  if (lane == B - 1) worklist[0] = incl;
+  __builtin_amdgcn_wave_barrier();
+  for (int i = lane; i < B * kFullMaxSplits; i += 64) {
     const int b = i / kFullMaxSplits, s = i % kFullMaxSplits;
-    if (s < counts[b]) A.worklist[1 + starts[b] + s] = (b << 20) | s;
+    if (s < s_count[b]) worklist[1 + s_start[b] + s] = (b << 20) | s;
   }
 }
 
-// smallest tile width in {1, 2, 4, 8} that holds min(B, 8) rows
-int nb_of(int B) { return B > 4 ? 8 : (B > 2 ? 4 : (B > 1 ? 2 : 1)); }
+// One block: wave w scores sequences w, w+4, ...; wave 0 then applies the
+// rule and writes the compacted work list (exclusive scan of flag * nsplit).
+__global__ void __launch_bounds__(kThreads) k_out_rule(OutArgs A) {
+  __shared__ float s_q[kMaxBatch];
+  __shared__ int s_start[kMaxBatch + 1];
+  __shared__ int s_count[kMaxBatch];
+  constexpr int KI = kTower / 256;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float4 wg[KI];
+#pragma unroll
+  for (int i = 0; i < KI; ++i) wg[i] = mul4(ld4(A.w + 256 * i + lane * 4), ld4(A.gamma + 256 * i + lane * 4));
+  for (int b = wave; b < A.B; b += kWaves) {
+    float d = 0.0f, ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const float4 x = ld4(A.u + (size_t)b * kTower + 256 * i + lane * 4);
+      d += dot4(wg[i], x);
+      ss += dot4(x, x);
+    }
+    d = wave_sum64(d);
+    ss = wave_sum64(ss);
+    if (lane == 0) s_q[b] = d * rsqrtf(ss / (float)kTower + kEps) + A.c[0];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  int cnt = 0;
+  if (lane < A.B) {
+    const float q = s_q[lane];
+    A.score[lane] = q;
+    const int fo = A.force != nullptr ? (int)A.force[lane] : -1;
+    const int f = fo >= 0 ? (fo != 0) : ((q > A.theta) || !isfinite(q));
+    A.flag[lane] = (uint8_t)f;
+    cnt = f ? full_nsplit(A.pos[lane] + 1) : 0;
+    s_count[lane] = cnt;
+  }
+  write_worklist(cnt, lane, A.B, s_start, s_count, A.worklist);
+}
 
-#define ODA_NB_DISPATCH(KERNEL, GRID, ARGS, B, S)                                         \
-  do {                                                                                   \
-    const int nb_ = nb_of(B);                                                            \
-    if (nb_ == 8) hipLaunchKernelGGL(KERNEL<8>, GRID, dim3(kThreads), 0, S, ARGS);       \
-    else if (nb_ == 4) hipLaunchKernelGGL(KERNEL<4>, GRID, dim3(kThreads), 0, S, ARGS);  \
-    else if (nb_ == 2) hipLaunchKernelGGL(KERNEL<2>, GRID, dim3(kThreads), 0, S, ARGS);  \
-    else hipLaunchKernelGGL(KERNEL<1>, GRID, dim3(kThreads), 0, S, ARGS);                \
-  } while (0)
+__global__ void __launch_bounds__(64) k_worklist(const uint8_t* flag, const int32_t* pos, int32_t* worklist, int B) {
+  __shared__ int s_start[kMaxBatch + 1];
+  __shared__ int s_count[kMaxBatch];
+  const int lane = threadIdx.x;
+  int cnt = 0;
+  if (lane < B) {
+    cnt = flag[lane] ? full_nsplit(pos[lane] + 1) : 0;
+    s_count[lane] = cnt;
+  }
+  write_worklist(cnt, lane, B, s_start, s_count, worklist);
+}
 
-}  // namespace
+int nbm_of(int B) { return B > 16 ? 32 : B > 8 ? 16 : B > 4 ? 8 : B > 2 ? 4 : B > 1 ? 2 : 1; }
 
-// offs: host array of the ODA_HEAD_NTENSORS+1 tensor offsets (oda_head_offsets order)
-int launch_recall_head(const HeadParams& p, const int64_t* offs, hipStream_t s) {
+template <int NBM>
+int launch_head_t(const HeadParams& p, const int64_t* offs, hipStream_t s) {
   const int B = p.B;
-  // tiles of 8 rows; a batch of B uses ceil(B/8) tiles (kernels guard b < B)
-  const int tiles = (B + kMaxNB - 1) / kMaxNB;
-  const int nbB = B > kMaxNB ? kMaxNB : B;
-
+#ifndef ODA_TOWER_ROWS
+#define ODA_TOWER_ROWS 1
+#endif
+  constexpr int R = NBM <= 8 ? ODA_TOWER_ROWS : 1;  // rows per wave: fewer when many batch accumulators are live
   TowerArgs ta;
   ta.w = p.w;
   for (int t = 0; t < 3; ++t) {
@@ -379,8 +371,13 @@ int launch_recall_head(const HeadParams& p, const int64_t* offs, hipStream_t s) 
   ta.x[2] = p.h_local;
   ta.out = p.act.towers;
   ta.B = B;
-  ta.D = p.D;
-  ODA_NB_DISPATCH(k_tower, dim3(kTower / kRows, 3, tiles), ta, nbB, s);
+  const dim3 tgrid(kTower / (kWaves * R), 3);
+  switch (p.D) {
+    case 1024: hipLaunchKernelGGL((k_tower<4, R, NBM>), tgrid, dim3(kThreads), 0, s, ta); break;
+    case 2048: hipLaunchKernelGGL((k_tower<8, R, NBM>), tgrid, dim3(kThreads), 0, s, ta); break;
+    case 4096: hipLaunchKernelGGL((k_tower<16, 1, NBM>), dim3(kTower / kWaves, 3), dim3(kThreads), 0, s, ta); break;
+    default: return ODA_E_UNSUPPORTED;
+  }
 
   InteractArgs ia;
   ia.W = p.w + offs[9];
@@ -388,7 +385,7 @@ int launch_recall_head(const HeadParams& p, const int64_t* offs, hipStream_t s) 
   ia.towers = p.act.towers;
   ia.out = p.act.u0;
   ia.B = B;
-  ODA_NB_DISPATCH(k_interact, dim3(kTower / kRows, 1, tiles), ia, nbB, s);
+  hipLaunchKernelGGL(k_interact<NBM>, dim3(kTower / kWaves), dim3(kThreads), 0, s, ia);
 
   const float* u_in = p.act.u0;
   float* u_out[2] = {p.act.u1, p.act.u2};
@@ -401,14 +398,14 @@ int launch_recall_head(const HeadParams& p, const int64_t* offs, hipStream_t s) 
     ga.u = u_in;
     ga.hdn = p.act.hdn;
     ga.B = B;
-    ODA_NB_DISPATCH(k_gateup, dim3(kFfn / (kRows / 2), 1, tiles), ga, nbB, s);
+    hipLaunchKernelGGL((k_gateup<R, NBM>), dim3(kFfn / (kWaves * R)), dim3(kThreads), 0, s, ga);
     DownArgs da;
     da.Wd = p.w + offs[base + 3];
     da.hdn = p.act.hdn;
     da.u = u_in;
     da.out = u_out[blk];
     da.B = B;
-    ODA_NB_DISPATCH(k_down, dim3(kTower / kRows, 1, tiles), da, nbB, s);
+    hipLaunchKernelGGL(k_down<NBM>, dim3(kTower / kWaves), dim3(kThreads), 0, s, da);
     u_in = u_out[blk];
   }
 
@@ -426,6 +423,25 @@ int launch_recall_head(const HeadParams& p, const int64_t* offs, hipStream_t s) 
   oa.B = B;
   hipLaunchKernelGGL(k_out_rule, dim3(1), dim3(kThreads), 0, s, oa);
   return hipGetLastError() == hipSuccess ? ODA_OK : ODA_E_LAUNCH;
+}
+
+}  // namespace
+
+// offs: host array of the ODA_HEAD_NTENSORS+1 tensor offsets (oda_head_offsets order)
+int launch_worklist(const uint8_t* flag, const int32_t* pos, int32_t* worklist, int B, hipStream_t s) {
+  hipLaunchKernelGGL(k_worklist, dim3(1), dim3(64), 0, s, flag, pos, worklist, B);
+  return hipGetLastError() == hipSuccess ? ODA_OK : ODA_E_LAUNCH;
+}
+
+int launch_recall_head(const HeadParams& p, const int64_t* offs, hipStream_t s) {
+  switch (nbm_of(p.B)) {
+    case 1: return launch_head_t<1>(p, offs, s);
+    case 2: return launch_head_t<2>(p, offs, s);
+    case 4: return launch_head_t<4>(p, offs, s);
+    case 8: return launch_head_t<8>(p, offs, s);
+    case 16: return launch_head_t<16>(p, offs, s);
+    default: return launch_head_t<32>(p, offs, s);
+  }
 }
 
 }  // namespace oda

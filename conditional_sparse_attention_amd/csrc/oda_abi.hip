@@ -261,6 +261,17 @@ int oda_recall_score(const oda_dims* dims, const float* head_w, const oda_bf16* 
   return launch_recall_head(p, offs, stream);
 }
 
+int oda_worklist(const oda_dims* dims, const uint8_t* flag, const int32_t* pos, void* ws, size_t ws_bytes,
+                 hipStream_t stream) {
+  int st;
+  if (!dims_valid(dims, &st)) return st;
+  if (flag == nullptr || pos == nullptr || ws == nullptr) return ODA_E_NULL;
+  const WsLayout L = ws_layout(dims);
+  if (ws_bytes < L.total) return ODA_E_WORKSPACE;
+  return launch_worklist(flag, pos, reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.worklist), dims->batch,
+                         stream);
+}
+
 int oda_commit(const oda_dims* dims, const oda_kv* kv, int32_t* pos, const uint8_t* flag, const oda_bf16* k_cur_L,
                const oda_bf16* v_cur_L, const oda_bf16* k_cur_F, const oda_bf16* v_cur_F,
                const oda_bf16* out_last_L, const oda_bf16* out_last_F, oda_bf16* h_prev, void* ws, size_t ws_bytes,

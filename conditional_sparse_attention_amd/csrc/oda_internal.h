@@ -114,6 +114,7 @@ struct HeadParams {
   HeadWs act;
 };
 int launch_recall_head(const HeadParams& p, const int64_t* offs, hipStream_t s);
+int launch_worklist(const uint8_t* flag, const int32_t* pos, int32_t* worklist, int B, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // commit / ranges / init
@@ -151,6 +152,32 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
+}
+
+// DPP move within a 16-lane row (compile-time control word).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the same bits.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_mov<0x141>(x);  // row_half_mirror
+  x += dpp_mov<0x140>(x);  // row_mirror
+  return x;
+}
+
+// Sum over the 64 lanes of a wave, identical (wave-uniform) in every lane:
+// row sums by DPP, then the four row results read out and added in fixed order.
+__device__ __forceinline__ float wave_sum64(float x) {
+  x = row16_sum(x);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 // Local index set S^L of a sequence whose current 0-based position is t-1:

@@ -188,6 +188,14 @@ int oda_recall_score(const oda_dims *dims, const float *head_w, const oda_bf16 *
                      const int32_t *pos, float *score, uint8_t *flag, void *ws, size_t ws_bytes,
                      hipStream_t stream);
 
+/* Device-side compaction alone [row A6]: writes the full-branch work list
+ * of the workspace from caller-given flags (flag[b] != 0 -> sequence b runs
+ * the full branch), exactly as oda_recall_score does after its rule.  For
+ * schedules decided outside the head (forced calls, an always-full
+ * baseline).  flag, pos: [B]. */
+int oda_worklist(const oda_dims *dims, const uint8_t *flag, const int32_t *pos, void *ws, size_t ws_bytes,
+                 hipStream_t stream);
+
 /* Full-branch attention of layer `layer` over S^F = [0, pos[b]] for the
  * sequences on the work list [ODA notes §2.1 eq. o_t over S^F; §2.3: the
  * full branch restarts from the same pre-step state, so it reads the cache

@@ -149,3 +149,23 @@ def test_device_generator_paged_matches_contig():
     K2 = torch.zeros_like(pr.K)
     sd.fill_cache(K2, wl, synth.TAG_K, pr.t0_dev, tables=pr.tables, num_blocks=pr.num_blocks)
     assert torch.equal(K2, pr.K)
+
+
+def test_worklist_entry_point_bitexact():
+    """oda_worklist (compaction from caller flags) writes the same list as
+    the oracle's work list for ragged positions and mixed flags."""
+    from oracle import full_worklist
+    rng = np.random.default_rng(5)
+    for B in (1, 7, 32):
+        pos = rng.integers(0, 200000, size=B).astype(np.int32)
+        flags = rng.integers(0, 2, size=B).astype(np.uint8)
+        dims = C.make_dims(2, B, 16, 8, t_cap=1 << 18)
+        ws = torch.zeros(C.oda_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+        C.oda_workspace_init(dims, ws)
+        C.oda_worklist(dims, torch.from_numpy(flags).cuda(), torch.from_numpy(pos).cuda(), ws)
+        torch.cuda.synchronize()
+        off = C.oda_workspace_worklist_offset(dims)
+        w = ws[off:].view(torch.int32).cpu().numpy()
+        got = [(int(x) >> 20, int(x) & 0xFFFFF) for x in w[1:1 + w[0]]]
+        nsplit = [min(32, -(-(int(p) + 1) // 1024)) for p in pos]
+        assert got == full_worklist(flags, nsplit)
