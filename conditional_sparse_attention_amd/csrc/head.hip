@@ -350,6 +350,386 @@ __global__ void __launch_bounds__(64) k_worklist(const uint8_t* flag, const int3
   write_worklist(cnt, lane, B, s_start, s_count, worklist);
 }
 
+// ------------------------------------------------ dense batches: fp32 MFMA
+// From about ten sequences on, the same layers are dense enough to run as
+// skinny GEMMs on the matrix cores: Y[n][col] = sum_k W[n][k] X[col][k] with
+// v_mfma_f32_16x16x4f32, A = 16 weight rows x 4 k, B = 4 k x 16 batch
+// columns.  In lane l = 16q + i the instruction takes A[i][q] and B[q][i] and
+// returns D[4q + r][i] in accumulator component r.
+//
+// A workgroup owns TW row tiles (16 rows each) and one of KSPLIT slices of K;
+// each of its NW waves takes JB blocks of 16 k: lane (i, q) loads the float4
+// at k_j + 4q of weight row i of every tile and of batch column i, so one
+// load instruction reads 64 contiguous bytes of 16 rows, and sub-step (j, c)
+// pairs component c of the lane's j-th float4 on both operands (any fixed
+// pairing of k between A and B gives the same sum).  In the dense layers the
+// blocks are 4 consecutive ones (k_j = k0 + 16j); in the interaction they are
+// the 9 segments at one position (k_j = 1024 j + p), so a lane reads a, b and
+// c once and forms all nine segment values from them.  Every operand is
+// consumed straight from the load: the RMSNorm gain is applied to X as it
+// arrives and the sum of squares is gathered from the same registers (the
+// 1/rms scale is applied to the finished dot product).
+// The waves of a workgroup are summed through LDS, the KSPLIT workgroups of a
+// row block through coherent partial tiles: the last to take the row block's
+// ticket adds them in split order (deterministic) and applies the layer's
+// epilogue.
+using f4v = __attribute__((ext_vector_type(4))) float;
+
+enum DenseMode { kTowerMode = 0, kInterMode = 1, kGateUpMode = 2, kDownMode = 3 };
+
+struct DenseArgs {
+  const float* W[3];      // weights [N][K]: one per tower; gate, up for the FFN
+  const float* gamma[3];  // RMSNorm gains [K]
+  const float* bias[3];   // [N]
+  const uint16_t* xb[3];  // bf16 tower inputs [B][K]
+  const float* xf;        // fp32 input [B][K]; the towers [3][B][T] for the interaction
+  const float* resid;     // [B][T] residual of the down projection
+  float* out[3];          // [B][N] per tower / layer output
+  float* part;
+  int32_t* tickets;
+  int B;
+};
+
+__device__ __forceinline__ void part_put(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float part_get(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float comp(const float4 v, int c) {
+  return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
+}
+__device__ __forceinline__ float f4v_comp(const f4v v, int r) { return v[r]; }
+__device__ __forceinline__ float4 as_f4(const uint4 u) {
+  return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+}
+
+template <int TW, int NG>
+constexpr int dense_part_stride() {
+  return TW * NG * 4 * 64 + 64;  // accumulator tile, then one sum of squares per column
+}
+
+template <int MODE>
+constexpr int dense_jb() {
+  return MODE == kInterMode ? 9 : 4;
+}
+
+template <int MODE, int K, int TW, int NW, int NG, int KSPLIT>
+__global__ void __launch_bounds__(NW * 64) k_dense(DenseArgs A) {
+  constexpr int JB = dense_jb<MODE>();    // 16-k blocks per wave
+  static_assert(K == KSPLIT * NW * JB * 16, "K slices");
+  constexpr int NT = NW * 64;
+  constexpr int NV = TW * NG * 4;         // accumulator floats per lane
+  constexpr int PMAIN = NV * 64;
+  constexpr int PSZ = dense_part_stride<TW, NG>();
+  constexpr bool kNorm = MODE == kTowerMode || MODE == kGateUpMode;
+  constexpr int HALF = TW / 2;            // gate tiles of the FFN pairs
+  constexpr int ROWS = MODE == kGateUpMode ? HALF * 16 : TW * 16;
+  constexpr int VPR = NV < 128 / NW ? NV : 128 / NW;  // values per LDS round (32 KB)
+  __shared__ float red[NW * VPR * 64];
+  __shared__ float s_inv[32];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 15, lq = lane >> 4;
+  const int rb = blockIdx.x, ks = blockIdx.y, z = blockIdx.z;
+  const int B = A.B;
+  // k of this lane's float4 in block j: k0 + kstep * j
+  constexpr int kstep = MODE == kInterMode ? kTower : 16;
+  const int k0 = (MODE == kInterMode ? (ks * NW + wave) * 16 : (ks * NW + wave) * 64) + 4 * lq;
+
+  // Batch columns past B repeat column B-1: a column of B only reaches the
+  // same column of the result, and those outputs are never written.
+  // Loads go out first (batch operands from L2, then every weight load from
+  // HBM), the scheduler is fenced so none of them slides behind arithmetic,
+  // and the operand transforms wait only for the batch loads.
+  constexpr int XR = MODE == kInterMode ? 3 : 4;  // loads per column group
+  uint4 xr[NG][XR];
+  float4 g[4];
+  if (kNorm) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) g[j] = ld4(A.gamma[z] + k0 + 16 * j);
+  }
+#pragma unroll
+  for (int cg = 0; cg < NG; ++cg) {
+    const int col = min(16 * cg + li, B - 1);
+    if (MODE == kTowerMode) {
+      const uint16_t* xp = A.xb[z] + (size_t)col * K + k0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint2 v = *reinterpret_cast<const uint2*>(xp + 16 * j);
+        xr[cg][j] = make_uint4(v.x, v.y, 0u, 0u);
+      }
+    } else if (MODE == kInterMode) {
+      const float* ta = A.xf + (size_t)col * kTower + k0;
+#pragma unroll
+      for (int tw = 0; tw < 3; ++tw) xr[cg][tw] = *reinterpret_cast<const uint4*>(ta + (size_t)tw * B * kTower);
+    } else {
+      const float* xp = A.xf + (size_t)col * K + k0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xr[cg][j] = *reinterpret_cast<const uint4*>(xp + 16 * j);
+    }
+  }
+  float4 w[TW][JB];
+#pragma unroll
+  for (int t = 0; t < TW; ++t) {
+    const float* Wt;
+    int row;
+    if (MODE == kGateUpMode) {
+      Wt = A.W[t < HALF ? 0 : 1];
+      row = rb * ROWS + 16 * (t < HALF ? t : t - HALF) + li;
+    } else {
+      Wt = A.W[z];
+      row = rb * ROWS + 16 * t + li;
+    }
+    const float* wp = Wt + (size_t)row * K + k0;
+#pragma unroll
+    for (int j = 0; j < JB; ++j) w[t][j] = ld4(wp + kstep * j);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  float4 x[NG][JB];
+  float ss[NG];
+#pragma unroll
+  for (int cg = 0; cg < NG; ++cg) {
+    if (MODE == kTowerMode) {
+#pragma unroll
+      for (int j = 0; j < JB; ++j)
+        x[cg][j] = make_float4(bf16lo(xr[cg][j].x), bf16hi(xr[cg][j].x), bf16lo(xr[cg][j].y), bf16hi(xr[cg][j].y));
+    } else if (MODE == kInterMode) {
+      // [a, b, c, ab, ac, bc, |a-b|, |a-c|, |b-c|]
+      const float4 a = as_f4(xr[cg][0]), b = as_f4(xr[cg][1]), c = as_f4(xr[cg][2]);
+#pragma unroll
+      for (int j = 0; j < JB; ++j) x[cg][j] = seg_value(j, a, b, c);
+    } else {
+#pragma unroll
+      for (int j = 0; j < JB; ++j) x[cg][j] = as_f4(xr[cg][j]);
+    }
+    ss[cg] = 0.0f;
+    if (kNorm) {
+#pragma unroll
+      for (int j = 0; j < JB; ++j) {
+        ss[cg] += dot4(x[cg][j], x[cg][j]);
+        x[cg][j] = mul4(x[cg][j], g[j]);
+      }
+    }
+  }
+
+  f4v acc[TW][NG];
+#pragma unroll
+  for (int t = 0; t < TW; ++t)
+#pragma unroll
+    for (int cg = 0; cg < NG; ++cg) acc[t][cg] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < JB; ++j)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int t = 0; t < TW; ++t)
+#pragma unroll
+        for (int cg = 0; cg < NG; ++cg)
+          acc[t][cg] = __builtin_amdgcn_mfma_f32_16x16x4f32(comp(w[t][j], c), comp(x[cg][j], c), acc[t][cg], 0, 0, 0);
+
+  // ---- sum the waves (LDS), store this workgroup's partial tile
+  const int rbg = z * gridDim.x + rb;
+  float* part = A.part + ((size_t)rbg * KSPLIT + ks) * PSZ;
+#pragma unroll
+  for (int r0 = 0; r0 < NV; r0 += VPR) {
+#pragma unroll
+    for (int v = 0; v < VPR; ++v) {
+      const int vv = r0 + v;
+      red[(wave * VPR + v) * 64 + lane] = f4v_comp(acc[vv / (NG * 4)][(vv / 4) % NG], vv % 4);
+    }
+    __syncthreads();
+    for (int i = tid; i < VPR * 64; i += NT) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int wv = 0; wv < NW; ++wv) sum += red[wv * VPR * 64 + i];
+      part_put(part + r0 * 64 + i, sum);
+    }
+    __syncthreads();
+  }
+  if (kNorm) {
+#pragma unroll
+    for (int cg = 0; cg < NG; ++cg) red[(wave * NG + cg) * 64 + lane] = ss[cg];
+    __syncthreads();
+    if (tid < NG * 16) {
+      const int cg = tid >> 4, i = tid & 15;
+      float sum = 0.0f;
+      for (int wv = 0; wv < NW; ++wv)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sum += red[(wv * NG + cg) * 64 + 16 * q + i];
+      part_put(part + PMAIN + tid, sum);
+    }
+  }
+
+  // ---- hand-off: the last workgroup of the row block finishes it
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(A.tickets + rbg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == KSPLIT - 1;
+  __syncthreads();
+  if (!s_last) return;
+
+  const float* pb = A.part + (size_t)rbg * KSPLIT * PSZ;
+  constexpr int NOUT = MODE == kGateUpMode ? PMAIN / 2 : PMAIN;
+  static_assert(NOUT % NT == 0, "outputs per thread");
+  constexpr int NO = NOUT / NT;
+  constexpr int NSUM = MODE == kGateUpMode ? 2 : 1;
+  // every partial this thread needs (sums of squares included) in one batch
+  // of loads, then added in split order
+  float sq[KSPLIT];
+  if (kNorm && tid < NG * 16) {
+#pragma unroll
+    for (int sp = 0; sp < KSPLIT; ++sp) sq[sp] = part_get(pb + (size_t)sp * PSZ + PMAIN + tid);
+  }
+  float pv[NO][NSUM][KSPLIT];
+#pragma unroll
+  for (int o = 0; o < NO; ++o)
+#pragma unroll
+    for (int h = 0; h < NSUM; ++h)
+#pragma unroll
+      for (int sp = 0; sp < KSPLIT; ++sp)
+        pv[o][h][sp] = part_get(pb + (size_t)sp * PSZ + h * (PMAIN / 2) + tid + o * NT);
+  if (kNorm) {
+    if (tid < NG * 16) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int sp = 0; sp < KSPLIT; ++sp) sum += sq[sp];
+      s_inv[tid] = rsqrtf(sum / (float)K + kEps);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int o = 0; o < NO; ++o) {
+    const int i = tid + o * NT;
+    const int v = i >> 6, l = i & 63;
+    const int t = v / (NG * 4), cg = (v >> 2) % NG, r = v & 3;
+    const int col = 16 * cg + (l & 15);
+    const int n = rb * ROWS + 16 * t + 4 * (l >> 4) + r;
+    float y = 0.0f;
+#pragma unroll
+    for (int sp = 0; sp < KSPLIT; ++sp) y += pv[o][0][sp];
+    if (col >= B) continue;
+    if (MODE == kTowerMode) {
+      A.out[z][(size_t)col * kTower + n] = silu(y * s_inv[col] + A.bias[z][n]);
+    } else if (MODE == kInterMode) {
+      const float* ta = A.xf + (size_t)col * kTower + n;
+      const float resid = ta[0] + ta[(size_t)B * kTower] + ta[(size_t)2 * B * kTower];
+      A.out[0][(size_t)col * kTower + n] = y + A.bias[0][n] + resid;
+    } else if (MODE == kGateUpMode) {
+      float yu = 0.0f;
+#pragma unroll
+      for (int sp = 0; sp < KSPLIT; ++sp) yu += pv[o][NSUM - 1][sp];
+      const float inv = s_inv[col];
+      A.out[0][(size_t)col * kFfn + n] = silu(y * inv) * (yu * inv);
+    } else {
+      const size_t oo = (size_t)col * kTower + n;
+      A.out[0][oo] = A.resid[oo] + y;
+    }
+  }
+  if (tid == 0) __hip_atomic_store(A.tickets + rbg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Shapes of the dense layers: tiles per wave, waves per workgroup, K slices.
+// K = KSPLIT * NW * 64 (the interaction: KSPLIT * NW * 16 positions of its 9
+// segments); each keeps a few hundred workgroups in flight.
+struct DenseShape {
+  int tw, nw, ksplit, rowblocks, z;
+};
+DenseShape tower_shape(int D) {
+  return D == 4096 ? DenseShape{4, 8, 8, kTower / 64, 3} : D == 2048 ? DenseShape{4, 4, 8, kTower / 64, 3}
+                                                                     : DenseShape{4, 4, 4, kTower / 64, 3};
+}
+constexpr DenseShape kInterShape{2, 8, 8, kTower / 32, 1};
+constexpr DenseShape kGateUpShape{4, 4, 4, kFfn / 32, 1};
+constexpr DenseShape kDownShape{2, 4, 8, kTower / 32, 1};
+
+size_t shape_part_floats(const DenseShape& s, int ng) {
+  return (size_t)s.z * s.rowblocks * s.ksplit * (s.tw * ng * 4 * 64 + 64);
+}
+
+template <int NG>
+int launch_dense_t(const HeadParams& p, const int64_t* offs, hipStream_t s) {
+  const int B = p.B;
+  const dim3 blk256(256), blk512(512);
+  DenseArgs ta{};
+  for (int t = 0; t < 3; ++t) {
+    ta.gamma[t] = p.w + offs[3 * t + 0];
+    ta.W[t] = p.w + offs[3 * t + 1];
+    ta.bias[t] = p.w + offs[3 * t + 2];
+    ta.out[t] = p.act.towers + (size_t)t * B * kTower;
+  }
+  ta.xb[0] = p.h_prev;
+  ta.xb[1] = p.emb;
+  ta.xb[2] = p.h_local;
+  ta.part = p.act.part;
+  ta.tickets = p.tickets;
+  ta.B = B;
+  const DenseShape ts = tower_shape(p.D);
+  const dim3 tgrid(ts.rowblocks, ts.ksplit, 3);
+  switch (p.D) {
+    case 1024: hipLaunchKernelGGL((k_dense<kTowerMode, 1024, 4, 4, NG, 4>), tgrid, blk256, 0, s, ta); break;
+    case 2048: hipLaunchKernelGGL((k_dense<kTowerMode, 2048, 4, 4, NG, 8>), tgrid, blk256, 0, s, ta); break;
+    case 4096: hipLaunchKernelGGL((k_dense<kTowerMode, 4096, 4, 8, NG, 8>), tgrid, blk512, 0, s, ta); break;
+    default: return ODA_E_UNSUPPORTED;
+  }
+
+  DenseArgs ia{};
+  ia.W[0] = p.w + offs[9];
+  ia.bias[0] = p.w + offs[10];
+  ia.xf = p.act.towers;
+  ia.out[0] = p.act.u0;
+  ia.part = p.act.part;
+  ia.tickets = p.tickets;
+  ia.B = B;
+  hipLaunchKernelGGL((k_dense<kInterMode, 9 * kTower, 2, 8, NG, 8>),
+                     dim3(kInterShape.rowblocks, kInterShape.ksplit), blk512, 0, s, ia);
+
+  const float* u_in = p.act.u0;
+  float* u_out[2] = {p.act.u1, p.act.u2};
+  for (int b = 0; b < 2; ++b) {
+    const int base = 11 + 4 * b;
+    DenseArgs ga{};
+    ga.gamma[0] = p.w + offs[base + 0];
+    ga.W[0] = p.w + offs[base + 1];
+    ga.W[1] = p.w + offs[base + 2];
+    ga.xf = u_in;
+    ga.out[0] = p.act.hdn;
+    ga.part = p.act.part;
+    ga.tickets = p.tickets;
+    ga.B = B;
+    hipLaunchKernelGGL((k_dense<kGateUpMode, kTower, 4, 4, NG, 4>),
+                       dim3(kGateUpShape.rowblocks, kGateUpShape.ksplit), blk256, 0, s, ga);
+    DenseArgs da{};
+    da.W[0] = p.w + offs[base + 3];
+    da.xf = p.act.hdn;
+    da.resid = u_in;
+    da.out[0] = u_out[b];
+    da.part = p.act.part;
+    da.tickets = p.tickets;
+    da.B = B;
+    hipLaunchKernelGGL((k_dense<kDownMode, kFfn, 2, 4, NG, 8>), dim3(kDownShape.rowblocks, kDownShape.ksplit),
+                       blk256, 0, s, da);
+    u_in = u_out[b];
+  }
+
+  OutArgs oa;
+  oa.gamma = p.w + offs[19];
+  oa.w = p.w + offs[20];
+  oa.c = p.w + offs[21];
+  oa.u = u_in;
+  oa.theta = p.theta;
+  oa.force = p.force;
+  oa.pos = p.pos;
+  oa.score = p.score;
+  oa.flag = p.flag;
+  oa.worklist = p.worklist;
+  oa.B = B;
+  hipLaunchKernelGGL(k_out_rule, dim3(1), dim3(kThreads), 0, s, oa);
+  return hipGetLastError() == hipSuccess ? ODA_OK : ODA_E_LAUNCH;
+}
+
 int nbm_of(int B) { return B > 16 ? 32 : B > 8 ? 16 : B > 4 ? 8 : B > 2 ? 4 : B > 1 ? 2 : 1; }
 
 template <int NBM>
@@ -427,6 +807,17 @@ int launch_head_t(const HeadParams& p, const int64_t* offs, hipStream_t s) {
 
 }  // namespace
 
+size_t dense_head_part_floats(int B, int D) {
+  const int ng = B > 16 ? 2 : 1;
+  size_t m = shape_part_floats(tower_shape(D), ng);
+  const DenseShape others[3] = {kInterShape, kGateUpShape, kDownShape};
+  for (const DenseShape& s : others) {
+    const size_t n = shape_part_floats(s, ng);
+    if (n > m) m = n;
+  }
+  return m;
+}
+
 // offs: host array of the ODA_HEAD_NTENSORS+1 tensor offsets (oda_head_offsets order)
 int launch_worklist(const uint8_t* flag, const int32_t* pos, int32_t* worklist, int B, hipStream_t s) {
   hipLaunchKernelGGL(k_worklist, dim3(1), dim3(64), 0, s, flag, pos, worklist, B);
@@ -434,6 +825,7 @@ int launch_worklist(const uint8_t* flag, const int32_t* pos, int32_t* worklist, 
 }
 
 int launch_recall_head(const HeadParams& p, const int64_t* offs, hipStream_t s) {
+  if (p.B >= kHeadDenseMin) return p.B > 16 ? launch_dense_t<2>(p, offs, s) : launch_dense_t<1>(p, offs, s);
   switch (nbm_of(p.B)) {
     case 1: return launch_head_t<1>(p, offs, s);
     case 2: return launch_head_t<2>(p, offs, s);

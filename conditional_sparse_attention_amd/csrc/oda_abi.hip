@@ -67,12 +67,14 @@ WsLayout ws_layout(const oda_dims* d) {
   at = align256(at + (size_t)B * Hkv * sizeof(int32_t));
   L.tick_commit = at;
   at = align256(at + (size_t)B * sizeof(int32_t));
+  L.tick_head = at;
+  at = align256(at + (size_t)kHeadTickets * sizeof(int32_t));
   L.part_local = at;
   at = align256(at + (size_t)B * Hkv * kLocalMaxSplits * G * kPartStride * sizeof(float));
   L.part_full = at;
   at = align256(at + (size_t)B * Hkv * kFullMaxSplits * G * kPartStride * sizeof(float));
   L.head = at;
-  at = align256(at + head_ws_floats(B) * sizeof(float));
+  at = align256(at + head_ws_floats(B, d->hidden) * sizeof(float));
   L.total = at;
   L.t_max = d->kv_layout == ODA_KV_CONTIG ? d->t_cap : (int64_t)d->block_size * d->max_blocks_per_seq;
   return L;
@@ -257,7 +259,8 @@ int oda_recall_score(const oda_dims* dims, const float* head_w, const oda_bf16* 
   p.worklist = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.worklist);
   p.B = dims->batch;
   p.D = dims->hidden;
-  p.act = head_ws(ws, L, dims->batch);
+  p.tickets = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.tick_head);
+  p.act = head_ws(ws, L, dims->batch, dims->hidden);
   return launch_recall_head(p, offs, stream);
 }
 

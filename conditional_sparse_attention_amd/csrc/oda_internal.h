@@ -30,9 +30,10 @@ struct WsLayout {
   size_t tick_local;   // int32[B * Hkv]
   size_t tick_full;    // int32[B * Hkv]
   size_t tick_commit;  // int32[B]
+  size_t tick_head;    // int32[kHeadTickets] (dense-batch head GEMM)
   size_t part_local;   // float[B * Hkv * kLocalMaxSplits * G * kPartStride]
   size_t part_full;    // float[B * Hkv * kFullMaxSplits * G * kPartStride]
-  size_t head;         // float: towers[3][B][T], u[B][T], hdn[B][F], u1[B][T], u2[B][T]
+  size_t head;         // float: see HeadWs
   size_t total;
   int64_t t_max;            // capacity of one sequence in positions
 };
@@ -47,14 +48,24 @@ bool dims_valid(const oda_dims* d, int* status);
 WsLayout ws_layout(const oda_dims* d);
 
 // head activation sub-regions (float offsets inside WsLayout::head)
+constexpr int kHeadTickets = 256;
+constexpr int kHeadDenseMin = 9;  // batches from here on take the dense (MFMA) head path
 struct HeadWs {
   float* towers;  // [3][B][T]  (a, b, c)
   float* u0;      // [B][T]
   float* hdn;     // [B][F]
   float* u1;      // [B][T]
   float* u2;      // [B][T]
+  float* part;    // split-K partial tiles of the dense path (B >= kHeadDenseMin)
 };
-inline HeadWs head_ws(void* ws, const WsLayout& L, int B) {
+// floats of split-K partial tiles the dense head GEMMs need (largest layer)
+size_t dense_head_part_floats(int B, int D);
+inline size_t head_ws_floats(int B, int D) {
+  size_t n = (size_t)B * (3 * kTower + kTower + kFfn + 2 * kTower);
+  if (B >= kHeadDenseMin) n += dense_head_part_floats(B, D);
+  return n;
+}
+inline HeadWs head_ws(void* ws, const WsLayout& L, int B, int D) {
   float* base = reinterpret_cast<float*>(static_cast<char*>(ws) + L.head);
   HeadWs h;
   h.towers = base;
@@ -62,9 +73,9 @@ inline HeadWs head_ws(void* ws, const WsLayout& L, int B) {
   h.hdn = h.u0 + B * kTower;
   h.u1 = h.hdn + B * kFfn;
   h.u2 = h.u1 + B * kTower;
+  h.part = h.u2 + B * kTower;
   return h;
 }
-inline size_t head_ws_floats(int B) { return (size_t)B * (3 * kTower + kTower + kFfn + 2 * kTower); }
 
 // ---------------------------------------------------------------------------
 // attention launch parameters
@@ -110,10 +121,12 @@ struct HeadParams {
   float* score;
   uint8_t* flag;
   int32_t* worklist;
+  int32_t* tickets;   // kHeadTickets, zero between calls
   int32_t B, D;
   HeadWs act;
 };
 int launch_recall_head(const HeadParams& p, const int64_t* offs, hipStream_t s);
+int launch_recall_head_dense(const HeadParams& p, const int64_t* offs, hipStream_t s);
 int launch_worklist(const uint8_t* flag, const int32_t* pos, int32_t* worklist, int B, hipStream_t s);
 
 // ---------------------------------------------------------------------------

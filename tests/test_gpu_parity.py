@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import synth
-from oracle import local_index_set
+from oracle import branch_rule, local_index_set, recall_score, unpack_head
 
 pytestmark = pytest.mark.gpu
 
@@ -169,3 +169,51 @@ def test_worklist_entry_point_bitexact():
         got = [(int(x) >> 20, int(x) & 0xFFFFF) for x in w[1:1 + w[0]]]
         nsplit = [min(32, -(-(int(p) + 1) // 1024)) for p in pos]
         assert got == full_worklist(flags, nsplit)
+
+
+@pytest.mark.parametrize("B,hq", [(1, 16), (8, 16), (9, 8), (16, 32), (17, 16), (32, 8), (32, 32), (24, 16)])
+def test_recall_head_batch_sizes(B, hq):
+    """oda_recall_score alone, on both sides of the switch from the
+    bandwidth-shaped GEMV (up to 8 sequences) to the fp32 MFMA GEMMs (9 and
+    up: one 16-wide column group through 16, two from 17), at D = 1024, 2048
+    and 4096, with a perturbed head so every bias and gain term counts.
+    Scores to 1e-4 (1 + |q|); flags bit-exact outside the tie band; the work
+    list bit-exact against the oracle's for the GPU's flags."""
+    from oracle import full_worklist
+    from _harness import SCORE_TOL, TIE_BAND
+    D = hq * 128
+    seed = 40 + B
+    blob = synth.head_blob(D, seed, perturb=True)
+    P = unpack_head(blob, D)
+    idx = np.arange(B * D)
+    xs = [synth.bf16_at(seed, tag, idx).reshape(B, D) for tag in (synth.TAG_H0, synth.TAG_E, synth.TAG_QL)]
+    pos = synth.word32_at(seed, synth.TAG_LEN, np.arange(B)).astype(np.int64) % 150000
+    pos = pos.astype(np.int32)
+    force = np.full(B, -1, np.int8)
+    force[::5] = 1
+    dims = C.make_dims(1, B, hq, 8, t_cap=1 << 18)
+    ws = torch.zeros(C.oda_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    C.oda_workspace_init(dims, ws)
+    dev = [to_dev_u16(x) for x in xs]
+    w = torch.from_numpy(blob).cuda()
+    score = torch.zeros(B, dtype=torch.float32, device="cuda")
+    flag = torch.zeros(B, dtype=torch.uint8, device="cuda")
+    qs = np.array([recall_score(P, xs[0][b], xs[1][b], xs[2][b]) for b in range(B)])
+    theta = float(np.median(qs))
+    for rep in range(2):  # the second call reuses the zeroed tickets of the first
+        C.oda_recall_score(dims, w, dev[0], dev[1], dev[2], theta, torch.from_numpy(force).cuda(),
+                           torch.from_numpy(pos).cuda(), score, flag, ws)
+        torch.cuda.synchronize()
+        got = score.cpu().numpy().astype(np.float64)
+        err = np.abs(got - qs)
+        assert np.all(err <= SCORE_TOL * (1 + np.abs(qs))), (rep, float(np.max(err / (1 + np.abs(qs)))))
+        f = flag.cpu().numpy()
+        for b in range(B):
+            want = branch_rule(qs[b], theta, int(force[b]))
+            if force[b] >= 0 or abs(qs[b] - theta) >= TIE_BAND:
+                assert f[b] == want, (b, qs[b], theta)
+        off = C.oda_workspace_worklist_offset(dims)
+        wl_ = ws[off:].view(torch.int32).cpu().numpy()
+        items = [(int(x) >> 20, int(x) & 0xFFFFF) for x in wl_[1:1 + wl_[0]]]
+        nsplit = [min(32, -(-(int(p) + 1) // 1024)) for p in pos]
+        assert items == full_worklist(f, nsplit)
