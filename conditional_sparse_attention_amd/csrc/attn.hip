@@ -48,13 +48,17 @@ typedef __attribute__((address_space(1))) const v4u_t gv4_t;
 #endif
 
 #ifndef ODA_LOCAL_DEPTH
-#define ODA_LOCAL_DEPTH 4
+#define ODA_LOCAL_DEPTH 2
 #endif
 #ifndef ODA_FULL_DEPTH
 #define ODA_FULL_DEPTH 3
 #endif
+// The local set is small (at most sink + window keys per sequence and KV
+// head): 8 workgroups per pair already spread it over the chip, and each
+// further split lengthens the cross-workgroup merge more than it shortens the
+// streaming.
 #ifndef ODA_LOCAL_SPLITS
-#define ODA_LOCAL_SPLITS 16
+#define ODA_LOCAL_SPLITS 8
 #endif
 #ifndef ODA_LOCAL_WAVES
 #define ODA_LOCAL_WAVES 4
