@@ -57,6 +57,12 @@ def parse():
                          "attention and no recall head (the feed, the work list, the full attention, the commit)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--matrix", action="store_true",
+                    help="context x forced recall-rate matrix at batch 1, warm and first-request timings "
+                         "(one JSON line per cell, then a summary line)")
+    ap.add_argument("--matrix-contexts", default="4096,16384,32768,65536,131072")
+    ap.add_argument("--matrix-rates", default="0,0.125,0.25,0.5,1")
+    ap.add_argument("--matrix-cell", default="", help=argparse.SUPPRESS)  # child process: CONTEXT:RATE, cold run
     return ap.parse_args()
 
 
@@ -66,11 +72,21 @@ def main():
         print(json.dumps({"error": "single-GPU build: this benchmark runs on one GPU only; "
                                    "multi-GPU runs are not part of it", "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.matrix:
+        return matrix(args)
     import torch
     import synth
     import synth.device as sd
     import conditional_sparse_attention_amd as C
     from conditional_sparse_attention_amd.step import StepBuffers, StepPlan
+
+    if args.matrix_cell:
+        ctx, rate = args.matrix_cell.split(":")
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            print(json.dumps(matrix_cell(int(ctx), float(rate), args, stream, torch, synth, sd, C, StepBuffers,
+                                         StepPlan, cold=True)), flush=True)
+        return
 
     wl_key = int(args.workload) if args.workload.isdigit() else args.workload
     wl = synth.workloads()[wl_key]
@@ -422,6 +438,151 @@ def cpu_baseline(wl, blob, theta, rate):
                        f"({t_full:.2f} s); scaled to {L} layers x {B} sequences and {rate:.3f}*{B} flagged "
                        f"sequences per step"),
             "sample_cpu_s": round(t_local + t_head + t_full, 2)}
+
+
+# ---------------------------------------------------------------------------
+# context x recall-rate matrix (batch 1), warm and first-request timings
+# ---------------------------------------------------------------------------
+MATRIX_LAYERS, MATRIX_HQ, MATRIX_HKV = 28, 16, 8
+
+
+def matrix_workload(ctx, steps, synth):
+    return synth.Workload(f"matrix-{ctx}", MATRIX_LAYERS, MATRIX_HQ, MATRIX_HKV, 128, 1,
+                          np.array([ctx], dtype=np.int64), steps, seed=3, head_seed=103, t_cap_slack=16)
+
+
+def matrix_cell(ctx, rate, args, stream, torch, synth, sd, C, StepBuffers, StepPlan, cold):
+    """One cell: forced rate `rate` (negative: the always-full baseline) at
+    context `ctx`.  The cache fill (standing in for prefill) is not timed.
+    Warm: W warm-up steps, graph capture, then the median of REPEATS replays of
+    K steps.  Cold (a fresh process): capture and the first K steps, timed
+    together on the host clock."""
+    dev = "cuda"
+    wl = matrix_workload(ctx, args.steps + args.warmup, synth)
+    L, B, Hq, Hkv, d, D = wl.layers, wl.batch, wl.hq, wl.hkv, wl.head_dim, wl.hidden
+    t0 = torch.from_numpy(wl.t0.astype(np.int32)).to(dev)
+    dims = C.make_dims(L, B, Hq, Hkv, t_cap=wl.t_cap, sink=wl.sink, window=wl.window)
+    K = torch.empty((L, B, Hkv, wl.t_cap, d), dtype=torch.int16, device=dev)
+    V = torch.empty_like(K)
+    sd.fill_cache(K, wl, synth.TAG_K, t0)
+    sd.fill_cache(V, wl, synth.TAG_V, t0)
+    kv = C.make_kv(K, V)
+    ws = torch.zeros(C.oda_workspace_bytes(dims), dtype=torch.uint8, device=dev)
+    C.oda_workspace_init(dims, ws)
+    h0 = torch.from_numpy(synth.h_prev0(wl).view(np.int16)).to(dev)
+    z = lambda *sh, dt=torch.int16: torch.zeros(sh, dtype=dt, device=dev)
+    bufs = StepBuffers(pos=t0.clone(), qL=z(L, B, Hq, d), kL=z(L, B, Hkv, d), vL=z(L, B, Hkv, d),
+                       qF=z(L, B, Hq, d), kF=z(L, B, Hkv, d), vF=z(L, B, Hkv, d), emb=z(B, D), h_prev=h0.clone(),
+                       head_w=torch.from_numpy(synth.head_blob(D, wl.head_seed)).to(dev), oL=z(L, B, Hq, d),
+                       oF=z(L, B, Hq, d), score=z(B, dt=torch.float32), flag=z(B, dt=torch.uint8),
+                       force=torch.full((B,), -1, dtype=torch.int8, device=dev))
+    plan = StepPlan(dims, kv, ws, bufs, theta=0.0, stream=stream)
+    feed = {"qL": bufs.qL, "qF": bufs.qF, "kL": bufs.kL, "vL": bufs.vL, "kF": bufs.kF, "vF": bufs.vF, "e": bufs.emb}
+    nsteps = args.steps + args.warmup
+    # per-step forced flags (exact count round(rate * steps)), looked up on the
+    # device from the step index pos - t0 so that one graph serves every step
+    table = torch.from_numpy(synth.forced_rate_flags(wl.seed, nsteps, B, max(rate, 0.0))).to(dev)
+    flag_all = torch.ones(B, dtype=torch.uint8, device=dev)
+    lib = plan._lib
+    dp = ctypes.byref(dims)
+    wsb = ws.numel()
+    commit_args = list(plan.commit_args)
+    commit_args[3] = flag_all.data_ptr()
+
+    def step():
+        sd.fill_step(feed, wl, bufs.pos, t0)
+        if rate < 0:   # always-full: every sequence takes the full branch, no local, no head
+            C.check(lib.oda_worklist(dp, flag_all.data_ptr(), bufs.pos.data_ptr(), ws.data_ptr(), wsb,
+                                     stream.cuda_stream), "oda_worklist")
+            plan.full()
+            C.check(lib.oda_commit(*commit_args), "oda_commit")
+        else:
+            j = (bufs.pos - t0).clamp_(0, nsteps - 1).long()
+            bufs.force.copy_(torch.index_select(table, 0, j).view(-1))
+            plan.run()
+
+    def reset():
+        bufs.pos.copy_(t0)
+        bufs.h_prev.copy_(h0)
+
+    torch.cuda.synchronize()
+    out = {"context": ctx, "rate": rate if rate >= 0 else "always-full", "steps": args.steps}
+    if cold:
+        # the torch ops of the flag lookup are plumbing: load their kernels first
+        torch.index_select(table, 0, (bufs.pos - t0).clamp(0, nsteps - 1).long())
+        reset()
+        torch.cuda.synchronize()
+        c0 = time.perf_counter()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            step()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - c0) * 1e3
+        out.update({"cold_ms_per_step": round(ms / args.steps, 4), "cold_steps_per_s": round(1e3 * args.steps / ms, 2)})
+    else:
+        reset()
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            step()
+        runs = []
+        for _ in range(args.repeats):
+            reset()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.steps):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            runs.append(e0.elapsed_time(e1))
+        ms = statistics.median(runs) / args.steps
+        out.update({"warm_ms_per_step": round(ms, 4), "warm_steps_per_s": round(1e3 / ms, 2)})
+    assert int(ws[:4].view(torch.int32).item()) == 0, "device error bits set"
+    return out
+
+
+def matrix(args):
+    """Parent of the matrix: warm cells in this process, each cold cell in a
+    fresh child process (started as a subprocess before this process touches
+    the GPU for that cell's timing)."""
+    import subprocess
+    import torch
+    import synth
+    import synth.device as sd
+    import conditional_sparse_attention_amd as C
+    from conditional_sparse_attention_amd.step import StepBuffers, StepPlan
+    ctxs = [int(x) for x in args.matrix_contexts.split(",") if x]
+    rates = [float(x) for x in args.matrix_rates.split(",") if x] + [-1.0]
+    cells = []
+    stream = torch.cuda.Stream()
+    for ctx in ctxs:
+        for r in rates:
+            with torch.cuda.stream(stream):
+                w = matrix_cell(ctx, r, args, stream, torch, synth, sd, C, StepBuffers, StepPlan, cold=False)
+            torch.cuda.empty_cache()
+            cmd = [sys.executable, os.path.abspath(__file__), "--matrix-cell", f"{ctx}:{r}", "--steps",
+                   str(args.steps), "--warmup", str(args.warmup)]
+            cp = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+            if cp.returncode != 0:
+                raise SystemExit(f"cold cell {ctx}:{r} failed ({cp.returncode}): {cp.stderr[-2000:]}")
+            c = json.loads(cp.stdout.strip().splitlines()[-1])
+            w.update({k: v for k, v in c.items() if k.startswith("cold")})
+            cells.append(w)
+            print(json.dumps(w), flush=True)
+    summary = {"matrix": "ODA decode steps/s at batch 1, 28 layers, 16/8 heads, d 128: context x forced rate",
+               "steps": args.steps, "warmup": args.warmup, "repeats": args.repeats, "cells": cells}
+    for ctx in ctxs:
+        base = [c for c in cells if c["context"] == ctx and c["rate"] == "always-full"][0]
+        for c in cells:
+            if c["context"] == ctx and c["rate"] != "always-full":
+                c["warm_speedup_vs_always_full"] = round(c["warm_steps_per_s"] / base["warm_steps_per_s"], 3)
+                c["cold_speedup_vs_always_full"] = round(c["cold_steps_per_s"] / base["cold_steps_per_s"], 3)
+    print(json.dumps(summary), flush=True)
 
 
 if __name__ == "__main__":

@@ -53,13 +53,10 @@ typedef __attribute__((address_space(1))) const v4u_t gv4_t;
 #ifndef ODA_FULL_DEPTH
 #define ODA_FULL_DEPTH 3
 #endif
-// The local set is small (at most sink + window keys per sequence and KV
-// head): 8 workgroups per pair already spread it over the chip, and each
-// further split lengthens the cross-workgroup merge more than it shortens the
-// streaming.
-#ifndef ODA_LOCAL_SPLITS
-#define ODA_LOCAL_SPLITS 8
-#endif
+// Workgroups per (sequence, KV head) in the local branch, between these
+// bounds (see local_splits()).
+constexpr int kLocalSplitsMin = 4;
+constexpr int kLocalSplitsMax = 8;
 #ifndef ODA_LOCAL_WAVES
 #define ODA_LOCAL_WAVES 4
 #endif
@@ -559,13 +556,13 @@ __global__ void __launch_bounds__(kLocalWaves * 64) k_attn_local(AttnParams P) {
   const LocalSet S = local_set(t, P.sink, P.window);
   const int n = S.size();
   int ns = (n + kLocalMinChunk - 1) / kLocalMinChunk;
-  ns = ns < ODA_LOCAL_SPLITS ? ns : ODA_LOCAL_SPLITS;
+  ns = ns < P.local_splits ? ns : P.local_splits;
   const int chunk = (n + ns - 1) / ns;
   if (split >= ns) return;
   const int v_lo = split * chunk;
   const int v_hi = (v_lo + chunk) < n ? v_lo + chunk : n;
   float* part_bg = P.part + ((size_t)(b * P.Hkv + g) * kLocalMaxSplits) * G * kPartStride;
-  attn_unit<G, PAGED, NW, ODA_LOCAL_DEPTH, ODA_LOCAL_U, ODA_LOCAL_SPLITS>(P, b, g, split, ns, v_lo, v_hi, S, P.tickets + b * P.Hkv + g, part_bg, lds);
+  attn_unit<G, PAGED, NW, ODA_LOCAL_DEPTH, ODA_LOCAL_U, kLocalSplitsMax>(P, b, g, split, ns, v_lo, v_hi, S, P.tickets + b * P.Hkv + g, part_bg, lds);
 }
 
 template <int G, bool PAGED>
@@ -601,15 +598,7 @@ __global__ void __launch_bounds__(FullWaves<G>::value * 64) k_attn_full(AttnPara
   }
 }
 
-template <int G, bool PAGED>
-int launch_local_t(const AttnParams& p, hipStream_t s) {
-  static_assert(ODA_LOCAL_SPLITS <= kLocalMaxSplits, "local splits exceed the workspace slots");
-  dim3 grid(ODA_LOCAL_SPLITS, p.Hkv, p.B);
-  hipLaunchKernelGGL((k_attn_local<G, PAGED>), grid, dim3(kLocalWaves * 64), 0, s, p);
-  return hipGetLastError() == hipSuccess ? ODA_OK : ODA_E_LAUNCH;
-}
-
-int full_grid(const AttnParams& p) {
+int device_cus() {
   static int cus[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -618,8 +607,34 @@ int full_grid(const AttnParams& p) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
     cus[dev] = n;
   }
+  return cus[dev];
+}
+
+// Workgroups per (sequence, KV head) in the local branch: about four per
+// compute unit over the whole batch, within [kLocalSplitsMin,
+// kLocalSplitsMax].  The local set is small (at most sink + window keys), so
+// past 8 splits the cross-workgroup merge costs more than the extra streaming
+// parallelism gains, and below 4 a workgroup streams too much alone.  At 8 KV
+// heads: 8 splits up to 16 sequences, 4 at 32.
+int local_splits(const AttnParams& p) {
+  const int pairs = p.B * p.Hkv;
+  const int ns = (4 * device_cus() + pairs - 1) / pairs;
+  return ns < kLocalSplitsMin ? kLocalSplitsMin : (ns > kLocalSplitsMax ? kLocalSplitsMax : ns);
+}
+
+template <int G, bool PAGED>
+int launch_local_t(const AttnParams& p_in, hipStream_t s) {
+  static_assert(kLocalSplitsMax <= kLocalMaxSplits, "local splits exceed the workspace slots");
+  AttnParams p = p_in;
+  p.local_splits = local_splits(p);
+  dim3 grid(p.local_splits, p.Hkv, p.B);
+  hipLaunchKernelGGL((k_attn_local<G, PAGED>), grid, dim3(kLocalWaves * 64), 0, s, p);
+  return hipGetLastError() == hipSuccess ? ODA_OK : ODA_E_LAUNCH;
+}
+
+int full_grid(const AttnParams& p) {
   const long units_max = (long)p.B * p.Hkv * kFullMaxSplits;
-  long grid = cus[dev];
+  const long grid = device_cus();
   return (int)(units_max < grid ? units_max : grid);
 }
 

@@ -101,6 +101,7 @@ struct AttnParams {
   int32_t B, Hq, Hkv, sink, window;
   int64_t t_max;
   float scale_log2;         // log2(e) / sqrt(d)
+  int32_t local_splits;     // local branch: workgroups per (sequence, KV head), set at launch
 };
 
 int launch_local_attn(const AttnParams& p, int G, bool paged, hipStream_t s);
