@@ -19,7 +19,7 @@
 // with no LDS and no barrier.  RMSNorm scales are folded in after the dot
 // product (W (gamma*x) / rms(x)), the sum of squares gathered in the same
 // pass; the interaction vector is formed on the fly from the tower outputs.
-#include "oda_internal.h"
+#include "head_internal.h"
 
 namespace oda {
 namespace {
@@ -351,8 +351,8 @@ __global__ void __launch_bounds__(64) k_worklist(const uint8_t* flag, const int3
 }
 
 // ------------------------------------------------ dense batches: fp32 MFMA
-// From about ten sequences on, the same layers are dense enough to run as
-// skinny GEMMs on the matrix cores: Y[n][col] = sum_k W[n][k] X[col][k] with
+// From five sequences on, the same layers run faster as skinny GEMMs on the
+// matrix cores: Y[n][col] = sum_k W[n][k] X[col][k] with
 // v_mfma_f32_16x16x4f32, A = 16 weight rows x 4 k, B = 4 k x 16 batch
 // columns.  In lane l = 16q + i the instruction takes A[i][q] and B[q][i] and
 // returns D[4q + r][i] in accumulator component r.

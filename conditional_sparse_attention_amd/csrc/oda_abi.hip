@@ -4,7 +4,7 @@
 #include <math.h>
 #include <string.h>
 
-#include "oda_internal.h"
+#include "head_internal.h"
 
 namespace oda {
 

@@ -30,10 +30,10 @@ struct WsLayout {
   size_t tick_local;   // int32[B * Hkv]
   size_t tick_full;    // int32[B * Hkv]
   size_t tick_commit;  // int32[B]
-  size_t tick_head;    // int32[kHeadTickets] (dense-batch head GEMM)
+  size_t tick_head;    // int32[kHeadTickets] (dense-batch head GEMM, head_internal.h)
   size_t part_local;   // float[B * Hkv * kLocalMaxSplits * G * kPartStride]
   size_t part_full;    // float[B * Hkv * kFullMaxSplits * G * kPartStride]
-  size_t head;         // float: see HeadWs
+  size_t head;         // float: head activations (HeadWs, head_internal.h)
   size_t total;
   int64_t t_max;            // capacity of one sequence in positions
 };
@@ -46,36 +46,6 @@ __device__ __host__ __forceinline__ int full_nsplit(int t) {
 
 bool dims_valid(const oda_dims* d, int* status);
 WsLayout ws_layout(const oda_dims* d);
-
-// head activation sub-regions (float offsets inside WsLayout::head)
-constexpr int kHeadTickets = 256;
-constexpr int kHeadDenseMin = 9;  // batches from here on take the dense (MFMA) head path
-struct HeadWs {
-  float* towers;  // [3][B][T]  (a, b, c)
-  float* u0;      // [B][T]
-  float* hdn;     // [B][F]
-  float* u1;      // [B][T]
-  float* u2;      // [B][T]
-  float* part;    // split-K partial tiles of the dense path (B >= kHeadDenseMin)
-};
-// floats of split-K partial tiles the dense head GEMMs need (largest layer)
-size_t dense_head_part_floats(int B, int D);
-inline size_t head_ws_floats(int B, int D) {
-  size_t n = (size_t)B * (3 * kTower + kTower + kFfn + 2 * kTower);
-  if (B >= kHeadDenseMin) n += dense_head_part_floats(B, D);
-  return n;
-}
-inline HeadWs head_ws(void* ws, const WsLayout& L, int B, int D) {
-  float* base = reinterpret_cast<float*>(static_cast<char*>(ws) + L.head);
-  HeadWs h;
-  h.towers = base;
-  h.u0 = h.towers + 3 * B * kTower;
-  h.hdn = h.u0 + B * kTower;
-  h.u1 = h.hdn + B * kFfn;
-  h.u2 = h.u1 + B * kTower;
-  h.part = h.u2 + B * kTower;
-  return h;
-}
 
 // ---------------------------------------------------------------------------
 // attention launch parameters
@@ -106,29 +76,6 @@ struct AttnParams {
 
 int launch_local_attn(const AttnParams& p, int G, bool paged, hipStream_t s);
 int launch_full_attn(const AttnParams& p, int G, bool paged, hipStream_t s);
-
-// ---------------------------------------------------------------------------
-// recall head launch parameters
-// ---------------------------------------------------------------------------
-struct HeadParams {
-  const float* w;          // packed blob
-  const int64_t* offs;     // unused on device; host-side offsets
-  const uint16_t* h_prev;
-  const uint16_t* emb;
-  const uint16_t* h_local;
-  float theta;
-  const int8_t* force;
-  const int32_t* pos;
-  float* score;
-  uint8_t* flag;
-  int32_t* worklist;
-  int32_t* tickets;   // kHeadTickets, zero between calls
-  int32_t B, D;
-  HeadWs act;
-};
-int launch_recall_head(const HeadParams& p, const int64_t* offs, hipStream_t s);
-int launch_recall_head_dense(const HeadParams& p, const int64_t* offs, hipStream_t s);
-int launch_worklist(const uint8_t* flag, const int32_t* pos, int32_t* worklist, int B, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // commit / ranges / init
@@ -181,17 +128,6 @@ __device__ __forceinline__ float row16_sum(float x) {
   x += dpp_mov<0x141>(x);  // row_half_mirror
   x += dpp_mov<0x140>(x);  // row_mirror
   return x;
-}
-
-// Sum over the 64 lanes of a wave, identical (wave-uniform) in every lane:
-// row sums by DPP, then the four row results read out and added in fixed order.
-__device__ __forceinline__ float wave_sum64(float x) {
-  x = row16_sum(x);
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
-  return (r0 + r1) + (r2 + r3);
 }
 
 // Local index set S^L of a sequence whose current 0-based position is t-1:

@@ -171,10 +171,10 @@ def test_worklist_entry_point_bitexact():
         assert got == full_worklist(flags, nsplit)
 
 
-@pytest.mark.parametrize("B,hq", [(1, 16), (8, 16), (9, 8), (16, 32), (17, 16), (32, 8), (32, 32), (24, 16)])
+@pytest.mark.parametrize("B,hq", [(1, 16), (4, 16), (5, 8), (8, 16), (9, 8), (16, 32), (17, 16), (32, 8), (32, 32), (24, 16)])
 def test_recall_head_batch_sizes(B, hq):
     """oda_recall_score alone, on both sides of the switch from the
-    bandwidth-shaped GEMV (up to 8 sequences) to the fp32 MFMA GEMMs (9 and
+    bandwidth-shaped GEMV (up to 4 sequences) to the fp32 MFMA GEMMs (5 and
     up: one 16-wide column group through 16, two from 17), at D = 1024, 2048
     and 4096, with a perturbed head so every bias and gain term counts.
     Scores to 1e-4 (1 + |q|); flags bit-exact outside the tie band; the work
