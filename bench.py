@@ -6,24 +6,25 @@ Workload (default): Qwen3-1.7B-shaped attention stack -- 28 layers, 16 query
 cache per sequence (60 GB), three planted far needles, random Xavier fp32
 recall head, threshold tuned so that 12.5% of (sequence, step) decisions
 take the full branch.  All inputs are synthetic (seeded generator G, filled
-on the device); the time excludes that fill.
+on the device) and resident in HBM before any timing: the cache, and every
+step's q / k / v of both branches and embedding.
 
 One step = local attention of all 28 layers, recall score + rule + work
-list, conditional full attention of all 28 layers, commit, plus the feed
-kernel that writes the step's synthetic q/k/v/embedding.
+list, conditional full attention of all 28 layers, commit.
 
 Protocol: a calibration pass with theta = +inf (all local) records the
 head's scores and sets theta to the midpoint between the k-th and (k+1)-th
 largest, k = round(0.125 * B * steps); the state is reset; W warm-up steps.
-The timed region is K steps replayed from one captured HIP graph (the step
-has no host synchronisation, so it is one graph), run REPEATS times from the
-same start state; the median is the reported warm throughput.  The same K
-steps are then launched one call at a time, the L back-to-back
-full-attention launches of each step bracketed by a pair of HIP events on
-their stream: that gives the dominant kernel's average launch duration and, from the recorded flags and positions, its
-algorithmic bytes per launch, t_b * 4096 B (K and V of every key of every
-flagged sequence, including the staged current token).  Both passes run the
-same kernels on the same inputs, so they follow the same trajectory.
+Each step is captured into its own HIP graph, bound to that step's inputs.
+The timed region replays the K graphs in order from one start state, REPEATS
+times; the median is the reported warm throughput.  The same K steps are
+then replayed as three graphs each (local + score | the L full-attention
+launches | commit), the middle one bracketed by a pair of HIP events on its
+stream: that gives the dominant kernel's average launch duration and, from
+the recorded flags and positions, its algorithmic bytes per launch, t_b *
+4096 B (K and V of every key of every flagged sequence, including the staged
+current token).  Both passes run the same kernels on the same inputs, so
+they follow the same trajectory.
 
 Prints one JSON line.
 """
@@ -31,6 +32,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import dataclasses
 import json
 import math
 import os
@@ -76,79 +78,185 @@ def main():
         return matrix(args)
     import torch
     import synth
-    import synth.device as sd
-    import conditional_sparse_attention_amd as C
-    from conditional_sparse_attention_amd.step import StepBuffers, StepPlan
 
     if args.matrix_cell:
         ctx, rate = args.matrix_cell.split(":")
         stream = torch.cuda.Stream()
         with torch.cuda.stream(stream):
-            print(json.dumps(matrix_cell(int(ctx), float(rate), args, stream, torch, synth, sd, C, StepBuffers,
-                                         StepPlan, cold=True)), flush=True)
+            print(json.dumps(matrix_cell(int(ctx), float(rate), args, stream, torch, cold=True)), flush=True)
         return
 
     wl_key = int(args.workload) if args.workload.isdigit() else args.workload
     wl = synth.workloads()[wl_key]
     if wl.bernoulli_odd is not None:
         raise SystemExit("the bench runs head-decided schedules; this workload forces per-step flags")
-    total_steps_needed = args.steps + max(args.warmup, 0)
-    if args.steps > wl.steps + wl.t_cap_slack:
+    if max(args.steps, args.warmup) > wl.steps + wl.t_cap_slack:
         raise SystemExit("too many steps for the cache capacity")
-    dev = "cuda"
-    stream = torch.cuda.Stream()  # a non-default stream, so the step can also be graph-captured
+    stream = torch.cuda.Stream()  # a non-default stream, so the steps can be graph-captured
     with torch.cuda.stream(stream):
-        run(args, wl, stream, torch, synth, sd, C, StepBuffers, StepPlan, dev)
+        run(args, wl, stream, torch)
 
 
-def run(args, wl, stream, torch, synth, sd, C, StepBuffers, StepPlan, dev):
+class Session:
+    """Device state of one workload: the cache, the workspace, every step's
+    synthetic inputs (written into HBM here, before any timing) and one
+    StepPlan per step bound to that step's inputs.  ``force_table`` (host
+    [steps][B] int8) bakes per-step forced flags into the plans."""
+
+    def __init__(self, wl, nsteps, stream, theta, force_table=None):
+        import torch
+        import synth
+        import synth.device as sd
+        import conditional_sparse_attention_amd as C
+        from conditional_sparse_attention_amd.step import StepBuffers, StepPlan
+        self.torch, self.C, self.wl, self.nsteps, self.stream = torch, C, wl, nsteps, stream
+        dev = "cuda"
+        L, B, Hq, Hkv, d, D = wl.layers, wl.batch, wl.hq, wl.hkv, wl.head_dim, wl.hidden
+        self.t0 = torch.from_numpy(wl.t0.astype(np.int32)).to(dev)
+        if wl.layout == "paged":
+            tables_np, nblocks = synth.paged_block_tables(wl)
+            tables = torch.from_numpy(tables_np).to(dev)
+            self.dims = C.make_dims(L, B, Hq, Hkv, kv_layout=C.ODA_KV_PAGED, block_size=wl.block_size,
+                                    max_blocks_per_seq=tables_np.shape[1], num_blocks=nblocks, sink=wl.sink,
+                                    window=wl.window)
+            self.K = torch.empty((L, nblocks, Hkv, wl.block_size, d), dtype=torch.int16, device=dev)
+        else:
+            tables, nblocks = None, 0
+            self.dims = C.make_dims(L, B, Hq, Hkv, t_cap=wl.t_cap, sink=wl.sink, window=wl.window)
+            self.K = torch.empty((L, B, Hkv, wl.t_cap, d), dtype=torch.int16, device=dev)
+        self.V = torch.empty_like(self.K)
+        sd.fill_cache(self.K, wl, synth.TAG_K, self.t0, tables=tables, num_blocks=nblocks)
+        sd.fill_cache(self.V, wl, synth.TAG_V, self.t0, tables=tables, num_blocks=nblocks)
+        self.tables = tables
+        self.kv = C.make_kv(self.K, self.V, tables)
+        self.ws = torch.zeros(C.oda_workspace_bytes(self.dims), dtype=torch.uint8, device=dev)
+        C.oda_workspace_init(self.dims, self.ws)
+        self.blob = synth.head_blob(D, wl.head_seed)
+        self.h0 = torch.from_numpy(synth.h_prev0(wl).view(np.int16)).to(dev)
+        z = lambda *sh, dt=torch.int16: torch.zeros(sh, dtype=dt, device=dev)
+        # every step's inputs: [step][L][B][H][d] and [step][B][D]
+        self.inp = {"qL": z(nsteps, L, B, Hq, d), "qF": z(nsteps, L, B, Hq, d), "kL": z(nsteps, L, B, Hkv, d),
+                    "vL": z(nsteps, L, B, Hkv, d), "kF": z(nsteps, L, B, Hkv, d), "vF": z(nsteps, L, B, Hkv, d),
+                    "e": z(nsteps, B, D)}
+        pos_j = self.t0.clone()
+        for j in range(nsteps):
+            pos_j.copy_(self.t0 + j)
+            sd.fill_step({k: v[j] for k, v in self.inp.items()}, wl, pos_j, self.t0)
+        self.force_dev = None if force_table is None else torch.from_numpy(np.asarray(force_table, np.int8)).to(dev)
+        self.state = StepBuffers(pos=self.t0.clone(), qL=None, kL=None, vL=None, qF=None, kF=None, vF=None, emb=None,
+                                 h_prev=self.h0.clone(), head_w=torch.from_numpy(self.blob).to(dev),
+                                 oL=z(L, B, Hq, d), oF=z(L, B, Hq, d), score=z(B, dt=torch.float32),
+                                 flag=z(B, dt=torch.uint8), force=torch.full((B,), -1, dtype=torch.int8, device=dev))
+        self.plans = []
+        for j in range(nsteps):
+            b = dataclasses.replace(self.state, qL=self.inp["qL"][j], kL=self.inp["kL"][j], vL=self.inp["vL"][j],
+                                    qF=self.inp["qF"][j], kF=self.inp["kF"][j], vF=self.inp["vF"][j],
+                                    emb=self.inp["e"][j],
+                                    force=self.state.force if self.force_dev is None else self.force_dev[j])
+            self.plans.append(StepPlan(self.dims, self.kv, self.ws, b, theta=theta, stream=stream))
+        self.flag_all = torch.ones(B, dtype=torch.uint8, device=dev)
+        # one plan on fixed step buffers, for a single graph that serves every
+        # step: the step's inputs (and forced flags) are copied into the
+        # buffers on the device, selected by pos - t0
+        self.buf = {k: torch.zeros_like(v[0]) for k, v in self.inp.items()}
+        fb = dataclasses.replace(self.state, qL=self.buf["qL"], kL=self.buf["kL"], vL=self.buf["vL"],
+                                 qF=self.buf["qF"], kF=self.buf["kF"], vF=self.buf["vF"], emb=self.buf["e"])
+        self.fixed_plan = StepPlan(self.dims, self.kv, self.ws, fb, theta=theta, stream=stream)
+        torch.cuda.synchronize()
+
+    def feed_fixed(self):
+        """Copy the current step's inputs (and forced flags) from the resident
+        per-step table into the fixed step buffers (device-side selection)."""
+        torch = self.torch
+        j = (self.state.pos[:1] - self.t0[:1]).clamp(0, self.nsteps - 1).long()
+        for k, v in self.inp.items():
+            torch.index_select(v, 0, j, out=self.buf[k].unsqueeze(0))
+        if self.force_dev is not None:
+            torch.index_select(self.force_dev, 0, j, out=self.state.force.unsqueeze(0))
+
+    def fixed_step(self, always_full=False):
+        self.feed_fixed()
+        if always_full:
+            p = self.fixed_plan
+            dp = ctypes.byref(self.dims)
+            self.C.check(p._lib.oda_worklist(dp, self.flag_all.data_ptr(), self.state.pos.data_ptr(),
+                                             self.ws.data_ptr(), self.ws.numel(), self.stream.cuda_stream),
+                         "oda_worklist")
+            p.full()
+            a = list(p.commit_args)
+            a[3] = self.flag_all.data_ptr()
+            self.C.check(p._lib.oda_commit(*a), "oda_commit")
+        else:
+            self.fixed_plan.run()
+
+    def reset(self):
+        self.state.pos.copy_(self.t0)
+        self.state.h_prev.copy_(self.h0)
+
+    def set_theta(self, theta):
+        for p in self.plans + [self.fixed_plan]:
+            p.set_theta(theta)
+
+    def always_full_step(self, j):
+        """The always-full baseline's step j: every sequence takes the full
+        branch; no local attention and no recall head."""
+        p = self.plans[j]
+        C = self.C
+        dp = ctypes.byref(self.dims)
+        C.check(p._lib.oda_worklist(dp, self.flag_all.data_ptr(), self.state.pos.data_ptr(), self.ws.data_ptr(),
+                                    self.ws.numel(), self.stream.cuda_stream), "oda_worklist")
+        p.full()
+        a = list(p.commit_args)
+        a[3] = self.flag_all.data_ptr()
+        C.check(p._lib.oda_commit(*a), "oda_commit")
+
+    def capture(self, fn, count):
+        """One HIP graph per step j < count, each capturing fn(j)."""
+        torch = self.torch
+        graphs = []
+        for j in range(count):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=self.stream):
+                fn(j)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        return graphs
+
+    def time_graphs(self, graphs, repeats):
+        """Median over repeats of the time to replay the graphs in order from
+        the start state (ms)."""
+        torch = self.torch
+        runs = []
+        for _ in range(repeats):
+            self.reset()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(self.stream)
+            for g in graphs:
+                g.replay()
+            e1.record(self.stream)
+            torch.cuda.synchronize()
+            runs.append(e0.elapsed_time(e1))
+        return statistics.median(runs)
+
+    def error_bits(self):
+        return int(self.ws[:4].view(self.torch.int32).item())
+
+
+def run(args, wl, stream, torch):
     L, B, Hq, Hkv, d, D = wl.layers, wl.batch, wl.hq, wl.hkv, wl.head_dim, wl.hidden
     t_setup = time.time()
-    t0 = torch.from_numpy(wl.t0.astype(np.int32)).to(dev)
-    if wl.layout == "paged":
-        tables_np, nblocks = synth.paged_block_tables(wl)
-        tables = torch.from_numpy(tables_np).to(dev)
-        dims = C.make_dims(L, B, Hq, Hkv, kv_layout=C.ODA_KV_PAGED, block_size=wl.block_size,
-                           max_blocks_per_seq=tables_np.shape[1], num_blocks=nblocks, sink=wl.sink, window=wl.window)
-        K = torch.empty((L, nblocks, Hkv, wl.block_size, d), dtype=torch.int16, device=dev)
-    else:
-        tables, nblocks = None, 0
-        dims = C.make_dims(L, B, Hq, Hkv, t_cap=wl.t_cap, sink=wl.sink, window=wl.window)
-        K = torch.empty((L, B, Hkv, wl.t_cap, d), dtype=torch.int16, device=dev)
-    V = torch.empty_like(K)
-    sd.fill_cache(K, wl, synth.TAG_K, t0, tables=tables, num_blocks=nblocks)
-    sd.fill_cache(V, wl, synth.TAG_V, t0, tables=tables, num_blocks=nblocks)
-    kv = C.make_kv(K, V, tables)
-    ws = torch.zeros(C.oda_workspace_bytes(dims), dtype=torch.uint8, device=dev)
-    C.oda_workspace_init(dims, ws)
-    blob = synth.head_blob(D, wl.head_seed)
-    h0 = torch.from_numpy(synth.h_prev0(wl).view(np.int16)).to(dev)
-    z = lambda *s, dt=torch.int16: torch.zeros(s, dtype=dt, device=dev)
-    bufs = StepBuffers(pos=t0.clone(), qL=z(L, B, Hq, d), kL=z(L, B, Hkv, d), vL=z(L, B, Hkv, d),
-                       qF=z(L, B, Hq, d), kF=z(L, B, Hkv, d), vF=z(L, B, Hkv, d), emb=z(B, D), h_prev=h0.clone(),
-                       head_w=torch.from_numpy(blob).to(dev), oL=z(L, B, Hq, d), oF=z(L, B, Hq, d),
-                       score=z(B, dt=torch.float32), flag=z(B, dt=torch.uint8),
-                       force=torch.full((B,), -1, dtype=torch.int8, device=dev))
-    plan = StepPlan(dims, kv, ws, bufs, theta=math.inf, stream=stream)
-    feed = {"qL": bufs.qL, "qF": bufs.qF, "kL": bufs.kL, "vL": bufs.vL, "kF": bufs.kF, "vF": bufs.vF, "e": bufs.emb}
-
-    def reset():
-        bufs.pos.copy_(t0)
-        bufs.h_prev.copy_(h0)
-
-    def step():
-        sd.fill_step(feed, wl, bufs.pos, t0)
-        plan.run()
-
-    torch.cuda.synchronize()
+    nsteps = max(args.steps, args.warmup, 1)
+    S = Session(wl, nsteps, stream, theta=math.inf)
     setup_s = time.time() - t_setup
+    K = args.steps
 
     # ---- calibration: all-local scores -> theta for the target rate
-    reset()
-    scores = torch.zeros((args.steps, B), dtype=torch.float32, device=dev)
-    for j in range(args.steps):
-        step()
-        scores[j].copy_(bufs.score)
+    S.reset()
+    scores = torch.zeros((K, B), dtype=torch.float32, device="cuda")
+    for j in range(K):
+        S.plans[j].run()
+        scores[j].copy_(S.state.score)
     torch.cuda.synchronize()
     sc = np.sort(scores.cpu().numpy().reshape(-1))[::-1]
     rate = wl.rate
@@ -157,113 +265,97 @@ def run(args, wl, stream, torch, synth, sd, C, StepBuffers, StepPlan, dev):
         theta = float((sc[k - 1] + sc[k]) / 2) if 0 < k < sc.size else (math.inf if k == 0 else -math.inf)
     else:
         theta = float(wl.theta)
-    plan.set_theta(theta)
+    S.set_theta(theta)
 
     # ---- warm-up
-    reset()
-    for _ in range(args.warmup):
-        step()
+    S.reset()
+    for j in range(args.warmup):
+        S.plans[j].run()
     torch.cuda.synchronize()
 
-    # ---- timed region: K steps replayed from one captured HIP graph, from the
+    # ---- timed region: the K per-step graphs replayed in order from the
     # same start state, REPEATS times; the median is the reported throughput
-    reset()
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        step()
-    torch.cuda.synchronize()
-    run_ms = []
-    for rep in range(args.repeats):
-        reset()
-        torch.cuda.synchronize()
-        t_start = torch.cuda.Event(enable_timing=True)
-        t_end = torch.cuda.Event(enable_timing=True)
-        t_start.record(stream)
-        for j in range(args.steps):
-            graph.replay()
-        t_end.record(stream)
-        torch.cuda.synchronize()
-        run_ms.append(t_start.elapsed_time(t_end))
+    graphs = S.capture(lambda j: S.plans[j].run(), K)
+    ms_total = S.time_graphs(graphs, args.repeats)
+    del graphs
 
-    # ---- the same K steps replayed as three graphs per step (feed + local +
-    # score | the L full-attention launches | commit), with a pair of HIP
-    # events on the stream around the middle graph: the dominant kernel's
-    # average launch duration, free of host launch gaps; the recorded flags
-    # and positions fix its algorithmic bytes
-    reset()
-    torch.cuda.synchronize()
-    g_pre, g_full, g_post = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_pre, stream=stream):
-        sd.fill_step(feed, wl, bufs.pos, t0)
-        plan.local()
-        plan.score()
-    with torch.cuda.graph(g_full, stream=stream):
-        plan.full()
-    with torch.cuda.graph(g_post, stream=stream):
-        plan.commit()
-    flags_hist = torch.zeros((args.steps, B), dtype=torch.uint8, device=dev)
-    pos_hist = torch.zeros((args.steps, B), dtype=torch.int32, device=dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    reset()
+    # ---- the same K steps as three graphs per step (local + score | the L
+    # full-attention launches | commit), a pair of HIP events on the stream
+    # around the middle one: the dominant kernel's average launch duration,
+    # free of host launch gaps; the recorded flags and positions fix its
+    # algorithmic bytes
+    def pre(j):
+        S.plans[j].local()
+        S.plans[j].score()
+    g_pre = S.capture(pre, K)
+    g_full = S.capture(lambda j: S.plans[j].full(), K)
+    g_post = S.capture(lambda j: S.plans[j].commit(), K)
+    flags_hist = torch.zeros((K, B), dtype=torch.uint8, device="cuda")
+    pos_hist = torch.zeros((K, B), dtype=torch.int32, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    S.reset()
     torch.cuda.synchronize()
     e_start = torch.cuda.Event(enable_timing=True)
     e_end = torch.cuda.Event(enable_timing=True)
     e_start.record(stream)
-    for j in range(args.steps):
-        pos_hist[j].copy_(bufs.pos)
-        g_pre.replay()
+    for j in range(K):
+        pos_hist[j].copy_(S.state.pos)
+        g_pre[j].replay()
         e0, e1 = ev[j]
         e0.record(stream)
-        g_full.replay()
+        g_full[j].replay()
         e1.record(stream)
-        g_post.replay()
-        flags_hist[j].copy_(bufs.flag)
+        g_post[j].replay()
+        flags_hist[j].copy_(S.state.flag)
     e_end.record(stream)
     torch.cuda.synchronize()
     split_ms = e_start.elapsed_time(e_end)
     full_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev)
+    del g_pre, g_full, g_post
     fl = flags_hist.cpu().numpy().astype(np.int64)
     ps = pos_hist.cpu().numpy().astype(np.int64)
     full_bytes = float(np.sum(fl * (ps + 1))) * Hkv * d * 2 * 2 * L
-    assert int(ws[:4].view(torch.int32).item()) == 0, "device error bits set"
+    assert S.error_bits() == 0, "device error bits set"
 
-    ms_total = statistics.median(run_ms)
-    ms_step = ms_total / args.steps
+    ms_step = ms_total / K
     steps_per_s = 1000.0 / ms_step
     realised = float(fl.mean())
     kv_local = 0
     for b in range(B):
-        for j in range(args.steps):
+        for j in range(K):
             t = int(wl.t0[b]) + j + 1
             kv_local += min(t, wl.sink + wl.window)
-    kv_bytes_step = (kv_local + float(np.sum(fl * (ps + 1)))) * Hkv * d * 2 * 2 * L / args.steps
+    kv_bytes_step = (kv_local + float(np.sum(fl * (ps + 1)))) * Hkv * d * 2 * 2 * L / K
     always_full = None
     if args.always_full:
-        always_full = always_full_leg(args, wl, dims, kv, ws, bufs, plan, feed, sd, t0, reset, stream, torch, C)
+        g_af = S.capture(S.always_full_step, K)
+        m = S.time_graphs(g_af, args.repeats) / K
+        del g_af
+        always_full = {"steps_per_s": round(1000.0 / m, 2), "ms_per_step": round(m, 4)}
     out = {
         "metric": "ODA decode steps/s + KV HBM GB/s (% peak) at 128K ctx, 12.5% recall, 1 GPU",
         "value": round(steps_per_s, 2),
         "unit": "steps/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded generator, device-filled; random-init Xavier recall head)",
+        "data": "synthetic (seeded generator, inputs device-generated into HBM before timing; random-init Xavier "
+                "recall head)",
         "config": {"workload": wl.name, "layers": L, "batch": B, "context": int(wl.t0[0]) if np.all(wl.t0 == wl.t0[0])
                    else f"ragged mean {float(np.mean(wl.t0)):.0f}", "q_heads": Hq,
                    "kv_heads": Hkv, "head_dim": d, "kv_layout": wl.layout, "recall_rate_target": rate,
                    "recall_rate_realised": realised, "theta": theta, "tokens_per_s": round(steps_per_s * B, 1),
-                   "repeats": args.repeats, "timing": "hip-graph replay, median of repeats",
-                   "split_graph_steps_per_s": round(1000.0 * args.steps / split_ms, 2)},
+                   "repeats": args.repeats, "timing": "per-step hip-graph replay, median of repeats",
+                   "split_graph_steps_per_s": round(1000.0 * K / split_ms, 2)},
         "kv_gbs": round(kv_bytes_step / (ms_step * 1e-3) / 1e9, 1),
         "kv_frac_peak": round(kv_bytes_step / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
     }
-    nlaunch = args.steps * L
+    nlaunch = K * L
     avg_us = full_ms * 1e3 / nlaunch
     bytes_per_launch = full_bytes / nlaunch
     achieved = bytes_per_launch / (avg_us * 1e-6) / 1e9
@@ -277,16 +369,16 @@ def run(args, wl, stream, torch, synth, sd, C, StepBuffers, StepPlan, dev):
         out["always_full"]["oda_speedup"] = round(steps_per_s / always_full["steps_per_s"], 3)
     out["setup_s"] = round(setup_s, 1)
     if args.rate_sweep:
-        out["rate_sweep"] = rate_sweep(args, wl, plan, bufs, step, reset, torch)
+        out["rate_sweep"] = rate_sweep(args, S)
     if args.copy_calibration:
-        src = torch.empty(1 << 29, dtype=torch.int16, device=dev)
+        src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = 2 * src.numel() * src.element_size()
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, blob, theta, realised)
+        out["cpu_baseline"] = cpu_baseline(wl, S.blob, theta, realised)
     print(json.dumps(out), flush=True)
 
 
@@ -321,60 +413,29 @@ def measured_traffic(bytes_per_launch):
     return int(ratio * bytes_per_launch), f"PMC ratio {ratio:.5f} of algorithmic bytes ({os.path.basename(TRAFFIC_FILE)})"
 
 
-def always_full_leg(args, wl, dims, kv, ws, bufs, plan, feed, sd, t0, reset, stream, torch, C):
-    """K steps of the always-full baseline from the same start state, one graph
-    per step, median of the repeats."""
-    flag_all = torch.ones(wl.batch, dtype=torch.uint8, device="cuda")
-    lib = plan._lib
-    dp = ctypes.byref(dims)
-    wsb = ws.numel() * ws.element_size()
-    s = stream.cuda_stream
-    commit_args = list(plan.commit_args)
-    commit_args[3] = flag_all.data_ptr()
-    reset()
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        sd.fill_step(feed, wl, bufs.pos, t0)
-        C.check(lib.oda_worklist(dp, flag_all.data_ptr(), bufs.pos.data_ptr(), ws.data_ptr(), wsb, s), "oda_worklist")
-        plan.full()
-        C.check(lib.oda_commit(*commit_args), "oda_commit")
-    torch.cuda.synchronize()
-    ms = []
-    for _ in range(args.repeats):
-        reset()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.steps):
-            g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms.append(e0.elapsed_time(e1))
-    m = statistics.median(ms) / args.steps
-    return {"steps_per_s": round(1000.0 / m, 2), "ms_per_step": round(m, 4)}
-
-
-def rate_sweep(args, wl, plan, bufs, step, reset, torch):
+def rate_sweep(args, S):
     """Step time at forced full-branch rates (exact counts placed by seeded
-    uniforms), to show step time scaling with the recall rate."""
+    uniforms), to show step time scaling with the recall rate.  Eager
+    launches; the state's force buffer is set before each step."""
     import synth
+    torch = S.torch
+    wl = S.wl
     res = []
-    saved = bufs.force.clone()
+    saved = S.state.force.clone()
     for r in [float(x) for x in args.rate_sweep.split(",") if x]:
         flags = synth.forced_rate_flags(wl.seed, args.steps, wl.batch, r)
         fdev = torch.from_numpy(flags).to("cuda")
-        reset()
+        S.reset()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+        e0.record(S.stream)
         for j in range(args.steps):
-            bufs.force.copy_(fdev[j])
-            step()
-        e1.record()
+            S.state.force.copy_(fdev[j])
+            S.plans[j].run()
+        e1.record(S.stream)
         torch.cuda.synchronize()
         res.append({"rate": r, "ms_per_step": round(e0.elapsed_time(e1) / args.steps, 4)})
-    bufs.force.copy_(saved)
+    S.state.force.copy_(saved)
     x = np.array([q["rate"] for q in res])
     y = np.array([q["ms_per_step"] for q in res])
     if len(res) >= 2:
@@ -451,67 +512,28 @@ def matrix_workload(ctx, steps, synth):
                           np.array([ctx], dtype=np.int64), steps, seed=3, head_seed=103, t_cap_slack=16)
 
 
-def matrix_cell(ctx, rate, args, stream, torch, synth, sd, C, StepBuffers, StepPlan, cold):
+def matrix_cell(ctx, rate, args, stream, torch, cold):
     """One cell: forced rate `rate` (negative: the always-full baseline) at
-    context `ctx`.  The cache fill (standing in for prefill) is not timed.
-    Warm: W warm-up steps, graph capture, then the median of REPEATS replays of
-    K steps.  Cold (a fresh process): capture and the first K steps, timed
-    together on the host clock."""
-    dev = "cuda"
+    context `ctx`.  The cache and every step's inputs are written into HBM
+    before the clock starts (the cache fill stands in for prefill).  A single
+    graph serves every step, as a serving engine's would: each step first
+    copies its inputs from the resident table into fixed buffers (device
+    side, ~0.3 MB at batch 1).  Warm: W warm-up steps, capture, then the median
+    of REPEATS replays of K steps.  Cold (a fresh process): capture and the
+    first K steps, timed together on the host clock."""
+    import synth
     wl = matrix_workload(ctx, args.steps + args.warmup, synth)
-    L, B, Hq, Hkv, d, D = wl.layers, wl.batch, wl.hq, wl.hkv, wl.head_dim, wl.hidden
-    t0 = torch.from_numpy(wl.t0.astype(np.int32)).to(dev)
-    dims = C.make_dims(L, B, Hq, Hkv, t_cap=wl.t_cap, sink=wl.sink, window=wl.window)
-    K = torch.empty((L, B, Hkv, wl.t_cap, d), dtype=torch.int16, device=dev)
-    V = torch.empty_like(K)
-    sd.fill_cache(K, wl, synth.TAG_K, t0)
-    sd.fill_cache(V, wl, synth.TAG_V, t0)
-    kv = C.make_kv(K, V)
-    ws = torch.zeros(C.oda_workspace_bytes(dims), dtype=torch.uint8, device=dev)
-    C.oda_workspace_init(dims, ws)
-    h0 = torch.from_numpy(synth.h_prev0(wl).view(np.int16)).to(dev)
-    z = lambda *sh, dt=torch.int16: torch.zeros(sh, dtype=dt, device=dev)
-    bufs = StepBuffers(pos=t0.clone(), qL=z(L, B, Hq, d), kL=z(L, B, Hkv, d), vL=z(L, B, Hkv, d),
-                       qF=z(L, B, Hq, d), kF=z(L, B, Hkv, d), vF=z(L, B, Hkv, d), emb=z(B, D), h_prev=h0.clone(),
-                       head_w=torch.from_numpy(synth.head_blob(D, wl.head_seed)).to(dev), oL=z(L, B, Hq, d),
-                       oF=z(L, B, Hq, d), score=z(B, dt=torch.float32), flag=z(B, dt=torch.uint8),
-                       force=torch.full((B,), -1, dtype=torch.int8, device=dev))
-    plan = StepPlan(dims, kv, ws, bufs, theta=0.0, stream=stream)
-    feed = {"qL": bufs.qL, "qF": bufs.qF, "kL": bufs.kL, "vL": bufs.vL, "kF": bufs.kF, "vF": bufs.vF, "e": bufs.emb}
-    nsteps = args.steps + args.warmup
-    # per-step forced flags (exact count round(rate * steps)), looked up on the
-    # device from the step index pos - t0 so that one graph serves every step
-    table = torch.from_numpy(synth.forced_rate_flags(wl.seed, nsteps, B, max(rate, 0.0))).to(dev)
-    flag_all = torch.ones(B, dtype=torch.uint8, device=dev)
-    lib = plan._lib
-    dp = ctypes.byref(dims)
-    wsb = ws.numel()
-    commit_args = list(plan.commit_args)
-    commit_args[3] = flag_all.data_ptr()
-
-    def step():
-        sd.fill_step(feed, wl, bufs.pos, t0)
-        if rate < 0:   # always-full: every sequence takes the full branch, no local, no head
-            C.check(lib.oda_worklist(dp, flag_all.data_ptr(), bufs.pos.data_ptr(), ws.data_ptr(), wsb,
-                                     stream.cuda_stream), "oda_worklist")
-            plan.full()
-            C.check(lib.oda_commit(*commit_args), "oda_commit")
-        else:
-            j = (bufs.pos - t0).clamp_(0, nsteps - 1).long()
-            bufs.force.copy_(torch.index_select(table, 0, j).view(-1))
-            plan.run()
-
-    def reset():
-        bufs.pos.copy_(t0)
-        bufs.h_prev.copy_(h0)
-
-    torch.cuda.synchronize()
+    nsteps = max(args.steps, args.warmup, 1)
+    # exact count round(rate * steps) of forced full calls
+    table = synth.forced_rate_flags(wl.seed, nsteps, wl.batch, max(rate, 0.0))
+    S = Session(wl, nsteps, stream, theta=0.0, force_table=table)
+    # the plumbing ops of the input selection load their kernels outside the clock
+    S.feed_fixed()
+    step = lambda: S.fixed_step(always_full=rate < 0)
     out = {"context": ctx, "rate": rate if rate >= 0 else "always-full", "steps": args.steps}
+    S.reset()
+    torch.cuda.synchronize()
     if cold:
-        # the torch ops of the flag lookup are plumbing: load their kernels first
-        torch.index_select(table, 0, (bufs.pos - t0).clamp(0, nsteps - 1).long())
-        reset()
-        torch.cuda.synchronize()
         c0 = time.perf_counter()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
@@ -522,27 +544,15 @@ def matrix_cell(ctx, rate, args, stream, torch, synth, sd, C, StepBuffers, StepP
         ms = (time.perf_counter() - c0) * 1e3
         out.update({"cold_ms_per_step": round(ms / args.steps, 4), "cold_steps_per_s": round(1e3 * args.steps / ms, 2)})
     else:
-        reset()
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             step()
-        runs = []
-        for _ in range(args.repeats):
-            reset()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(args.steps):
-                g.replay()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            runs.append(e0.elapsed_time(e1))
-        ms = statistics.median(runs) / args.steps
+        ms = S.time_graphs([g] * args.steps, args.repeats) / args.steps
         out.update({"warm_ms_per_step": round(ms, 4), "warm_steps_per_s": round(1e3 / ms, 2)})
-    assert int(ws[:4].view(torch.int32).item()) == 0, "device error bits set"
+    assert S.error_bits() == 0, "device error bits set"
     return out
 
 
@@ -552,10 +562,6 @@ def matrix(args):
     the GPU for that cell's timing)."""
     import subprocess
     import torch
-    import synth
-    import synth.device as sd
-    import conditional_sparse_attention_amd as C
-    from conditional_sparse_attention_amd.step import StepBuffers, StepPlan
     ctxs = [int(x) for x in args.matrix_contexts.split(",") if x]
     rates = [float(x) for x in args.matrix_rates.split(",") if x] + [-1.0]
     cells = []
@@ -563,7 +569,7 @@ def matrix(args):
     for ctx in ctxs:
         for r in rates:
             with torch.cuda.stream(stream):
-                w = matrix_cell(ctx, r, args, stream, torch, synth, sd, C, StepBuffers, StepPlan, cold=False)
+                w = matrix_cell(ctx, r, args, stream, torch, cold=False)
             torch.cuda.empty_cache()
             cmd = [sys.executable, os.path.abspath(__file__), "--matrix-cell", f"{ctx}:{r}", "--steps",
                    str(args.steps), "--warmup", str(args.warmup)]
