@@ -4,3 +4,4 @@ Only tests/, __graft_entry__.smoke() and the cpu_baseline leg of bench.py may
 import this package.  The product path never does.
 """
 from .oda_oracle import *  # noqa: F401,F403
+from . import oda_decoder_oracle as decoder  # noqa: F401

@@ -162,9 +162,46 @@ __global__ void k_fill_step(StepFill F) {
   }
 }
 
+// Decoder matrices (synth/gen.py dec_matrix_bits): element e of tensor T is
+// bf16(((m - 2^21) + 0.5) * s) with m the top 22 bits of the hash of the
+// logical index (T << 40) + e; one thread per 8 elements.
+__global__ void k_fill_dec(uint16_t* dst, int64_t n, uint64_t key, uint64_t base, uint32_t scale_bits) {
+  const float s = __uint_as_float(scale_bits);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * 8;
+  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8; i < n; i += stride) {
+    uint32_t out[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint16_t v2[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint64_t h = splitmix64(key + base + (uint64_t)(i + 2 * k + e));
+        const int m = (int)(h >> 42) - (1 << 21);
+        v2[e] = bf16_rne(__fmul_rn(__fadd_rn((float)m, 0.5f), s));
+      }
+      out[k] = (uint32_t)v2[0] | ((uint32_t)v2[1] << 16);
+    }
+    *reinterpret_cast<uint4*>(dst + i) = make_uint4(out[0], out[1], out[2], out[3]);
+  }
+}
+
 }  // namespace
 
 extern "C" {
+
+// n elements of decoder matrix `tensor_id` (n a multiple of 8, dst 16-B aligned).
+int synth_fill_dec_matrix(uint16_t* dst, int64_t n, uint64_t seed, uint64_t tensor_id, uint32_t scale_bits,
+                          hipStream_t stream) {
+  if (dst == nullptr || n < 0 || n % 8 != 0 || (reinterpret_cast<uintptr_t>(dst) & 15) != 0) return -1;
+  if (n == 0) return 0;
+  const int64_t threads = n / 8;
+  int64_t blocks = (threads + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(k_fill_dec, dim3((unsigned)blocks), dim3(256), 0, stream, dst, n, stream_key(seed, 16),
+                     tensor_id << 40, scale_bits);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
 
 // Fills layers [layer0, layer0 + L) of a KV cache (tag 1 = K with needles,
 // tag 2 = V).  Contiguous: dst [L][B][Hkv][t_cap][d]; paged: dst

@@ -45,6 +45,8 @@ def lib() -> ctypes.CDLL:
                                        i32, ctypes.POINTER(ctypes.c_int32), vp]
         L.synth_fill_step.restype = ctypes.c_int
         L.synth_fill_step.argtypes = [vp] * 7 + [u64, i32, i32, i32, i32, i32, vp, vp, i32, vp]
+        L.synth_fill_dec_matrix.restype = ctypes.c_int
+        L.synth_fill_dec_matrix.argtypes = [vp, i64, u64, u64, ctypes.c_uint32, vp]
         _lib = L
     return _lib
 
@@ -76,3 +78,32 @@ def fill_step(bufs: dict, wl: "gen.Workload", pos_dev, t0_dev) -> None:
                                t0_dev.data_ptr(), len(wl.needles), _stream())
     if rc != 0:
         raise RuntimeError(f"synth_fill_step failed: {rc}")
+
+
+def fill_dec_matrix(dst, seed: int, tensor_id: int) -> None:
+    """Decoder matrix `tensor_id` (gen.dec_matrix_bits) into the contiguous
+    device tensor `dst` (int16 storage), element order = flat order."""
+    scale_bits = int(np.asarray(gen.DEC_SCALE, dtype=np.float32).view(np.uint32))
+    rc = lib().synth_fill_dec_matrix(dst.data_ptr(), dst.numel(), seed, tensor_id, scale_bits, _stream())
+    if rc != 0:
+        raise RuntimeError(f"synth_fill_dec_matrix failed: {rc}")
+
+
+def fill_dec_layer(blob, seed: int, shape: "gen.DecoderShape", layer: int, perturb: bool = False) -> None:
+    """One layer's blob (gen.dec_layer_blob) on the device: matrices from the
+    device generator, norm gains from the host generator."""
+    import torch
+    at = 0
+    for name, sh in gen.dec_layer_tensors(shape):
+        n = int(np.prod(sh))
+        part = blob[at:at + n]
+        if name.startswith("gamma"):
+            part.copy_(torch.from_numpy(gen.dec_gain_bits(seed, layer, name, n, perturb).view(np.int16)))
+        else:
+            fill_dec_matrix(part, seed, gen.dec_tensor_id(layer, name))
+        at += n
+
+
+def fill_dec_embed(table, seed: int) -> None:
+    """The token-embedding table [V][D] (gen.dec_embed_bits) on the device."""
+    fill_dec_matrix(table, seed, gen.DEC_EMBED_ID)

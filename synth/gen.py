@@ -54,6 +54,9 @@ TAG_HEAD = 12                  # recall-head weights
 TAG_LEN = 13                   # ragged context lengths
 TAG_BERN = 14                  # Bernoulli forced flags
 TAG_SHUF = 15                  # paged block shuffle
+TAG_DEC_W = 16                 # decoder weight matrices and the token-embedding table
+TAG_DEC_G = 17                 # decoder norm gains (perturbed variants)
+TAG_TOK = 18                   # first tokens of the decoder workloads
 
 MAX_B = 32          # logical batch stride of the index space
 POS_BITS = 18       # logical position stride 2**18
@@ -376,3 +379,97 @@ def head_blob(hidden: int, seed: int, perturb: bool = False, tower: int = 1024,
             blob[at:at + n] = (1.0 + (2.0 * uu - 1.0) * 0.1).astype(np.float32) if perturb else 1.0
         at += n
     return blob
+
+
+# --------------------------------------------------------------------------
+# decoder backbone around the path (random-init, Qwen3-1.7B-shaped)
+# --------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class DecoderShape:
+    """Shape of a dense decoder whose attention is the ODA path: pre-RMSNorm
+    attention with QK-norm and RoPE, then a pre-RMSNorm SwiGLU MLP, a final
+    RMSNorm and an LM head tied to the token embedding."""
+    name: str
+    hidden: int
+    layers: int
+    hq: int
+    hkv: int
+    head_dim: int
+    inter: int
+    vocab: int
+    rope_theta: float = 1.0e6
+    eps: float = 1e-6
+
+
+def decoder_shapes() -> dict:
+    return {
+        "qwen3-1.7b": DecoderShape("qwen3-1.7b", 2048, 28, 16, 8, 128, 6144, 151936),
+        "tiny": DecoderShape("tiny", 1024, 2, 8, 4, 128, 2048, 4096),
+    }
+
+
+# Matrices are uniform on (-a, a) with a = 0.02 * sqrt(3) (standard deviation
+# 0.02), drawn on a 2^22-level grid so that host and device compute the same
+# bits with one float32 multiply: value = bf16(((m - 2^21) + 0.5) * s), m the
+# top 22 bits of the 64-bit hash of the logical index, s = float32(a / 2^21).
+DEC_INIT_STD = 0.02
+DEC_SCALE = np.float32(DEC_INIT_STD * math.sqrt(3.0) / 2.0 ** 21)
+DEC_TENSOR_BITS = 40            # logical index = (tensor id << 40) + element
+DEC_EMBED_ID = 1 << 20          # tensor id of the token-embedding table
+DEC_MATRICES = ("W_qkv", "W_o", "W_gate", "W_up", "W_down")
+
+
+def dec_tensor_id(layer: int, name: str) -> int:
+    return layer * 8 + DEC_MATRICES.index(name)
+
+
+def dec_matrix_bits(seed: int, tensor_id: int, elems) -> np.ndarray:
+    """bf16 bits of elements `elems` of decoder matrix `tensor_id`."""
+    idx = (np.uint64(tensor_id) << np.uint64(DEC_TENSOR_BITS)) + np.asarray(elems, dtype=_U64)
+    h = hash_at(seed, TAG_DEC_W, idx)
+    m = (h >> _U64(42)).astype(np.int64) - (1 << 21)
+    x = m.astype(np.float32) + np.float32(0.5)
+    return f32_to_bf16_rne(x * DEC_SCALE)
+
+
+def dec_layer_tensors(shape: DecoderShape) -> Sequence[Tuple[str, tuple]]:
+    """(name, shape) of one layer's tensors in blob order (bf16 each)."""
+    D, d, I = shape.hidden, shape.head_dim, shape.inter
+    nqkv = (shape.hq + 2 * shape.hkv) * d
+    return [("gamma_in", (D,)), ("W_qkv", (nqkv, D)), ("gamma_q", (d,)), ("gamma_k", (d,)),
+            ("W_o", (D, shape.hq * d)), ("gamma_post", (D,)), ("W_gate", (I, D)), ("W_up", (I, D)),
+            ("W_down", (D, I))]
+
+
+def dec_gain_bits(seed: int, layer: int, name: str, n: int, perturb: bool) -> np.ndarray:
+    """Norm gains: 1, or 1 + U(-0.1, 0.1) when perturbed (host only)."""
+    if not perturb:
+        return np.full(n, 0x3F80, dtype=np.uint16)
+    tid = {"gamma_in": 0, "gamma_q": 1, "gamma_k": 2, "gamma_post": 3, "gamma_final": 4}[name]
+    u = uniform_at(seed, TAG_DEC_G, (np.uint64(layer * 8 + tid) << np.uint64(DEC_TENSOR_BITS)) +
+                   np.arange(n, dtype=_U64))
+    return f32_to_bf16_rne((1.0 + (2.0 * u - 1.0) * 0.1).astype(np.float32))
+
+
+def dec_layer_blob(seed: int, shape: DecoderShape, layer: int, perturb: bool = False) -> np.ndarray:
+    """One layer's bf16 blob (host; small shapes)."""
+    parts = []
+    for name, sh in dec_layer_tensors(shape):
+        n = int(np.prod(sh))
+        if name.startswith("gamma"):
+            parts.append(dec_gain_bits(seed, layer, name, n, perturb))
+        else:
+            parts.append(dec_matrix_bits(seed, dec_tensor_id(layer, name), np.arange(n)))
+    return np.concatenate(parts)
+
+
+def dec_embed_bits(seed: int, shape: DecoderShape, rows) -> np.ndarray:
+    """Rows of the token-embedding table [V][D] (also the tied LM head)."""
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1)
+    D = shape.hidden
+    el = (rows[:, None] * D + np.arange(D)[None, :]).astype(_U64)
+    return dec_matrix_bits(seed, DEC_EMBED_ID, el).reshape(len(rows), D)
+
+
+def dec_first_tokens(seed: int, batch: int, vocab: int) -> np.ndarray:
+    return (hash_at(seed, TAG_TOK, np.arange(batch)) % _U64(vocab)).astype(np.int32)
