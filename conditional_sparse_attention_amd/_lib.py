@@ -1,4 +1,4 @@
-"""ctypes binding of liboda (include/oda.h).
+"""ctypes binding of liboda (include/oda.h, include/oda_decoder.h).
 
 Argument marshalling only: every function takes torch tensors (or None for a
 nullable pointer), passes their device pointers and the current HIP stream
@@ -19,7 +19,9 @@ LIB_PATH = os.path.join(_HERE, "liboda.so")
 ODA_OK = 0
 ODA_E_NULL, ODA_E_DIMS, ODA_E_UNSUPPORTED, ODA_E_WORKSPACE, ODA_E_LAYER, ODA_E_LAUNCH = -1, -2, -3, -4, -5, -6
 ODA_KV_CONTIG, ODA_KV_PAGED = 0, 1
-ODA_ERR_CAPACITY, ODA_ERR_BLOCK = 1, 2
+ODA_ERR_CAPACITY, ODA_ERR_BLOCK, ODA_ERR_TOKEN = 1, 2, 4
+ODA_DEC_LOCAL, ODA_DEC_FULL = 0, 1
+ODA_DEC_NTENSORS = 9
 ODA_HEAD_NTENSORS = 22
 ODA_FULL_MIN_CHUNK = 1024
 ODA_FULL_MAX_SPLITS = 32
@@ -28,6 +30,8 @@ EXPORTED = (
     "oda_abi_version", "oda_status_str", "oda_head_param_count", "oda_head_offsets",
     "oda_workspace_bytes", "oda_workspace_worklist_offset", "oda_workspace_init",
     "oda_local_ranges", "oda_local_attn", "oda_recall_score", "oda_worklist", "oda_full_attn_if", "oda_commit",
+    "oda_dec_layer_numel", "oda_dec_layer_offsets", "oda_dec_workspace_bytes", "oda_dec_workspace_init",
+    "oda_dec_embed", "oda_dec_layer", "oda_dec_final_norm", "oda_dec_next_token",
 )
 
 
@@ -53,6 +57,11 @@ class oda_kv(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("block_tables", ctypes.c_void_p)]
 
 
+class oda_dec_dims(ctypes.Structure):
+    _fields_ = [("attn", oda_dims), ("inter", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("rope_theta", ctypes.c_float), ("eps", ctypes.c_float)]
+
+
 _lib = None
 
 
@@ -65,7 +74,7 @@ def lib() -> ctypes.CDLL:
                               "`python -m conditional_sparse_attention_amd.build` (no fallback exists)")
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
-        dp, kp = ctypes.POINTER(oda_dims), ctypes.POINTER(oda_kv)
+        dp, kp, ddp = ctypes.POINTER(oda_dims), ctypes.POINTER(oda_kv), ctypes.POINTER(oda_dec_dims)
         sig = {
             "oda_abi_version": (ctypes.c_int, []),
             "oda_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -80,6 +89,14 @@ def lib() -> ctypes.CDLL:
             "oda_worklist": (ctypes.c_int, [dp, vp, vp, vp, sz, vp]),
             "oda_full_attn_if": (ctypes.c_int, [dp, i32, kp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "oda_commit": (ctypes.c_int, [dp, kp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "oda_dec_layer_numel": (i64, [ddp]),
+            "oda_dec_layer_offsets": (ctypes.c_int, [ddp, ctypes.POINTER(i64)]),
+            "oda_dec_workspace_bytes": (sz, [ddp]),
+            "oda_dec_workspace_init": (ctypes.c_int, [ddp, vp, sz, vp]),
+            "oda_dec_embed": (ctypes.c_int, [ddp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "oda_dec_layer": (ctypes.c_int, [ddp, i32, i32, vp, kp, vp, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]),
+            "oda_dec_final_norm": (ctypes.c_int, [ddp, i32, vp, vp, vp, vp, sz, vp]),
+            "oda_dec_next_token": (ctypes.c_int, [ddp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -199,3 +216,56 @@ def oda_commit(dims, kv: oda_kv, pos, flag, k_cur_L, v_cur_L, k_cur_F, v_cur_F, 
     check(lib().oda_commit(ctypes.byref(dims), ctypes.byref(kv), _p(pos), _p(flag), _p(k_cur_L), _p(v_cur_L),
                             _p(k_cur_F), _p(v_cur_F), _p(out_last_L), _p(out_last_F), _p(h_prev), _p(ws),
                             _bytes(ws), _s(stream)), "oda_commit")
+
+
+# ---------------------------------------------------------------------------
+# decoder backbone around the path (include/oda_decoder.h)
+# ---------------------------------------------------------------------------
+def make_dec_dims(attn: oda_dims, inter: int, vocab: int, rope_theta: float = 1.0e6,
+                  eps: float = 1e-6) -> oda_dec_dims:
+    return oda_dec_dims(attn, inter, vocab, rope_theta, eps)
+
+
+def oda_dec_layer_numel(dd: oda_dec_dims) -> int:
+    n = int(lib().oda_dec_layer_numel(ctypes.byref(dd)))
+    if n < 0:
+        raise OdaError(ODA_E_DIMS, "oda_dec_layer_numel")
+    return n
+
+
+def oda_dec_layer_offsets(dd: oda_dec_dims):
+    arr = (ctypes.c_int64 * (ODA_DEC_NTENSORS + 1))()
+    check(lib().oda_dec_layer_offsets(ctypes.byref(dd), arr), "oda_dec_layer_offsets")
+    return list(arr)
+
+
+def oda_dec_workspace_bytes(dd: oda_dec_dims) -> int:
+    n = int(lib().oda_dec_workspace_bytes(ctypes.byref(dd)))
+    if n == 0:
+        raise OdaError(ODA_E_DIMS, "oda_dec_workspace_bytes")
+    return n
+
+
+def oda_dec_workspace_init(dd, dws, stream=None) -> None:
+    check(lib().oda_dec_workspace_init(ctypes.byref(dd), _p(dws), _bytes(dws), _s(stream)), "oda_dec_workspace_init")
+
+
+def oda_dec_embed(dd, embed, tokens, x_local, x_full, emb, ws=None, stream=None) -> None:
+    check(lib().oda_dec_embed(ctypes.byref(dd), _p(embed), _p(tokens), _p(x_local), _p(x_full), _p(emb), _p(ws),
+                              _bytes(ws) if ws is not None else 0, _s(stream)), "oda_dec_embed")
+
+
+def oda_dec_layer(dd, layer, branch, w_layer, kv: oda_kv, pos, x, q, k_cur, v_cur, o, ws, dws, stream=None) -> None:
+    check(lib().oda_dec_layer(ctypes.byref(dd), layer, branch, _p(w_layer), ctypes.byref(kv), _p(pos), _p(x), _p(q),
+                              _p(k_cur), _p(v_cur), _p(o), _p(ws), _bytes(ws), _p(dws), _bytes(dws), _s(stream)),
+          "oda_dec_layer")
+
+
+def oda_dec_final_norm(dd, branch, gamma_f, x, h, ws=None, stream=None) -> None:
+    check(lib().oda_dec_final_norm(ctypes.byref(dd), branch, _p(gamma_f), _p(x), _p(h), _p(ws),
+                                   _bytes(ws) if ws is not None else 0, _s(stream)), "oda_dec_final_norm")
+
+
+def oda_dec_next_token(dd, embed, h_local, h_full, flag, tokens, max_logit, dws, stream=None) -> None:
+    check(lib().oda_dec_next_token(ctypes.byref(dd), _p(embed), _p(h_local), _p(h_full), _p(flag), _p(tokens),
+                                   _p(max_logit), _p(dws), _bytes(dws), _s(stream)), "oda_dec_next_token")

@@ -78,6 +78,7 @@ extern "C" {
 #define ODA_WS_ERROR_WORD 0
 #define ODA_ERR_CAPACITY 1   /* pos[b] + 1 exceeds the sequence's capacity */
 #define ODA_ERR_BLOCK 2      /* a block-table entry is outside [0, num_blocks) */
+#define ODA_ERR_TOKEN 4      /* a decoder token id is outside [0, vocab) (oda_decoder.h) */
 
 /* recall head geometry [ODA notes §2.2]: three 1024-wide towers, a
  * 9*1024-wide interaction, two gated FFN blocks of hidden width 2048 */

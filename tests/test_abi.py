@@ -1,4 +1,4 @@
-"""The C-ABI library loads, exports every symbol include/oda.h declares,
+"""The C-ABI library loads, exports every symbol include/*.h declares,
 answers host-only queries, and rejects bad arguments before launching
 anything (these calls return before any device work, so they run on CPU)."""
 import ctypes
@@ -13,9 +13,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def declared_functions():
-    src = open(os.path.join(ROOT, "include", "oda.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(oda_[a-z_]+)\s*\(", src)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", h)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(oda_[a-z_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_header_declares_the_binding_names():
@@ -81,3 +85,40 @@ def test_entry_points_reject_bad_arguments_without_launching():
     assert lib.oda_workspace_init(dp, None, ws_bytes, None) == C.ODA_E_NULL
     assert lib.oda_local_ranges(None, fake, fake, None) == C.ODA_E_NULL
     assert C.status_str(C.ODA_E_WORKSPACE).startswith("workspace")
+
+
+def test_decoder_layout_agrees_with_oracle_and_generator():
+    """The library's layer blob offsets, the oracle's own layout statement
+    and the generator's tensor list describe the same blob."""
+    import numpy as np
+    import synth
+    from oracle import decoder as D
+    for key in ("qwen3-1.7b", "tiny"):
+        sh = synth.decoder_shapes()[key]
+        dd = C.make_dec_dims(C.make_dims(sh.layers, 4, sh.hq, sh.hkv, t_cap=8192), sh.inter, sh.vocab,
+                             sh.rope_theta, sh.eps)
+        offs = C.oda_dec_layer_offsets(dd)
+        lay = D.layer_layout(sh.hidden, sh.hq, sh.hkv, sh.head_dim, sh.inter)
+        sizes = [int(np.prod(s)) for _, s in lay]
+        assert offs == [0] + list(np.cumsum(sizes))
+        assert C.oda_dec_layer_numel(dd) == D.layer_param_count(sh.hidden, sh.hq, sh.hkv, sh.head_dim, sh.inter)
+        assert [n for n, _ in synth.dec_layer_tensors(sh)] == [n for n, _ in lay]
+
+
+def test_decoder_rejects_bad_arguments_before_launching():
+    import synth
+    sh = synth.decoder_shapes()["tiny"]
+    ok = C.make_dims(sh.layers, 4, sh.hq, sh.hkv, t_cap=8192)
+    assert C.oda_dec_workspace_bytes(C.make_dec_dims(ok, sh.inter, sh.vocab)) > 0
+    for inter, vocab in ((1000, sh.vocab), (sh.inter, 4000), (0, sh.vocab)):
+        with pytest.raises(C.OdaError):
+            C.oda_dec_workspace_bytes(C.make_dec_dims(ok, inter, vocab))
+    dd = C.make_dec_dims(ok, sh.inter, sh.vocab)
+    lib = C.lib()
+    assert lib.oda_dec_layer(ctypes.byref(dd), 0, 2, None, None, None, None, None, None, None, None, None, 0, None,
+                             0, None) == C.ODA_E_DIMS
+    assert lib.oda_dec_layer(ctypes.byref(dd), 5, 0, None, None, None, None, None, None, None, None, None, 0, None,
+                             0, None) == C.ODA_E_LAYER
+    assert lib.oda_dec_layer(ctypes.byref(dd), 0, 0, None, None, None, None, None, None, None, None, None, 0, None,
+                             0, None) == C.ODA_E_NULL
+    assert lib.oda_dec_next_token(ctypes.byref(dd), None, None, None, None, None, None, None, 0, None) == C.ODA_E_NULL
