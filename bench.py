@@ -65,6 +65,12 @@ def parse():
     ap.add_argument("--matrix-contexts", default="4096,16384,32768,65536,131072")
     ap.add_argument("--matrix-rates", default="0,0.125,0.25,0.5,1")
     ap.add_argument("--matrix-cell", default="", help=argparse.SUPPRESS)  # child process: CONTEXT:RATE, cold run
+    ap.add_argument("--decoder", action="store_true",
+                    help="the step with the dense Qwen3-1.7B-shaped decoder around the path (random-init bf16 "
+                         "weights): the workload's batch and context, theta tuned to its rate, against always-full")
+    ap.add_argument("--decoder-matrix", action="store_true",
+                    help="decoder step at batch 1: context x forced recall-rate matrix, warm and first-request")
+    ap.add_argument("--decoder-cell", default="", help=argparse.SUPPRESS)  # child process: CONTEXT:RATE, cold run
     return ap.parse_args()
 
 
@@ -76,6 +82,8 @@ def main():
         sys.exit(2)
     if args.matrix:
         return matrix(args)
+    if args.decoder_matrix:
+        return decoder_matrix(args)
     import torch
     import synth
 
@@ -86,8 +94,20 @@ def main():
             print(json.dumps(matrix_cell(int(ctx), float(rate), args, stream, torch, cold=True)), flush=True)
         return
 
+    if args.decoder_cell:
+        ctx, rate = args.decoder_cell.split(":")
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            print(json.dumps(decoder_cell(int(ctx), float(rate), args, stream, torch, cold=True)), flush=True)
+        return
+
     wl_key = int(args.workload) if args.workload.isdigit() else args.workload
     wl = synth.workloads()[wl_key]
+    if args.decoder:
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            decoder_bench(args, wl, stream, torch)
+        return
     if wl.bernoulli_odd is not None:
         raise SystemExit("the bench runs head-decided schedules; this workload forces per-step flags")
     if max(args.steps, args.warmup) > wl.steps + wl.t_cap_slack:
@@ -589,6 +609,209 @@ def matrix(args):
                 c["warm_speedup_vs_always_full"] = round(c["warm_steps_per_s"] / base["warm_steps_per_s"], 3)
                 c["cold_speedup_vs_always_full"] = round(c["cold_steps_per_s"] / base["cold_steps_per_s"], 3)
     print(json.dumps(summary), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# the step with the dense decoder backbone around the path
+# ---------------------------------------------------------------------------
+DECODER_SHAPE = "qwen3-1.7b"
+
+
+class DecSession:
+    """Device state of a decoder workload: cache, decoder and head weights
+    (device-generated, random init), workspaces and the step plan.  Every
+    input of a step is device resident: the token comes from the previous
+    step's argmax, so one captured graph serves every step.  `force_table`
+    (host [steps][B] int8) forces per-step flags, looked up on the device from
+    pos - t0."""
+
+    def __init__(self, t0, nsteps, stream, theta, force_table=None, seed=3):
+        import torch
+        import synth
+        import synth.device as sd
+        import conditional_sparse_attention_amd as C
+        from conditional_sparse_attention_amd.decoder import DecoderBuffers, DecoderPlan, DecoderWeights
+        self.torch, self.C, self.stream, self.nsteps = torch, C, stream, nsteps
+        sh = synth.decoder_shapes()[DECODER_SHAPE]
+        self.sh = sh
+        t0 = np.asarray(t0, dtype=np.int64)
+        B = len(t0)
+        wl = synth.Workload(f"decoder-{sh.name}", sh.layers, sh.hq, sh.hkv, sh.head_dim, B, t0, nsteps, seed=seed,
+                            head_seed=seed + 100, t_cap_slack=16)
+        self.wl = wl
+        dev = "cuda"
+        L, Dm = sh.layers, sh.hidden
+        self.attn = C.make_dims(L, B, sh.hq, sh.hkv, t_cap=wl.t_cap, sink=wl.sink, window=wl.window)
+        self.dd = C.make_dec_dims(self.attn, sh.inter, sh.vocab, sh.rope_theta, sh.eps)
+        self.t0 = torch.from_numpy(t0.astype(np.int32)).to(dev)
+        self.K = torch.empty((L, B, sh.hkv, wl.t_cap, sh.head_dim), dtype=torch.int16, device=dev)
+        self.V = torch.empty_like(self.K)
+        sd.fill_cache(self.K, wl, synth.TAG_K, self.t0)
+        sd.fill_cache(self.V, wl, synth.TAG_V, self.t0)
+        self.kv = C.make_kv(self.K, self.V)
+        layers = torch.empty((L, C.oda_dec_layer_numel(self.dd)), dtype=torch.int16, device=dev)
+        for l in range(L):
+            sd.fill_dec_layer(layers[l], seed, sh, l)
+        embed = torch.empty((sh.vocab, Dm), dtype=torch.int16, device=dev)
+        sd.fill_dec_embed(embed, seed)
+        gamma_f = torch.from_numpy(synth.dec_gain_bits(seed, L, "gamma_final", Dm, False).view(np.int16)).to(dev)
+        self.weights = DecoderWeights(layers, embed, gamma_f)
+        self.blob = synth.head_blob(Dm, wl.head_seed)
+        self.tok0 = torch.from_numpy(synth.dec_first_tokens(seed, B, sh.vocab)).to(dev)
+        self.h0 = torch.from_numpy(synth.h_prev0(wl).view(np.int16)).to(dev)
+        self.bufs = DecoderBuffers.allocate(self.dd, torch.from_numpy(self.blob).to(dev), self.tok0.clone(),
+                                            self.t0.clone(), self.h0.clone())
+        self.ws = torch.zeros(C.oda_workspace_bytes(self.attn), dtype=torch.uint8, device=dev)
+        C.oda_workspace_init(self.attn, self.ws)
+        self.dws = torch.zeros(C.oda_dec_workspace_bytes(self.dd), dtype=torch.uint8, device=dev)
+        C.oda_dec_workspace_init(self.dd, self.dws)
+        self.plan = DecoderPlan(self.dd, self.kv, self.weights, self.bufs, self.ws, self.dws, theta=theta,
+                                stream=stream)
+        self.force_dev = None if force_table is None else torch.from_numpy(np.asarray(force_table, np.int8)).to(dev)
+        self.flag_all = torch.ones(B, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    def reset(self):
+        self.bufs.pos.copy_(self.t0)
+        self.bufs.h_prev.copy_(self.h0)
+        self.bufs.tokens.copy_(self.tok0)
+
+    def step(self, always_full=False):
+        torch = self.torch
+        if always_full:
+            self.plan.run_always_full(self.flag_all)
+            return
+        if self.force_dev is not None:
+            j = (self.bufs.pos[:1] - self.t0[:1]).clamp(0, self.nsteps - 1).long()
+            torch.index_select(self.force_dev, 0, j, out=self.bufs.force.unsqueeze(0))
+        self.plan.run()
+
+    def warm_ms(self, steps, warmup, repeats, always_full=False):
+        """Median ms per step over repeats of `steps` graph replays."""
+        torch = self.torch
+        self.reset()
+        for _ in range(warmup):
+            self.step(always_full)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=self.stream):
+            self.step(always_full)
+        runs = []
+        for _ in range(repeats):
+            self.reset()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(self.stream)
+            for _ in range(steps):
+                g.replay()
+            e1.record(self.stream)
+            torch.cuda.synchronize()
+            runs.append(e0.elapsed_time(e1))
+        assert int(self.ws[:4].view(torch.int32).item()) == 0, "device error bits set"
+        return statistics.median(runs) / steps
+
+
+def decoder_bench(args, wl, stream, torch):
+    """The workload's batch and contexts with the decoder backbone: theta
+    tuned on an all-local pass to the workload's rate, then warm graph
+    replay, against the always-full baseline."""
+    K = args.steps
+    S = DecSession(wl.t0, max(K, args.warmup, 1), stream, theta=math.inf)
+    S.reset()
+    scores = torch.zeros((K, wl.batch), dtype=torch.float32, device="cuda")
+    for j in range(K):
+        S.step()
+        scores[j].copy_(S.bufs.score)
+    torch.cuda.synchronize()
+    sc = np.sort(scores.cpu().numpy().reshape(-1))[::-1]
+    rate = wl.rate if wl.rate is not None else 0.0
+    k = int(round(rate * sc.size))
+    theta = float((sc[k - 1] + sc[k]) / 2) if 0 < k < sc.size else (math.inf if k == 0 else -math.inf)
+    S.plan.set_theta(theta)
+    # realised rate on an eager pass with this theta
+    S.reset()
+    flags = torch.zeros((K, wl.batch), dtype=torch.uint8, device="cuda")
+    for j in range(K):
+        S.step()
+        flags[j].copy_(S.bufs.flag)
+    torch.cuda.synchronize()
+    realised = float(flags.float().mean().item())
+    ms = S.warm_ms(K, args.warmup, args.repeats)
+    ms_af = S.warm_ms(K, args.warmup, args.repeats, always_full=True)
+    sh = S.sh
+    print(json.dumps({
+        "metric": "ODA decode steps/s with the dense decoder backbone around the path",
+        "value": round(1e3 / ms, 2), "unit": "steps/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic (seeded generator; random-init bf16 decoder weights and fp32 recall head)",
+        "config": {"workload": f"{wl.name} + {sh.name} decoder", "layers": sh.layers, "batch": wl.batch,
+                   "context": int(wl.t0[0]), "hidden": sh.hidden, "mlp": sh.inter, "vocab": sh.vocab,
+                   "recall_rate_target": rate, "recall_rate_realised": realised, "theta": theta,
+                   "tokens_per_s": round(1e3 / ms * wl.batch, 1), "timing": "hip-graph replay, median of repeats"},
+        "always_full": {"steps_per_s": round(1e3 / ms_af, 2), "ms_per_step": round(ms_af, 4),
+                        "oda_speedup": round(ms_af / ms, 3)},
+    }), flush=True)
+
+
+def decoder_cell(ctx, rate, args, stream, torch, cold):
+    """Batch 1, context `ctx`, forced rate `rate` (negative: always-full)."""
+    import synth
+    nsteps = max(args.steps, args.warmup, 1)
+    table = synth.forced_rate_flags(3, nsteps, 1, max(rate, 0.0))
+    S = DecSession([ctx], nsteps, stream, theta=0.0, force_table=table)
+    af = rate < 0
+    out = {"context": ctx, "rate": rate if rate >= 0 else "always-full", "steps": args.steps}
+    if cold:
+        torch.index_select(S.force_dev, 0, (S.bufs.pos[:1] - S.t0[:1]).long(), out=S.bufs.force.unsqueeze(0))
+        S.reset()
+        torch.cuda.synchronize()
+        c0 = time.perf_counter()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            S.step(af)
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - c0) * 1e3 / args.steps
+        out.update({"cold_ms_per_step": round(ms, 4), "cold_tokens_per_s": round(1e3 / ms, 2)})
+    else:
+        ms = S.warm_ms(args.steps, args.warmup, args.repeats, always_full=af)
+        out.update({"warm_ms_per_step": round(ms, 4), "warm_tokens_per_s": round(1e3 / ms, 2)})
+    return out
+
+
+def decoder_matrix(args):
+    """Batch-1 decoder steps over contexts x forced rates plus always-full,
+    warm in this process, first-request in a fresh child per cell."""
+    import subprocess
+    import torch
+    ctxs = [int(x) for x in args.matrix_contexts.split(",") if x]
+    rates = [float(x) for x in args.matrix_rates.split(",") if x] + [-1.0]
+    cells = []
+    stream = torch.cuda.Stream()
+    for ctx in ctxs:
+        for r in rates:
+            with torch.cuda.stream(stream):
+                w = decoder_cell(ctx, r, args, stream, torch, cold=False)
+            torch.cuda.empty_cache()
+            cmd = [sys.executable, os.path.abspath(__file__), "--decoder-cell", f"{ctx}:{r}", "--steps",
+                   str(args.steps), "--warmup", str(args.warmup)]
+            cp = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+            if cp.returncode != 0:
+                raise SystemExit(f"cold decoder cell {ctx}:{r} failed ({cp.returncode}): {cp.stderr[-2000:]}")
+            c = json.loads(cp.stdout.strip().splitlines()[-1])
+            w.update({k: v for k, v in c.items() if k.startswith("cold")})
+            cells.append(w)
+            print(json.dumps(w), flush=True)
+    for ctx in ctxs:
+        base = [c for c in cells if c["context"] == ctx and c["rate"] == "always-full"][0]
+        for c in cells:
+            if c["context"] == ctx and c["rate"] != "always-full":
+                c["warm_speedup_vs_always_full"] = round(c["warm_tokens_per_s"] / base["warm_tokens_per_s"], 3)
+                c["cold_speedup_vs_always_full"] = round(c["cold_tokens_per_s"] / base["cold_tokens_per_s"], 3)
+    print(json.dumps({"matrix": "ODA decode tokens/s at batch 1 with the Qwen3-1.7B-shaped decoder backbone: "
+                                "context x forced rate", "steps": args.steps, "warmup": args.warmup,
+                      "repeats": args.repeats, "cells": cells}), flush=True)
 
 
 if __name__ == "__main__":

@@ -11,7 +11,7 @@
 // them all: v_mfma_f32_16x16x32_bf16 with A = 16 weight rows x 32 k and B = 32
 // k x 16 sequences.  In lane l = 16q + i the instruction takes A[i][8q..8q+7]
 // and B[8q..8q+7][i] (one 16-byte load each) and returns D[4q + r][i] in
-// accumulator component r.  A workgroup (4 waves) owns TW row tiles and one
+// accumulator component r.  A workgroup of NW waves owns TW row tiles and one
 // K slice; a wave takes 4 blocks of 32 k per pass and issues all its loads
 // before its first MFMA.  RMSNorm is fused into the operand load (the bf16
 // operand is gamma * x, the sum of squares is gathered from the same fp32
@@ -30,10 +30,8 @@ namespace {
 using f4v = __attribute__((ext_vector_type(4))) float;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kGemmWaves = 4;
-constexpr int kGemmThreads = kGemmWaves * 64;
-constexpr int kJB = 4;                                // 32-k blocks per wave pass
-constexpr int kKPass = kGemmWaves * kJB * 32;         // k of one workgroup pass (512)
+constexpr int kJB = 4;                                // 32-k blocks per wave pass (128 k)
+constexpr int kWaveK = kJB * 32;
 constexpr int kMaxCols = 32;
 
 enum GemmMode { kQkv = 0, kOut = 1, kGateUp = 2, kDown = 3, kLogits = 4 };
@@ -76,17 +74,18 @@ constexpr int part_stride() {
   return TW * NG * 4 * 64 + 64;
 }
 
-template <int MODE, int TW, int NG>
-__global__ void __launch_bounds__(kGemmThreads) k_gemm16(GemmArgs A) {
-  constexpr int NW = kGemmWaves, NT = kGemmThreads, JB = kJB;
+template <int MODE, int TW, int NW, int NG>
+__global__ void __launch_bounds__(NW * 64) k_gemm16(GemmArgs A) {
+  constexpr int NT = NW * 64, JB = kJB;
   constexpr int NV = TW * NG * 4;  // accumulator floats per lane
   constexpr int PMAIN = NV * 64;
   constexpr int PSZ = part_stride<TW, NG>();
   constexpr bool kNorm = MODE == kQkv || MODE == kGateUp;
   constexpr int HALF = TW / 2;
   constexpr int ROWS = MODE == kGateUp ? HALF * 16 : TW * 16;
-  static_assert(NV <= 32, "LDS staging holds 32 accumulator floats per lane");
-  __shared__ float red[NW * 32 * 64];
+  constexpr int VPR = NV < 8192 / NT ? NV : 8192 / NT;  // accumulator values per LDS round (32 KB)
+  static_assert(NV % VPR == 0, "LDS rounds");
+  __shared__ float red[NW * VPR * 64];
   __shared__ float tile[PMAIN];
   __shared__ float s_ss[kMaxCols];
   __shared__ int s_last;
@@ -97,7 +96,7 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm16(GemmArgs A) {
   const int rb = blockIdx.x, ks = blockIdx.y, nks = gridDim.y;
   const int B = A.B, K = A.K;
   const int kslice = K / nks;
-  const int iters = kslice / kKPass;
+  const int iters = kslice / (NW * kWaveK);
 
   const uint16_t* wrow[TW];
 #pragma unroll
@@ -192,17 +191,24 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm16(GemmArgs A) {
           acc[t][cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w[t][j]), xb8[cg][j], acc[t][cg], 0, 0, 0);
   }
 
-  // ---- waves -> LDS tile (value index v = (t * NG + cg) * 4 + r, lane l)
+  // ---- waves -> LDS tile (value index v = (t * NG + cg) * 4 + r, lane l), in
+  // rounds of VPR values
 #pragma unroll
-  for (int v = 0; v < NV; ++v) red[(wave * NV + v) * 64 + lane] = comp(acc[v / (NG * 4)][(v / 4) % NG], v % 4);
-  __syncthreads();
-  for (int i = tid; i < PMAIN; i += NT) {
-    float s = 0.0f;
+  for (int r0 = 0; r0 < NV; r0 += VPR) {
 #pragma unroll
-    for (int wv = 0; wv < NW; ++wv) s += red[wv * PMAIN + i];
-    tile[i] = s;
+    for (int v = 0; v < VPR; ++v) {
+      const int vv = r0 + v;
+      red[(wave * VPR + v) * 64 + lane] = comp(acc[vv / (NG * 4)][(vv / 4) % NG], vv % 4);
+    }
+    __syncthreads();
+    for (int i = tid; i < VPR * 64; i += NT) {
+      float s = 0.0f;
+#pragma unroll
+      for (int wv = 0; wv < NW; ++wv) s += red[wv * VPR * 64 + i];
+      tile[r0 * 64 + i] = s;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   if (kNorm) {
 #pragma unroll
     for (int cg = 0; cg < NG; ++cg) red[(wave * NG + cg) * 64 + lane] = ss[cg];
@@ -427,8 +433,8 @@ bool dec_derive(const oda_dec_dims* dd, DecDerived* o, int* st) {
     *st = ODA_E_DIMS;
     return false;
   }
-  if (o->D % kKPass != 0 || o->I % kKPass != 0 || (o->Hq * o->d) % kKPass != 0 || o->V % 64 != 0 ||
-      o->nqkv % 64 != 0 || o->D % 32 != 0 || o->I % 32 != 0 || o->B > kMaxCols) {
+  if (o->D % 1024 != 0 || o->I % 1024 != 0 || (o->I >= 2048 && o->I % 2048 != 0) || o->V % 64 != 0 ||
+      o->nqkv % 16 != 0 || o->B > kMaxCols) {
     *st = ODA_E_UNSUPPORTED;
     return false;
   }
@@ -450,22 +456,34 @@ struct DecWs {
   size_t qkv, act, part, tickets, cand_v, cand_i, total;
 };
 
-// row blocks and K slices of each split GEMM (logits: one slice)
+// Shape of one GEMM launch: row tiles per workgroup, waves per workgroup,
+// row blocks and K slices.  The projections use 16-row tiles and 16 waves
+// (8 when K is 1024), each wave loading its whole 128-k share at once, and a
+// single K slice where that still gives 256+ workgroups: no cross-workgroup
+// hand-off.  The down projection (K = I) keeps K / 2048 slices.  The LM head
+// has rows enough for 64-row tiles of 4 waves.
 struct GemmShape {
-  int nrb, nks;
+  int tw, nw, nrb, nks;
 };
-GemmShape shape_qkv(const DecDerived& g) { return {g.nqkv / 64, g.D / kKPass}; }
-GemmShape shape_out(const DecDerived& g) { return {g.D / 32, (g.Hq * g.d) / kKPass}; }
-GemmShape shape_gateup(const DecDerived& g) { return {g.I / 32, g.D / kKPass}; }
-GemmShape shape_down(const DecDerived& g) { return {g.D / 32, g.I / kKPass}; }
+// RMSNorm-fused modes hold the fp32 operand too: with two column groups
+// (B > 16) they run 8 waves, two passes each, inside the 1024-thread
+// register budget.
+int waves_for(int K, bool norm_two_groups) { return K >= 2048 && !norm_two_groups ? 16 : 8; }
+GemmShape shape_qkv(const DecDerived& g) { return {1, waves_for(g.D, g.B > 16), g.nqkv / 16, 1}; }
+GemmShape shape_out(const DecDerived& g) { return {1, waves_for(g.Hq * g.d, false), g.D / 16, 1}; }
+GemmShape shape_gateup(const DecDerived& g) { return {2, waves_for(g.D, g.B > 16), g.I / 16, 1}; }
+GemmShape shape_down(const DecDerived& g) {
+  const int nw = waves_for(g.I, false);
+  return {1, nw, g.D / 16, g.I / (nw * kWaveK)};
+}
+GemmShape shape_logits(const DecDerived& g) { return {4, 4, g.V / 64, 1}; }
 
 DecWs dec_ws(const DecDerived& g) {
   const GemmShape s4[4] = {shape_qkv(g), shape_out(g), shape_gateup(g), shape_down(g)};
-  const int tw[4] = {4, 2, 4, 2};
   size_t part = 0, tick = 0;
   for (int i = 0; i < 4; ++i) {
-    const size_t psz = (size_t)tw[i] * 2 * 4 * 64 + 64;  // two column groups: the largest tile
-    const size_t n = (size_t)s4[i].nrb * s4[i].nks * psz;
+    const size_t psz = (size_t)s4[i].tw * 2 * 4 * 64 + 64;  // two column groups: the largest tile
+    const size_t n = s4[i].nks > 1 ? (size_t)s4[i].nrb * s4[i].nks * psz : 0;
     if (n > part) part = n;
     if ((size_t)s4[i].nrb > tick) tick = s4[i].nrb;
   }
@@ -487,13 +505,36 @@ DecWs dec_ws(const DecDerived& g) {
   return w;
 }
 
+template <int MODE, int TW, int NW>
+int launch_gemm_nw(const GemmArgs& a, GemmShape s, hipStream_t st) {
+  const dim3 grid(s.nrb, s.nks);
+  constexpr bool kNorm = MODE == kQkv || MODE == kGateUp;
+  if (a.B <= 16) {
+    hipLaunchKernelGGL((k_gemm16<MODE, TW, NW, 1>), grid, dim3(NW * 64), 0, st, a);
+  } else if constexpr (!(kNorm && NW == 16)) {  // those run 8 waves at B > 16 (register budget)
+    hipLaunchKernelGGL((k_gemm16<MODE, TW, NW, 2>), grid, dim3(NW * 64), 0, st, a);
+  } else {
+    return ODA_E_UNSUPPORTED;
+  }
+  return ODA_OK;
+}
+
 template <int MODE, int TW>
 int launch_gemm(const GemmArgs& a, GemmShape s, hipStream_t st) {
-  const dim3 grid(s.nrb, s.nks);
-  if (a.B > 16)
-    hipLaunchKernelGGL((k_gemm16<MODE, TW, 2>), grid, dim3(kGemmThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((k_gemm16<MODE, TW, 1>), grid, dim3(kGemmThreads), 0, st, a);
+  if (s.tw != TW || a.K % (s.nks * s.nw * kWaveK) != 0 || a.K / s.nks < s.nw * kWaveK) return ODA_E_UNSUPPORTED;
+  int rc;
+  if constexpr (MODE == kLogits) {
+    if (s.nw != 4) return ODA_E_UNSUPPORTED;
+    rc = launch_gemm_nw<MODE, TW, 4>(a, s, st);
+  } else {
+    if (s.nw == 8)
+      rc = launch_gemm_nw<MODE, TW, 8>(a, s, st);
+    else if (s.nw == 16)
+      rc = launch_gemm_nw<MODE, TW, 16>(a, s, st);
+    else
+      return ODA_E_UNSUPPORTED;
+  }
+  if (rc != ODA_OK) return rc;
   return hipGetLastError() == hipSuccess ? ODA_OK : ODA_E_LAUNCH;
 }
 
@@ -594,7 +635,7 @@ int oda_dec_layer(const oda_dec_dims* dims, int32_t layer, int32_t branch, const
   a.out_b = qkv;
   a.N = g.nqkv;
   a.K = g.D;
-  if ((st = launch_gemm<kQkv, 4>(a, shape_qkv(g), stream)) != ODA_OK) return st;
+  if ((st = launch_gemm<kQkv, 1>(a, shape_qkv(g), stream)) != ODA_OK) return st;
   // QK-norm + RoPE, v copy: the branch's staged current key / value
   RopeArgs r{};
   r.qkv = qkv;
@@ -626,7 +667,7 @@ int oda_dec_layer(const oda_dec_dims* dims, int32_t layer, int32_t branch, const
   a.out_f = x;
   a.N = g.D;
   a.K = g.Hq * g.d;
-  if ((st = launch_gemm<kOut, 2>(a, shape_out(g), stream)) != ODA_OK) return st;
+  if ((st = launch_gemm<kOut, 1>(a, shape_out(g), stream)) != ODA_OK) return st;
   // gate / up (RMSNorm fused) -> SiLU(g) * u
   a.W0 = wl + g.offs[6];
   a.W1 = wl + g.offs[7];
@@ -637,7 +678,7 @@ int oda_dec_layer(const oda_dec_dims* dims, int32_t layer, int32_t branch, const
   a.out_f = nullptr;
   a.N = g.I;
   a.K = g.D;
-  if ((st = launch_gemm<kGateUp, 4>(a, shape_gateup(g), stream)) != ODA_OK) return st;
+  if ((st = launch_gemm<kGateUp, 2>(a, shape_gateup(g), stream)) != ODA_OK) return st;
   // down projection + residual
   a.W0 = wl + g.offs[8];
   a.W1 = nullptr;
@@ -648,7 +689,7 @@ int oda_dec_layer(const oda_dec_dims* dims, int32_t layer, int32_t branch, const
   a.out_f = x;
   a.N = g.D;
   a.K = g.I;
-  return launch_gemm<kDown, 2>(a, shape_down(g), stream);
+  return launch_gemm<kDown, 1>(a, shape_down(g), stream);
 }
 
 int oda_dec_final_norm(const oda_dec_dims* dims, int32_t branch, const oda_bf16* gamma_f, const float* x,
@@ -691,7 +732,7 @@ int oda_dec_next_token(const oda_dec_dims* dims, const oda_bf16* embed, const od
   a.N = g.V;
   a.K = g.D;
   a.eps = dims->eps;
-  if ((st = launch_gemm<kLogits, 4>(a, GemmShape{g.V / 64, 1}, stream)) != ODA_OK) return st;
+  if ((st = launch_gemm<kLogits, 4>(a, shape_logits(g), stream)) != ODA_OK) return st;
   hipLaunchKernelGGL(k_argmax, dim3(g.B), dim3(256), 0, stream, a.cand_v, a.cand_i, g.V / 64, g.B, tokens,
                      max_logit);
   return hipGetLastError() == hipSuccess ? ODA_OK : ODA_E_LAUNCH;

@@ -118,3 +118,12 @@ def test_decoder_tiny_layerwise_across_the_boundary():
     pr = DecProblem("tiny", [10, 2051, 2052, 5000], steps=1, seed=71)
     worst = layerwise_check(pr, [1, 1, 1, 1])
     print("tiny: worst |err| / bound", round(worst, 3))
+
+
+def test_decoder_tiny_layerwise_wide_batch():
+    """Twenty sequences (two 16-wide column groups in every GEMM) with ragged
+    contexts, half of them flagged, checked layer by layer."""
+    t0 = [7 + 211 * i for i in range(20)]
+    pr = DecProblem("tiny", t0, steps=1, seed=81)
+    worst = layerwise_check(pr, [i % 2 for i in range(20)])
+    print("tiny B=20: worst |err| / bound", round(worst, 3))
