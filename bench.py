@@ -71,6 +71,9 @@ def parse():
     ap.add_argument("--decoder-matrix", action="store_true",
                     help="decoder step at batch 1: context x forced recall-rate matrix, warm and first-request")
     ap.add_argument("--decoder-cell", default="", help=argparse.SUPPRESS)  # child process: CONTEXT:RATE, cold run
+    ap.add_argument("--train", action="store_true",
+                    help="one recall-head training step (labels through the tied LM head, then the head's "
+                         "forward, Huber loss and backward) on a 4 x 2048-position micro-batch")
     return ap.parse_args()
 
 
@@ -99,6 +102,12 @@ def main():
         stream = torch.cuda.Stream()
         with torch.cuda.stream(stream):
             print(json.dumps(decoder_cell(int(ctx), float(rate), args, stream, torch, cold=True)), flush=True)
+        return
+
+    if args.train:
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            train_bench(args, stream, torch)
         return
 
     wl_key = int(args.workload) if args.workload.isdigit() else args.workload
@@ -812,6 +821,137 @@ def decoder_matrix(args):
     print(json.dumps({"matrix": "ODA decode tokens/s at batch 1 with the Qwen3-1.7B-shaped decoder backbone: "
                                 "context x forced rate", "steps": args.steps, "warmup": args.warmup,
                       "repeats": args.repeats, "cells": cells}), flush=True)
+
+
+BF16_MFMA_PEAK_TFS = 2500.0   # MI355X dense bf16 matrix peak
+FP32_MFMA_PEAK_TFS = 157.3    # MI355X fp32 matrix peak
+
+
+def train_head_flops(N, D, T=1024, F=2048):
+    """fp32 multiply-add flops of the head step's GEMMs: every forward product
+    once more for its weight gradient and once more for its input gradient."""
+    fwd = 2 * N * (3 * T * D + 9 * T * T + 2 * (2 * F * T + F * T))
+    return 3 * fwd
+
+
+def train_bench(args, stream, torch):
+    """Recall-head training step on the 4 x 2048-position micro-batch:
+    oda_train_labels (the LM head's log-sum-exp for both candidates of every
+    row) then oda_train_head_step, inputs resident in HBM, HIP events on the
+    stream around each call of every timed step."""
+    import synth
+    import synth.device as sd
+    import conditional_sparse_attention_amd as C
+    sh = synth.train_shapes()["qwen3-1.7b-8k"]
+    N, D, V = sh.rows, sh.hidden, sh.vocab
+    t_setup = time.perf_counter()
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    pos, prev, tok, nxt = synth.train_rows(sh)
+    hl, hf = synth.train_hidden(sh)
+    blob = synth.head_blob(D, sh.head_seed, perturb=True)
+    td = C.make_train_dims(N, D, V, lam=sh.lam)
+    E = torch.empty((V, D), dtype=torch.int16, device="cuda")
+    sd.fill_dec_embed(E, sh.embed_seed)
+    head_w = dev(blob)
+    d_hl, d_hf = dev(hl.view(np.int16)), dev(hf.view(np.int16))
+    d_pos, d_prev, d_tok, d_nxt = dev(pos), dev(prev), dev(tok), dev(nxt)
+    gain = torch.zeros(N, dtype=torch.float32, device="cuda")
+    label, score = torch.zeros_like(gain), torch.zeros_like(gain)
+    valid = torch.zeros(N, dtype=torch.uint8, device="cuda")
+    loss = torch.zeros(1, dtype=torch.float32, device="cuda")
+    grad = torch.zeros(blob.size, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(C.oda_train_workspace_bytes(td), dtype=torch.uint8, device="cuda")
+    C.oda_train_workspace_init(td, ws, stream)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    def labels():
+        C.oda_train_labels(td, E, d_hl, d_hf, d_nxt, d_pos, gain, label, valid, ws, stream)
+
+    def head():
+        C.oda_train_head_step(td, head_w, E, d_hl, d_hf, d_tok, d_prev, gain, label, valid, score, loss, grad, ws,
+                              stream)
+
+    for _ in range(args.warmup):
+        labels()
+        head()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for j in range(K):
+        ev[j][0].record(stream)
+        labels()
+        ev[j][1].record(stream)
+        head()
+        ev[j][2].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3 / K
+    lab_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    head_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ms = max(wall_ms, lab_ms + head_ms)
+    assert int(ws[:4].view(torch.int32).item()) == 0, "device error bits set"
+    nvalid = int(valid.sum().item())
+    lse_flops = 2.0 * (2 * N) * V * D
+    head_flops = float(train_head_flops(N, D))
+    lse_tfs = lse_flops / (lab_ms * 1e-3) / 1e12
+    head_tfs = head_flops / (head_ms * 1e-3) / 1e12
+    out = {
+        "metric": "recall-head training positions/s (labels through the tied LM head + fp32 head forward/backward)",
+        "value": round(N / (ms * 1e-3), 1), "unit": "positions/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 LM head, fp32 head", "data": "synthetic (seeded generator: bf16 hidden states, random-init "
+        "tied LM head and fp32 recall head)",
+        "config": {"workload": sh.name, "rows": N, "sequences": sh.runs, "positions_per_sequence": sh.rows_per_run,
+                   "first_position": sh.first_pos, "hidden": D, "vocab": V, "lambda": sh.lam,
+                   "valid_rows": nvalid, "loss": round(float(loss.item()), 6)},
+        "roofline": {"bound": "mfma", "kernel": "k_lse (oda_train_labels)", "achieved": round(lse_tfs, 1),
+                     "peak": BF16_MFMA_PEAK_TFS, "unit": "TFLOP/s", "frac": round(lse_tfs / BF16_MFMA_PEAK_TFS, 4),
+                     "traffic": None, "avg_launch_us": round(lab_ms * 1e3, 1),
+                     "algorithmic_flops_per_launch": lse_flops,
+                     "note": "event pair around oda_train_labels: k_lse plus three row kernels of a few us"},
+        "head_step": {"ms": round(head_ms, 4), "flops": head_flops, "achieved_tflops": round(head_tfs, 1),
+                      "peak": FP32_MFMA_PEAK_TFS, "frac": round(head_tfs / FP32_MFMA_PEAK_TFS, 4)},
+        "labels_ms": round(lab_ms, 4), "wall_ms_per_step": round(wall_ms, 4), "setup_s": round(setup_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = train_cpu_baseline(sh, E, blob, hl, hf, pos, prev, tok, nxt)
+    print(json.dumps(out), flush=True)
+
+
+def train_cpu_baseline(sh, E, blob, hl, hf, pos, prev, tok, nxt):
+    """The training oracle, untuned, on a bounded sample: the labels of 96 rows
+    over the whole vocabulary and the head's forward and backward on 2048
+    rows, each scaled to the micro-batch's N rows."""
+    from oracle import train as T
+    from oracle.oda_oracle import bf16_to_f64
+    from threadpoolctl import threadpool_info
+    N = sh.rows
+    Eb = E.cpu().numpy().view(np.uint16)
+    nl = 96
+    rows = np.arange(N - nl, N)
+    c0 = time.perf_counter()
+    g, y, v = T.labels(Eb, hl[rows], hf[rows], nxt[rows], pos[rows], sh.lam)
+    t_lab = (time.perf_counter() - c0) / len(rows)
+    n = 2048
+    rows = np.arange(N - n, N)
+    P = T.unpack(blob, sh.hidden, 1024, 2048)
+    hL = bf16_to_f64(hl[rows])
+    Hp = bf16_to_f64(hl[rows - 1])
+    Em = bf16_to_f64(Eb[tok[rows]])
+    yy = np.resize(y, n)
+    c0 = time.perf_counter()
+    q, cache = T.head_forward(P, Hp, Em, hL)
+    _, dq = T.loss_and_dq(q, yy, np.ones(n, dtype=bool))
+    T.head_backward(P, cache, dq)
+    t_head = (time.perf_counter() - c0) / n
+    step_s = N * (t_lab + t_head)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(N / step_s, 2), "unit": "positions/s", "cores": int(threads), "kind": "oracle",
+            "host_cpus": os.cpu_count(),
+            "sample": (f"labels of {nl} rows over {sh.vocab} vocabulary rows ({t_lab * nl:.2f} s), head forward "
+                       f"and backward on {n} rows ({t_head * n:.2f} s); scaled to {N} rows"),
+            "sample_cpu_s": round(t_lab * nl + t_head * n, 2)}
 
 
 if __name__ == "__main__":

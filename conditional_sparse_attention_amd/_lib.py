@@ -1,4 +1,4 @@
-"""ctypes binding of liboda (include/oda.h, include/oda_decoder.h).
+"""ctypes binding of liboda (include/oda.h, include/oda_decoder.h, include/oda_train.h).
 
 Argument marshalling only: every function takes torch tensors (or None for a
 nullable pointer), passes their device pointers and the current HIP stream
@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "liboda.so")
 ODA_OK = 0
 ODA_E_NULL, ODA_E_DIMS, ODA_E_UNSUPPORTED, ODA_E_WORKSPACE, ODA_E_LAYER, ODA_E_LAUNCH = -1, -2, -3, -4, -5, -6
 ODA_KV_CONTIG, ODA_KV_PAGED = 0, 1
-ODA_ERR_CAPACITY, ODA_ERR_BLOCK, ODA_ERR_TOKEN = 1, 2, 4
+ODA_ERR_CAPACITY, ODA_ERR_BLOCK, ODA_ERR_TOKEN, ODA_ERR_ROW = 1, 2, 4, 8
 ODA_DEC_LOCAL, ODA_DEC_FULL = 0, 1
 ODA_DEC_NTENSORS = 9
 ODA_HEAD_NTENSORS = 22
@@ -32,6 +32,7 @@ EXPORTED = (
     "oda_local_ranges", "oda_local_attn", "oda_recall_score", "oda_worklist", "oda_full_attn_if", "oda_commit",
     "oda_dec_layer_numel", "oda_dec_layer_offsets", "oda_dec_workspace_bytes", "oda_dec_workspace_init",
     "oda_dec_embed", "oda_dec_layer", "oda_dec_final_norm", "oda_dec_next_token",
+    "oda_train_workspace_bytes", "oda_train_workspace_init", "oda_train_labels", "oda_train_head_step",
 )
 
 
@@ -62,6 +63,11 @@ class oda_dec_dims(ctypes.Structure):
                 ("rope_theta", ctypes.c_float), ("eps", ctypes.c_float)]
 
 
+class oda_train_dims(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int32), ("hidden", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("sink", ctypes.c_int32), ("window", ctypes.c_int32), ("lam", ctypes.c_float)]
+
+
 _lib = None
 
 
@@ -75,6 +81,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
         dp, kp, ddp = ctypes.POINTER(oda_dims), ctypes.POINTER(oda_kv), ctypes.POINTER(oda_dec_dims)
+        tdp = ctypes.POINTER(oda_train_dims)
         sig = {
             "oda_abi_version": (ctypes.c_int, []),
             "oda_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -97,6 +104,11 @@ def lib() -> ctypes.CDLL:
             "oda_dec_layer": (ctypes.c_int, [ddp, i32, i32, vp, kp, vp, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]),
             "oda_dec_final_norm": (ctypes.c_int, [ddp, i32, vp, vp, vp, vp, sz, vp]),
             "oda_dec_next_token": (ctypes.c_int, [ddp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "oda_train_workspace_bytes": (sz, [tdp]),
+            "oda_train_workspace_init": (ctypes.c_int, [tdp, vp, sz, vp]),
+            "oda_train_labels": (ctypes.c_int, [tdp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "oda_train_head_step": (ctypes.c_int, [tdp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                                   vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -269,3 +281,35 @@ def oda_dec_final_norm(dd, branch, gamma_f, x, h, ws=None, stream=None) -> None:
 def oda_dec_next_token(dd, embed, h_local, h_full, flag, tokens, max_logit, dws, stream=None) -> None:
     check(lib().oda_dec_next_token(ctypes.byref(dd), _p(embed), _p(h_local), _p(h_full), _p(flag), _p(tokens),
                                    _p(max_logit), _p(dws), _bytes(dws), _s(stream)), "oda_dec_next_token")
+
+
+# --------------------------------------------------------------------------
+# recall-head training step (include/oda_train.h)
+# --------------------------------------------------------------------------
+def make_train_dims(rows: int, hidden: int, vocab: int, lam: float = 0.0, sink: int = 4,
+                    window: int = 2048) -> oda_train_dims:
+    return oda_train_dims(rows=rows, hidden=hidden, vocab=vocab, sink=sink, window=window, lam=lam)
+
+
+def oda_train_workspace_bytes(td: oda_train_dims) -> int:
+    n = int(lib().oda_train_workspace_bytes(ctypes.byref(td)))
+    if n == 0:
+        raise OdaError(ODA_E_DIMS, "oda_train_workspace_bytes")
+    return n
+
+
+def oda_train_workspace_init(td, ws, stream=None) -> None:
+    check(lib().oda_train_workspace_init(ctypes.byref(td), _p(ws), _bytes(ws), _s(stream)),
+          "oda_train_workspace_init")
+
+
+def oda_train_labels(td, lm_head, h_local, h_full, next_tok, pos, gain, label, valid, ws, stream=None) -> None:
+    check(lib().oda_train_labels(ctypes.byref(td), _p(lm_head), _p(h_local), _p(h_full), _p(next_tok), _p(pos),
+                                 _p(gain), _p(label), _p(valid), _p(ws), _bytes(ws), _s(stream)), "oda_train_labels")
+
+
+def oda_train_head_step(td, head_w, lm_head, h_local, h_full, tokens, prev, gain, label, valid, score, loss, grad,
+                        ws, stream=None) -> None:
+    check(lib().oda_train_head_step(ctypes.byref(td), _p(head_w), _p(lm_head), _p(h_local), _p(h_full), _p(tokens),
+                                    _p(prev), _p(gain), _p(label), _p(valid), _p(score), _p(loss), _p(grad), _p(ws),
+                                    _bytes(ws), _s(stream)), "oda_train_head_step")

@@ -78,7 +78,8 @@ extern "C" {
 #define ODA_WS_ERROR_WORD 0
 #define ODA_ERR_CAPACITY 1   /* pos[b] + 1 exceeds the sequence's capacity */
 #define ODA_ERR_BLOCK 2      /* a block-table entry is outside [0, num_blocks) */
-#define ODA_ERR_TOKEN 4      /* a decoder token id is outside [0, vocab) (oda_decoder.h) */
+#define ODA_ERR_TOKEN 4      /* a token id is outside [0, vocab) (oda_decoder.h, oda_train.h) */
+#define ODA_ERR_ROW 8        /* a previous-row index is outside [-1, rows) (oda_train.h) */
 
 /* recall head geometry [ODA notes §2.2]: three 1024-wide towers, a
  * 9*1024-wide interaction, two gated FFN blocks of hidden width 2048 */

@@ -57,6 +57,10 @@ TAG_SHUF = 15                  # paged block shuffle
 TAG_DEC_W = 16                 # decoder weight matrices and the token-embedding table
 TAG_DEC_G = 17                 # decoder norm gains (perturbed variants)
 TAG_TOK = 18                   # first tokens of the decoder workloads
+TAG_TRAIN_HL = 19              # training rows: local-branch final hidden states
+TAG_TRAIN_HF = 20              # training rows: full-branch final hidden states (rows that differ)
+TAG_TRAIN_TOK = 21             # training rows: token streams
+TAG_TRAIN_SEL = 22             # training rows: which rows' full state differs
 
 MAX_B = 32          # logical batch stride of the index space
 POS_BITS = 18       # logical position stride 2**18
@@ -473,3 +477,78 @@ def dec_embed_bits(seed: int, shape: DecoderShape, rows) -> np.ndarray:
 
 def dec_first_tokens(seed: int, batch: int, vocab: int) -> np.ndarray:
     return (hash_at(seed, TAG_TOK, np.arange(batch)) % _U64(vocab)).astype(np.int32)
+
+
+# --------------------------------------------------------------------------
+# recall-head training micro-batches (paired branch outputs)
+# --------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class TrainShape:
+    """A training micro-batch: `runs` stretches of `rows_per_run` consecutive
+    positions, the first at 0-based position `first_pos`.  Every row carries
+    the local and the full branch's final hidden state at its position; the
+    two are identical where the index sets coincide (pos < s + w) and, past
+    that, differ on a `differ_rate` share of the rows (independent draws) and
+    coincide on the rest."""
+    name: str
+    hidden: int
+    vocab: int
+    runs: int
+    rows_per_run: int
+    first_pos: int
+    differ_rate: float
+    seed: int
+    head_seed: int
+    embed_seed: int
+    lam: float = 0.0
+
+    @property
+    def rows(self) -> int:
+        return self.runs * self.rows_per_run
+
+
+def train_shapes() -> dict:
+    return {
+        # 4 sequences x 2048 positions starting at t = 2052 (the last position
+        # whose index sets coincide), with the Qwen3-1.7B hidden size and
+        # vocabulary
+        "qwen3-1.7b-8k": TrainShape("qwen3-1.7b-8k", 2048, 151936, 4, 2048, 2051, 0.25, seed=41,
+                                    head_seed=141, embed_seed=241),
+        "small": TrainShape("small", 2048, 151936, 2, 20, 2040, 0.5, seed=42, head_seed=142, embed_seed=242,
+                            lam=0.001),
+    }
+
+
+def train_rows(sh: TrainShape):
+    """pos, prev, tokens (x_t) and next tokens (x_{t+1}) of every row [N] int32.
+    prev is the row of the previous position, -1 at the first row of a run
+    whose position is 0 ... and also at the first row of a later stretch (its
+    predecessor is not in the micro-batch)."""
+    n = np.arange(sh.rows)
+    run, j = n // sh.rows_per_run, n % sh.rows_per_run
+    pos = (sh.first_pos + j).astype(np.int32)
+    prev = np.where(j > 0, n - 1, -1).astype(np.int32)
+    stream = (run.astype(_U64) << _U64(32))
+    tok = (hash_at(sh.seed, TAG_TRAIN_TOK, stream + pos.astype(_U64)) % _U64(sh.vocab)).astype(np.int32)
+    nxt = (hash_at(sh.seed, TAG_TRAIN_TOK, stream + pos.astype(_U64) + _U64(1)) % _U64(sh.vocab)).astype(np.int32)
+    return pos, prev, tok, nxt
+
+
+def train_differs(sh: TrainShape, pos: np.ndarray, sink: int = 4, window: int = 2048) -> np.ndarray:
+    """Rows whose full-branch state is drawn independently of the local one."""
+    u = uniform_at(sh.seed, TAG_TRAIN_SEL, np.arange(sh.rows))
+    return (u < sh.differ_rate) & (np.asarray(pos) >= sink + window)
+
+
+def train_hidden(sh: TrainShape, rows=None):
+    """bf16 bits of h^L and h^F for `rows` (default: all) [len][D]."""
+    rows = np.arange(sh.rows) if rows is None else np.asarray(rows, dtype=np.int64)
+    pos, _, _, _ = train_rows(sh)
+    D = sh.hidden
+    idx = (rows[:, None] * D + np.arange(D)[None, :]).astype(_U64)
+    hl = bf16_at(sh.seed, TAG_TRAIN_HL, idx)
+    hf = hl.copy()
+    dif = train_differs(sh, pos)[rows]
+    if np.any(dif):
+        hf[dif] = bf16_at(sh.seed, TAG_TRAIN_HF, idx[dif])
+    return hl, hf
