@@ -920,20 +920,20 @@ def train_bench(args, stream, torch):
 
 
 def train_cpu_baseline(sh, E, blob, hl, hf, pos, prev, tok, nxt):
-    """The training oracle, untuned, on a bounded sample: the labels of 96 rows
-    over the whole vocabulary and the head's forward and backward on 2048
+    """The training oracle, untuned, on a bounded sample: the labels of 640
+    rows over the whole vocabulary and the head's forward and backward on 4096
     rows, each scaled to the micro-batch's N rows."""
     from oracle import train as T
     from oracle.oda_oracle import bf16_to_f64
     from threadpoolctl import threadpool_info
     N = sh.rows
     Eb = E.cpu().numpy().view(np.uint16)
-    nl = 96
+    nl = 640
     rows = np.arange(N - nl, N)
     c0 = time.perf_counter()
     g, y, v = T.labels(Eb, hl[rows], hf[rows], nxt[rows], pos[rows], sh.lam)
     t_lab = (time.perf_counter() - c0) / len(rows)
-    n = 2048
+    n = 4096
     rows = np.arange(N - n, N)
     P = T.unpack(blob, sh.hidden, 1024, 2048)
     hL = bf16_to_f64(hl[rows])

@@ -4,11 +4,12 @@
 // §2.2 d, y, loss, paired supervision].  oda_train.h states what is computed.
 //
 // Labels.  The log-sum-exp over the vocabulary of E h for 2N hidden rows is a
-// dense bf16 contraction (2 N V D multiply-adds): k_lse tiles it 128 rows x
-// 128 vocabulary rows per workgroup on v_mfma_f32_16x16x32_bf16 (lane
-// 16q + i takes A[i][8q..8q+7] and B[8q..8q+7][i], returns D[4q + r][i]), K
-// staged through LDS 64 at a time, and reduces its tile to a (max, sum of
-// exp) pair per row, never writing logits.  Each XCD owns one slice of the
+// dense bf16 contraction (2 N V D multiply-adds): k_lse tiles it 256 rows x
+// 256 vocabulary rows per workgroup of eight waves (128 x 64 each) on
+// v_mfma_f32_16x16x32_bf16 (lane 16q + i takes A[i][8q..8q+7] and
+// B[8q..8q+7][i], returns D[4q + r][i]), K staged through LDS 32 at a time,
+// and reduces its tile to a (max, sum of exp) pair per row, never writing
+// logits.  Each XCD owns one slice of the
 // vocabulary and walks it for groups of row blocks, so E streams through
 // every L2 a few times and the hidden rows stay cache-resident.  k_lse_fin
 // merges the pairs in tile order.
@@ -31,6 +32,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "oda_train.h"
 #include "oda_internal.h"
@@ -44,7 +46,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr float kEps = 1e-6f;         // RMSNorm epsilon of the head
 constexpr int kMaxRows = 65536;
 constexpr int kXcds = 8;              // gfx950: workgroups are dealt to 8 XCDs in turn
-constexpr int kColChunks = 32;        // row chunks of a column sum
+constexpr int kColChunks = 256;       // at most this many row chunks in a column sum
 
 // ---------------------------------------------------------------------------
 // small device helpers
@@ -119,28 +121,40 @@ __device__ __forceinline__ void sg_fetch(const float* __restrict__ X, int64_t ld
   }
 }
 
-// Registers -> LDS tile S[row][k] (k contiguous).
+// Registers -> LDS.  A k-contiguous operand is stored as S[row][k] (row
+// stride kLdk), a row-contiguous one as S[k][row] (row stride kLdr): both
+// as 16-byte stores, and both read without bank conflicts by sg_frag.
+constexpr int kLdr = kBM + 4;
+constexpr int kTileFloats = kBM * kLdk > kBK * kLdr ? kBM * kLdk : kBK * kLdr;
+
 template <bool KC>
-__device__ __forceinline__ void sg_put(float (*S)[kLdk], int tid, const float4 (&v)[2]) {
+__device__ __forceinline__ void sg_put(float* S, int tid, const float4 (&v)[2]) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int idx = tid + 256 * i;
     if (KC) {
-      *reinterpret_cast<float4*>(&S[idx >> 2][4 * (idx & 3)]) = v[i];
+      *reinterpret_cast<float4*>(&S[(idx >> 2) * kLdk + 4 * (idx & 3)]) = v[i];
     } else {
-      const int k = idx >> 5, r = 4 * (idx & 31);
-      S[r][k] = v[i].x;
-      S[r + 1][k] = v[i].y;
-      S[r + 2][k] = v[i].z;
-      S[r + 3][k] = v[i].w;
+      *reinterpret_cast<float4*>(&S[(idx >> 5) * kLdr + 4 * (idx & 31)]) = v[i];
     }
   }
 }
 
+// The four values lane (q, i) feeds MFMA number j = 0..3 of a stage for the
+// 16 rows starting at r0: element (r0 + i, k = 4q + j).
+template <bool KC>
+__device__ __forceinline__ f4v sg_frag(const float* S, int r0, int li, int lq) {
+  if (KC) return *reinterpret_cast<const f4v*>(&S[(r0 + li) * kLdk + 4 * lq]);
+  f4v v;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = S[(4 * lq + j) * kLdr + r0 + li];
+  return v;
+}
+
 template <bool AK, bool BK, int EPI>
 __global__ void __launch_bounds__(256) k_sgemm(Sg g) {
-  __shared__ __attribute__((aligned(16))) float As[2][kBM][kLdk];
-  __shared__ __attribute__((aligned(16))) float Bs[2][kBN][kLdk];
+  __shared__ __attribute__((aligned(16))) float As[2][kTileFloats];
+  __shared__ __attribute__((aligned(16))) float Bs[2][kTileFloats];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, lq = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
   const int n0 = blockIdx.x * kBN, m0 = blockIdx.y * kBM, z = blockIdx.z;
@@ -170,8 +184,8 @@ __global__ void __launch_bounds__(256) k_sgemm(Sg g) {
     f4v a[4], b[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      a[t] = *reinterpret_cast<const f4v*>(&As[cur][wm * 64 + t * 16 + li][4 * lq]);
-      b[t] = *reinterpret_cast<const f4v*>(&Bs[cur][wn * 64 + t * 16 + li][4 * lq]);
+      a[t] = sg_frag<AK>(As[cur], wm * 64 + t * 16, li, lq);
+      b[t] = sg_frag<BK>(Bs[cur], wn * 64 + t * 16, li, lq);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -527,7 +541,8 @@ __global__ void __launch_bounds__(256) k_colsum_fin(const float* __restrict__ pa
 // ===========================================================================
 // labels: log-sum-exp of E h over the vocabulary for 2N rows
 // ===========================================================================
-constexpr int kLBM = 128, kLBN = 128, kLBK = 64, kLLd = kLBK + 8;  // 144-byte LDS rows: conflict-free b128 reads
+constexpr int kLBM = 256, kLBN = 256, kLBK = 32, kLLd = kLBK + 8;  // 80-byte LDS rows: conflict-free b128 reads
+constexpr int kLThreads = 512;                                       // 8 waves, 2 x 4, each 128 rows x 64 columns
 constexpr int kLGroup = 16;                                          // row blocks walked together per XCD
 
 struct LseArgs {
@@ -545,32 +560,34 @@ __device__ __forceinline__ const uint16_t* lse_row(const LseArgs& a, int r) {
   return r < a.N ? a.hL + (size_t)r * a.D : a.hF + (size_t)(r - a.N) * a.D;
 }
 
-__device__ __forceinline__ void lse_fetch(const LseArgs& a, int r0, int v0, int k0, int tid, uint4 (&ra)[4],
-                                          uint4 (&rb)[4]) {
+// One stage: 256 hidden rows and 256 vocabulary rows of 32 k each (two
+// 16-byte pieces per thread and operand).
+__device__ __forceinline__ void lse_fetch(const LseArgs& a, int r0, int v0, int k0, int tid, uint4 (&ra)[2],
+                                          uint4 (&rb)[2]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = tid + 256 * i, row = idx >> 3, kq = idx & 7;
+  for (int i = 0; i < 2; ++i) {
+    const int idx = tid + kLThreads * i, row = idx >> 2, kq = idx & 3;
     const int r = r0 + row, v = v0 + row;
     ra[i] = r < a.R ? *reinterpret_cast<const uint4*>(lse_row(a, r) + k0 + 8 * kq) : make_uint4(0, 0, 0, 0);
     rb[i] = v < a.V ? *reinterpret_cast<const uint4*>(a.E + (size_t)v * a.D + k0 + 8 * kq) : make_uint4(0, 0, 0, 0);
   }
 }
 
-__device__ __forceinline__ void lse_put(uint16_t (*As)[kLLd], uint16_t (*Bs)[kLLd], int tid, const uint4 (&ra)[4],
-                                        const uint4 (&rb)[4]) {
+__device__ __forceinline__ void lse_put(uint16_t (*As)[kLLd], uint16_t (*Bs)[kLLd], int tid, const uint4 (&ra)[2],
+                                        const uint4 (&rb)[2]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = tid + 256 * i, row = idx >> 3, kq = idx & 7;
+  for (int i = 0; i < 2; ++i) {
+    const int idx = tid + kLThreads * i, row = idx >> 2, kq = idx & 3;
     *reinterpret_cast<uint4*>(&As[row][8 * kq]) = ra[i];
     *reinterpret_cast<uint4*>(&Bs[row][8 * kq]) = rb[i];
   }
 }
 
-__global__ void __launch_bounds__(256) k_lse(LseArgs a) {
+__global__ void __launch_bounds__(kLThreads) k_lse(LseArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kLBM][kLLd];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kLBN][kLLd];
   __shared__ int s_tok[kLBM];
-  __shared__ float s_m[2][kLBM], s_s[2][kLBM];
+  __shared__ float s_m[4][kLBM], s_s[4][kLBM];
 
   // workgroup -> (row block, vocabulary tile): XCD x owns tiles
   // [x ntiles / 8, (x + 1) ntiles / 8) and walks them for kLGroup row blocks
@@ -585,52 +602,58 @@ __global__ void __launch_bounds__(256) k_lse(LseArgs a) {
   const int r0 = rb * kLBM, v0 = tile * kLBN;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, lq = lane >> 4;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   if (tid < kLBM) {
     const int r = r0 + tid;
     s_tok[tid] = r < a.R ? a.tok[r < a.N ? r : r - a.N] : -1;
   }
 
-  f4v acc[4][4];
+  f4v acc[8][4];
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+  for (int x = 0; x < 8; ++x)
 #pragma unroll
     for (int y = 0; y < 4; ++y) acc[x][y] = f4v{0.f, 0.f, 0.f, 0.f};
 
+  // K stages of 32: stage s is in LDS buffer s & 1 while the registers hold
+  // the next two stages' loads (set s & 1 is refilled with stage s + 2 as
+  // soon as stage s has gone to LDS), so a load has two stages of MFMA work
+  // to arrive in
   const int nst = a.D / kLBK;
-  uint4 ra[4], rb4[4];
-  lse_fetch(a, r0, v0, 0, tid, ra, rb4);
-  lse_put(As[0], Bs[0], tid, ra, rb4);
+  uint4 ra[2][2], rb2[2][2];
+  lse_fetch(a, r0, v0, 0, tid, ra[0], rb2[0]);
+  if (nst > 1) lse_fetch(a, r0, v0, kLBK, tid, ra[1], rb2[1]);
+  lse_put(As[0], Bs[0], tid, ra[0], rb2[0]);
   __syncthreads();
-  for (int s = 0; s < nst; ++s) {
-    const int cur = s & 1;
-    const bool more = s + 1 < nst;
-    if (more) lse_fetch(a, r0, v0, (s + 1) * kLBK, tid, ra, rb4);
+  auto stage = [&](int s, auto phase) {
+    constexpr int P = decltype(phase)::value;  // s & 1
+    if (s + 2 < nst) lse_fetch(a, r0, v0, (s + 2) * kLBK, tid, ra[P], rb2[P]);
+    bf16x8 bv[4];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 av[4], bv[4];
+    for (int t = 0; t < 4; ++t)
+      bv[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&Bs[P][wn * 64 + t * 16 + li][8 * lq]));
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        av[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&As[cur][wm * 64 + t * 16 + li][32 * kk + 8 * lq]));
-        bv[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&Bs[cur][wn * 64 + t * 16 + li][32 * kk + 8 * lq]));
-      }
+    for (int mt = 0; mt < 8; ++mt) {
+      const bf16x8 av =
+          __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&As[P][wm * 128 + mt * 16 + li][8 * lq]));
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt], bv[nt], acc[mt][nt], 0, 0, 0);
+      for (int nt = 0; nt < 4; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[nt], acc[mt][nt], 0, 0, 0);
     }
-    if (more) lse_put(As[cur ^ 1], Bs[cur ^ 1], tid, ra, rb4);
+    if (s + 1 < nst) lse_put(As[P ^ 1], Bs[P ^ 1], tid, ra[P ^ 1], rb2[P ^ 1]);
     __syncthreads();
+  };
+  for (int s = 0; s < nst; s += 2) {
+    stage(s, std::integral_constant<int, 0>{});
+    if (s + 1 < nst) stage(s + 1, std::integral_constant<int, 1>{});
   }
 
   // per row: max and sum of exp over this tile's columns (< V), the
   // reference token's logit where it falls in the tile
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int rl = wm * 64 + mt * 16 + 4 * lq + r;
+      const int rl = wm * 128 + mt * 16 + 4 * lq + r;
       float mx = -INFINITY;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
@@ -654,9 +677,13 @@ __global__ void __launch_bounds__(256) k_lse(LseArgs a) {
     }
   __syncthreads();
   if (tid < kLBM && r0 + tid < a.R) {
-    const float m0 = s_m[0][tid], m1 = s_m[1][tid];
-    const float M = fmaxf(m0, m1);
-    const float S = s_s[0][tid] * expf(m0 - M) + (m1 == -INFINITY ? 0.0f : s_s[1][tid] * expf(m1 - M));
+    float M = s_m[0][tid];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, s_m[w][tid]);
+    float S = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (s_m[w][tid] != -INFINITY) S += s_s[w][tid] * expf(s_m[w][tid] - M);
     a.part[(size_t)tile * a.R + r0 + tid] = make_float2(M, S);
   }
 }
@@ -862,7 +889,7 @@ Sg sg(const float* A, int64_t lda, const float* B, int64_t ldb, float* C, int64_
 
 void colsum(const float* A, const float* B, const float* rs, int rows, int cols, const float* post, float* out,
             float* part, hipStream_t st) {
-  const int chunks = std::min(kColChunks, rows);
+  const int chunks = std::max(1, std::min(kColChunks, rows / 32));
   dim3 g1((cols + 255) / 256, chunks);
   hipLaunchKernelGGL(k_colsum_part, g1, dim3(256), 0, st, A, B, rs, rows, cols, part);
   hipLaunchKernelGGL(k_colsum_fin, dim3((cols + 255) / 256), dim3(256), 0, st, part, chunks, cols, post, out);
@@ -922,7 +949,7 @@ int oda_train_labels(const oda_train_dims* dims, const oda_bf16* lm_head, const 
     const int t_lo = (int)((int64_t)a.ntiles * x / kXcds), t_hi = (int)((int64_t)a.ntiles * (x + 1) / kXcds);
     a.per_xcd = std::max(a.per_xcd, (t_hi - t_lo) * a.rblocks);
   }
-  hipLaunchKernelGGL(k_lse, dim3(a.per_xcd * kXcds), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(k_lse, dim3(a.per_xcd * kXcds), dim3(kLThreads), 0, stream, a);
   hipLaunchKernelGGL(k_lse_fin, dim3((2 * N + 63) / 64), dim3(256), 0, stream, a.part, a.ntiles, 2 * N, lse);
   hipLaunchKernelGGL(k_labels, dim3((N + 255) / 256), dim3(256), 0, stream, lse, tgt, tok, pos, N,
                      dims->sink + dims->window, dims->lambda, gain, label, valid);
