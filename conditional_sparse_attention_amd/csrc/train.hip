@@ -7,7 +7,7 @@
 // dense bf16 contraction (2 N V D multiply-adds): k_lse tiles it 256 rows x
 // 256 vocabulary rows per workgroup of eight waves (128 x 64 each) on
 // v_mfma_f32_16x16x32_bf16 (lane 16q + i takes A[i][8q..8q+7] and
-// B[8q..8q+7][i], returns D[4q + r][i]), K staged through LDS 32 at a time,
+// B[8q..8q+7][i], returns D[4q + r][i]), K staged through LDS 64 at a time,
 // and reduces its tile to a (max, sum of exp) pair per row, never writing
 // logits.  Each XCD owns one slice of the
 // vocabulary and walks it for groups of row blocks, so E streams through
@@ -32,7 +32,6 @@
 #include <string.h>
 
 #include <algorithm>
-#include <type_traits>
 
 #include "oda_train.h"
 #include "oda_internal.h"
@@ -529,19 +528,27 @@ __global__ void __launch_bounds__(256) k_colsum_part(const float* __restrict__ A
   part[(size_t)c * cols + j] = s;
 }
 
+// out[j] = sum over chunks of part[c][j] (* post[j]); four threads per
+// column take the chunks c = 4 i + t in order, then add their sums in t order.
 __global__ void __launch_bounds__(256) k_colsum_fin(const float* __restrict__ part, int chunks, int cols,
                                                     const float* __restrict__ post, float* __restrict__ out) {
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= cols) return;
+  const int j = blockIdx.x * 64 + (threadIdx.x >> 2), t = threadIdx.x & 3;
   float s = 0.0f;
-  for (int c = 0; c < chunks; ++c) s += part[(size_t)c * cols + j];
-  out[j] = post != nullptr ? s * post[j] : s;
+  if (j < cols)
+    for (int c = t; c < chunks; c += 4) s += part[(size_t)c * cols + j];
+  const int base = threadIdx.x & ~3;
+  const float s0 = __shfl(s, base, 64), s1 = __shfl(s, base + 1, 64), s2 = __shfl(s, base + 2, 64),
+              s3 = __shfl(s, base + 3, 64);
+  if (t == 0 && j < cols) {
+    const float v = (s0 + s1) + (s2 + s3);
+    out[j] = post != nullptr ? v * post[j] : v;
+  }
 }
 
 // ===========================================================================
 // labels: log-sum-exp of E h over the vocabulary for 2N rows
 // ===========================================================================
-constexpr int kLBM = 256, kLBN = 256, kLBK = 32, kLLd = kLBK + 8;  // 80-byte LDS rows: conflict-free b128 reads
+constexpr int kLBM = 256, kLBN = 256, kLBK = 64, kLLd = kLBK + 8;  // 144-byte LDS rows: conflict-free b128 reads
 constexpr int kLThreads = 512;                                       // 8 waves, 2 x 4, each 128 rows x 64 columns
 constexpr int kLGroup = 16;                                          // row blocks walked together per XCD
 
@@ -561,25 +568,69 @@ __device__ __forceinline__ const uint16_t* lse_row(const LseArgs& a, int r) {
 }
 
 // One stage: 256 hidden rows and 256 vocabulary rows of 32 k each (two
-// 16-byte pieces per thread and operand).
-__device__ __forceinline__ void lse_fetch(const LseArgs& a, int r0, int v0, int k0, int tid, uint4 (&ra)[2],
-                                          uint4 (&rb)[2]) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int idx = tid + kLThreads * i, row = idx >> 2, kq = idx & 3;
-    const int r = r0 + row, v = v0 + row;
-    ra[i] = r < a.R ? *reinterpret_cast<const uint4*>(lse_row(a, r) + k0 + 8 * kq) : make_uint4(0, 0, 0, 0);
-    rb[i] = v < a.V ? *reinterpret_cast<const uint4*>(a.E + (size_t)v * a.D + k0 + 8 * kq) : make_uint4(0, 0, 0, 0);
-  }
+// 16-byte pieces per thread and operand).  Rows past the ends are clamped to
+// the last row rather than skipped: their logits land in rows that are never
+// written and in columns the epilogue masks, and unconditional loads let the
+// compiler wait for exactly the stage it needs while later ones are in flight.
+// One stage: 256 hidden rows and 256 vocabulary rows of 64 k each, four
+// 16-byte pieces per thread and operand (rows idx / 8 + 64 j).  Named fields
+// rather than arrays keep the pieces in registers.  Rows past the ends are
+// clamped to the last row rather than skipped: their logits land in rows
+// that are never written and in columns the epilogue masks, and
+// unconditional loads keep the compiler's wait counts exact.
+struct LseStage {
+  uint4 a0, a1, a2, a3, b0, b1, b2, b3;
+};
+
+__device__ __forceinline__ uint4 lse_ld(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ LseStage lse_fetch(const LseArgs& a, int r0, int v0, int k0, int tid) {
+  const int row = tid >> 3, kk = k0 + 8 * (tid & 7);
+  const int rm = a.R - 1, vm = a.V - 1;
+  const uint16_t* E = a.E + kk;
+  const size_t D = a.D;
+  LseStage st;
+  st.a0 = lse_ld(lse_row(a, min(r0 + row, rm)) + kk);
+  st.a1 = lse_ld(lse_row(a, min(r0 + row + 64, rm)) + kk);
+  st.a2 = lse_ld(lse_row(a, min(r0 + row + 128, rm)) + kk);
+  st.a3 = lse_ld(lse_row(a, min(r0 + row + 192, rm)) + kk);
+  st.b0 = lse_ld(E + (size_t)min(v0 + row, vm) * D);
+  st.b1 = lse_ld(E + (size_t)min(v0 + row + 64, vm) * D);
+  st.b2 = lse_ld(E + (size_t)min(v0 + row + 128, vm) * D);
+  st.b3 = lse_ld(E + (size_t)min(v0 + row + 192, vm) * D);
+  return st;
 }
 
-__device__ __forceinline__ void lse_put(uint16_t (*As)[kLLd], uint16_t (*Bs)[kLLd], int tid, const uint4 (&ra)[2],
-                                        const uint4 (&rb)[2]) {
+__device__ __forceinline__ void lse_put(uint16_t (*As)[kLLd], uint16_t (*Bs)[kLLd], int tid, const LseStage& st) {
+  const int row = tid >> 3, c = 8 * (tid & 7);
+  *reinterpret_cast<uint4*>(&As[row][c]) = st.a0;
+  *reinterpret_cast<uint4*>(&As[row + 64][c]) = st.a1;
+  *reinterpret_cast<uint4*>(&As[row + 128][c]) = st.a2;
+  *reinterpret_cast<uint4*>(&As[row + 192][c]) = st.a3;
+  *reinterpret_cast<uint4*>(&Bs[row][c]) = st.b0;
+  *reinterpret_cast<uint4*>(&Bs[row + 64][c]) = st.b1;
+  *reinterpret_cast<uint4*>(&Bs[row + 128][c]) = st.b2;
+  *reinterpret_cast<uint4*>(&Bs[row + 192][c]) = st.b3;
+}
+
+// One stage of a wave's 128 x 64 block: two 32-k steps of 8 x 4 MFMAs.
+__device__ __forceinline__ void lse_mma(const uint16_t (*As)[kLLd], const uint16_t (*Bs)[kLLd], int wm, int wn,
+                                        int li, int lq, f4v (&acc)[8][4]) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int idx = tid + kLThreads * i, row = idx >> 2, kq = idx & 3;
-    *reinterpret_cast<uint4*>(&As[row][8 * kq]) = ra[i];
-    *reinterpret_cast<uint4*>(&Bs[row][8 * kq]) = rb[i];
+  for (int kk = 0; kk < kLBK / 32; ++kk) {
+    bf16x8 bv[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      bv[t] = __builtin_bit_cast(bf16x8,
+                                 *reinterpret_cast<const uint4*>(&Bs[wn * 64 + t * 16 + li][32 * kk + 8 * lq]));
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      const bf16x8 av = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const uint4*>(&As[wm * 128 + mt * 16 + li][32 * kk + 8 * lq]));
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[nt], acc[mt][nt], 0, 0, 0);
+    }
   }
 }
 
@@ -614,37 +665,19 @@ __global__ void __launch_bounds__(kLThreads) k_lse(LseArgs a) {
 #pragma unroll
     for (int y = 0; y < 4; ++y) acc[x][y] = f4v{0.f, 0.f, 0.f, 0.f};
 
-  // K stages of 32: stage s is in LDS buffer s & 1 while the registers hold
-  // the next two stages' loads (set s & 1 is refilled with stage s + 2 as
-  // soon as stage s has gone to LDS), so a load has two stages of MFMA work
-  // to arrive in
+  // K stages of 64, double-buffered in LDS: the next stage's loads are in
+  // flight during a stage's 64 MFMAs per wave
   const int nst = a.D / kLBK;
-  uint4 ra[2][2], rb2[2][2];
-  lse_fetch(a, r0, v0, 0, tid, ra[0], rb2[0]);
-  if (nst > 1) lse_fetch(a, r0, v0, kLBK, tid, ra[1], rb2[1]);
-  lse_put(As[0], Bs[0], tid, ra[0], rb2[0]);
+  LseStage g = lse_fetch(a, r0, v0, 0, tid);
+  lse_put(As[0], Bs[0], tid, g);
   __syncthreads();
-  auto stage = [&](int s, auto phase) {
-    constexpr int P = decltype(phase)::value;  // s & 1
-    if (s + 2 < nst) lse_fetch(a, r0, v0, (s + 2) * kLBK, tid, ra[P], rb2[P]);
-    bf16x8 bv[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      bv[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&Bs[P][wn * 64 + t * 16 + li][8 * lq]));
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      const bf16x8 av =
-          __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&As[P][wm * 128 + mt * 16 + li][8 * lq]));
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[nt], acc[mt][nt], 0, 0, 0);
-    }
-    if (s + 1 < nst) lse_put(As[P ^ 1], Bs[P ^ 1], tid, ra[P ^ 1], rb2[P ^ 1]);
+  for (int s = 0; s < nst; ++s) {
+    const int cur = s & 1;
+    const bool more = s + 1 < nst;
+    if (more) g = lse_fetch(a, r0, v0, (s + 1) * kLBK, tid);
+    lse_mma(As[cur], Bs[cur], wm, wn, li, lq, acc);
+    if (more) lse_put(As[cur ^ 1], Bs[cur ^ 1], tid, g);
     __syncthreads();
-  };
-  for (int s = 0; s < nst; s += 2) {
-    stage(s, std::integral_constant<int, 0>{});
-    if (s + 1 < nst) stage(s + 1, std::integral_constant<int, 1>{});
   }
 
   // per row: max and sum of exp over this tile's columns (< V), the
@@ -892,7 +925,7 @@ void colsum(const float* A, const float* B, const float* rs, int rows, int cols,
   const int chunks = std::max(1, std::min(kColChunks, rows / 32));
   dim3 g1((cols + 255) / 256, chunks);
   hipLaunchKernelGGL(k_colsum_part, g1, dim3(256), 0, st, A, B, rs, rows, cols, part);
-  hipLaunchKernelGGL(k_colsum_fin, dim3((cols + 255) / 256), dim3(256), 0, st, part, chunks, cols, post, out);
+  hipLaunchKernelGGL(k_colsum_fin, dim3((cols + 63) / 64), dim3(256), 0, st, part, chunks, cols, post, out);
 }
 
 }  // namespace
