@@ -6,3 +6,4 @@ import this package.  The product path never does.
 from .oda_oracle import *  # noqa: F401,F403
 from . import oda_decoder_oracle as decoder  # noqa: F401
 from . import oda_train_oracle as train  # noqa: F401
+from . import oda_hybrid_oracle as hybrid  # noqa: F401
