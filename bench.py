@@ -71,6 +71,10 @@ def parse():
     ap.add_argument("--decoder-matrix", action="store_true",
                     help="decoder step at batch 1: context x forced recall-rate matrix, warm and first-request")
     ap.add_argument("--decoder-cell", default="", help=argparse.SUPPRESS)  # child process: CONTEXT:RATE, cold run
+    ap.add_argument("--hybrid", action="store_true",
+                    help="hybrid backbone: 6 attention layers on the ODA path between 18 recurrent (gated delta "
+                         "rule) layers whose states go through the save / restore / commit transaction; theta "
+                         "tuned to the pages' hybrid call rate, against always-full")
     ap.add_argument("--train", action="store_true",
                     help="one recall-head training step (labels through the tied LM head, then the head's "
                          "forward, Huber loss and backward) on a 4 x 2048-position micro-batch")
@@ -104,6 +108,11 @@ def main():
             print(json.dumps(decoder_cell(int(ctx), float(rate), args, stream, torch, cold=True)), flush=True)
         return
 
+    if args.hybrid:
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            hybrid_bench(args, stream, torch)
+        return
     if args.train:
         stream = torch.cuda.Stream()
         with torch.cuda.stream(stream):
@@ -821,6 +830,146 @@ def decoder_matrix(args):
     print(json.dumps({"matrix": "ODA decode tokens/s at batch 1 with the Qwen3-1.7B-shaped decoder backbone: "
                                 "context x forced rate", "steps": args.steps, "warmup": args.warmup,
                       "repeats": args.repeats, "cells": cells}), flush=True)
+
+
+HYBRID_PATTERN = "GGGA" * 6
+
+
+class HybridSession:
+    """The attention Session of the hybrid workload (6 attention layers)
+    plus the recurrent layers: the state pool with a seeded pre-step state in
+    slot 0, its pristine copy for resets, every step's recurrent inputs
+    resident in HBM, and one HybridPlan per step."""
+
+    def __init__(self, nsteps, stream, theta):
+        import torch
+        import synth
+        import conditional_sparse_attention_amd as C
+        from conditional_sparse_attention_amd.hybrid import GdnBuffers, HybridPlan
+        self.torch, self.C = torch, C
+        wl = synth.workloads()["hybrid"]
+        self.wl = wl
+        self.S = Session(wl, nsteps, stream, theta)
+        self.sh = synth.GdnShape(layers=18, batch=wl.batch, heads=16, seed=67)
+        sh = self.sh
+        self.gd = C.make_gdn_dims(sh.layers, sh.batch, sh.heads, sh.d, sh.conv_width)
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+        g0 = GdnBuffers.allocate(self.gd)
+        rec, conv = g0.views(self.gd)
+        for l in range(sh.layers):
+            for b in range(sh.batch):
+                S0, c0 = synth.gdn_initial_state(sh, l, b)
+                rec[l, b, 0] = dev(S0)
+                conv[l, b, 0] = dev(c0.view(np.int16))
+            g0.conv_w[l] = dev(synth.gdn_conv_weights(sh, l).view(np.int16))
+        self.pool0 = g0.state.clone()
+        Lg, B, H, Cc = sh.layers, sh.batch, sh.heads, sh.channels
+        z = lambda *s, dt=torch.int16: torch.zeros(s, dtype=dt, device="cuda")
+        self.xin = {k: z(nsteps, Lg, B, Cc) for k in ("xL", "xF")}
+        self.gin = {k: z(nsteps, Lg, B, H, dt=torch.float32) for k in ("aL", "bL", "aF", "bF")}
+        for j in range(nsteps):
+            for l in range(Lg):
+                for br, (xk, ak, bk) in enumerate((("xL", "aL", "bL"), ("xF", "aF", "bF"))):
+                    self.xin[xk][j, l] = dev(synth.gdn_x(sh, l, br, j).view(np.int16))
+                    a, bb = synth.gdn_gates(sh, l, br, j)
+                    self.gin[ak][j, l] = dev(a)
+                    self.gin[bk][j, l] = dev(bb)
+        self.g0 = g0
+        self.plans = []
+        for j in range(nsteps):
+            gj = dataclasses.replace(g0, xL=self.xin["xL"][j], xF=self.xin["xF"][j], aL=self.gin["aL"][j],
+                                     bL=self.gin["bL"][j], aF=self.gin["aF"][j], bF=self.gin["bF"][j])
+            self.plans.append(HybridPlan(self.S.plans[j], self.gd, gj, HYBRID_PATTERN, stream))
+        self.flag_all = self.S.flag_all
+        torch.cuda.synchronize()
+
+    def reset(self):
+        self.S.reset()
+        self.g0.state.copy_(self.pool0)
+        self.g0.slot.zero_()
+
+    def set_theta(self, theta):
+        self.S.set_theta(theta)
+
+    def always_full_step(self, j):
+        """Every sequence full: attention over S^F and the recurrent layers'
+        full pass for all, no local trial and no recall head."""
+        C, p, S = self.C, self.plans[j], self.S
+        dp = ctypes.byref(S.dims)
+        C.check(p.plan._lib.oda_worklist(dp, self.flag_all.data_ptr(), S.state.pos.data_ptr(), S.ws.data_ptr(),
+                                         S.ws.numel(), S.stream.cuda_stream), "oda_worklist")
+        fa = self.flag_all.data_ptr()
+        for f, args, name in p.full_calls:
+            if name == "oda_gdn_step":
+                args = tuple(list(args[:5]) + [fa] + list(args[6:]))
+            C.check(f(*args), name)
+        a = list(p.plan.commit_args)
+        a[3] = fa
+        C.check(p.plan._lib.oda_commit(*a), "oda_commit")
+        C.check(p._lib.oda_gdn_commit(p.gdn_commit_args[0], p.gdn_commit_args[1], fa, p.gdn_commit_args[3]),
+                "oda_gdn_commit")
+
+    def warm_ms(self, K, repeats, always_full=False):
+        graphs = self.S.capture((lambda j: self.always_full_step(j)) if always_full else
+                                (lambda j: self.plans[j].run()), K)
+        torch = self.torch
+        runs = []
+        for _ in range(repeats):
+            self.reset()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(self.S.stream)
+            for g in graphs:
+                g.replay()
+            e1.record(self.S.stream)
+            torch.cuda.synchronize()
+            runs.append(e0.elapsed_time(e1))
+        del graphs
+        return statistics.median(runs) / K
+
+
+def hybrid_bench(args, stream, torch):
+    """Hybrid backbone (6 attention + 18 recurrent layers, 8 sequences at
+    32K): theta tuned on an all-local pass to the pages' hybrid call rate,
+    then one graph per step, against always-full."""
+    K = args.steps
+    H = HybridSession(max(K, args.warmup, 1), stream, theta=math.inf)
+    S = H.S
+    H.reset()
+    scores = torch.zeros((K, H.wl.batch), dtype=torch.float32, device="cuda")
+    for j in range(K):
+        H.plans[j].run()
+        scores[j].copy_(S.state.score)
+    torch.cuda.synchronize()
+    sc = np.sort(scores.cpu().numpy().reshape(-1))[::-1]
+    k = int(round(H.wl.rate * sc.size))
+    theta = float((sc[k - 1] + sc[k]) / 2) if 0 < k < sc.size else (math.inf if k == 0 else -math.inf)
+    H.set_theta(theta)
+    H.reset()
+    flags = torch.zeros((K, H.wl.batch), dtype=torch.uint8, device="cuda")
+    for j in range(K):
+        H.plans[j].run()
+        flags[j].copy_(S.state.flag)
+    torch.cuda.synchronize()
+    realised = float(flags.float().mean().item())
+    assert S.error_bits() == 0, "device error bits set"
+    ms = H.warm_ms(K, args.repeats)
+    ms_af = H.warm_ms(K, args.repeats, always_full=True)
+    sh, wl = H.sh, H.wl
+    print(json.dumps({
+        "metric": "hybrid-backbone ODA decode steps/s (attention layers on the ODA path, recurrent-state "
+                  "transaction)",
+        "value": round(1e3 / ms, 2), "unit": "steps/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": "bf16 attention, fp32 recurrent state",
+        "data": "synthetic (seeded generator: KV cache, q/k/v and recurrent-layer inputs, random-init recall head)",
+        "config": {"workload": wl.name, "pattern": HYBRID_PATTERN, "attention_layers": wl.layers,
+                   "recurrent_layers": sh.layers, "batch": wl.batch, "context": int(wl.t0[0]),
+                   "gdn_heads": sh.heads, "head_dim": sh.d, "conv_width": sh.conv_width,
+                   "recall_rate_target": wl.rate, "recall_rate_realised": realised, "theta": theta,
+                   "tokens_per_s": round(1e3 / ms * wl.batch, 1), "timing": "hip-graph per step, median of repeats"},
+        "always_full": {"steps_per_s": round(1e3 / ms_af, 2), "ms_per_step": round(ms_af, 4),
+                        "oda_speedup": round(ms_af / ms, 3)},
+    }), flush=True)
 
 
 BF16_MFMA_PEAK_TFS = 2500.0   # MI355X dense bf16 matrix peak

@@ -1,4 +1,4 @@
-"""ctypes binding of liboda (include/oda.h, include/oda_decoder.h, include/oda_train.h).
+"""ctypes binding of liboda (include/oda.h, oda_decoder.h, oda_train.h, oda_hybrid.h).
 
 Argument marshalling only: every function takes torch tensors (or None for a
 nullable pointer), passes their device pointers and the current HIP stream
@@ -21,6 +21,7 @@ ODA_E_NULL, ODA_E_DIMS, ODA_E_UNSUPPORTED, ODA_E_WORKSPACE, ODA_E_LAYER, ODA_E_L
 ODA_KV_CONTIG, ODA_KV_PAGED = 0, 1
 ODA_ERR_CAPACITY, ODA_ERR_BLOCK, ODA_ERR_TOKEN, ODA_ERR_ROW = 1, 2, 4, 8
 ODA_DEC_LOCAL, ODA_DEC_FULL = 0, 1
+ODA_GDN_LOCAL, ODA_GDN_FULL, ODA_GDN_SLOTS = 0, 1, 3
 ODA_DEC_NTENSORS = 9
 ODA_HEAD_NTENSORS = 22
 ODA_FULL_MIN_CHUNK = 1024
@@ -33,6 +34,7 @@ EXPORTED = (
     "oda_dec_layer_numel", "oda_dec_layer_offsets", "oda_dec_workspace_bytes", "oda_dec_workspace_init",
     "oda_dec_embed", "oda_dec_layer", "oda_dec_final_norm", "oda_dec_next_token",
     "oda_train_workspace_bytes", "oda_train_workspace_init", "oda_train_labels", "oda_train_head_step",
+    "oda_gdn_state_bytes", "oda_gdn_conv_offset", "oda_gdn_step", "oda_gdn_commit",
 )
 
 
@@ -68,6 +70,11 @@ class oda_train_dims(ctypes.Structure):
                 ("sink", ctypes.c_int32), ("window", ctypes.c_int32), ("lam", ctypes.c_float)]
 
 
+class oda_gdn_dims(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("conv_width", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -82,6 +89,7 @@ def lib() -> ctypes.CDLL:
         vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
         dp, kp, ddp = ctypes.POINTER(oda_dims), ctypes.POINTER(oda_kv), ctypes.POINTER(oda_dec_dims)
         tdp = ctypes.POINTER(oda_train_dims)
+        gdp = ctypes.POINTER(oda_gdn_dims)
         sig = {
             "oda_abi_version": (ctypes.c_int, []),
             "oda_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -109,6 +117,10 @@ def lib() -> ctypes.CDLL:
             "oda_train_labels": (ctypes.c_int, [tdp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "oda_train_head_step": (ctypes.c_int, [tdp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                                    vp]),
+            "oda_gdn_state_bytes": (sz, [gdp]),
+            "oda_gdn_conv_offset": (sz, [gdp]),
+            "oda_gdn_step": (ctypes.c_int, [gdp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+            "oda_gdn_commit": (ctypes.c_int, [gdp, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -313,3 +325,30 @@ def oda_train_head_step(td, head_w, lm_head, h_local, h_full, tokens, prev, gain
     check(lib().oda_train_head_step(ctypes.byref(td), _p(head_w), _p(lm_head), _p(h_local), _p(h_full), _p(tokens),
                                     _p(prev), _p(gain), _p(label), _p(valid), _p(score), _p(loss), _p(grad), _p(ws),
                                     _bytes(ws), _s(stream)), "oda_train_head_step")
+
+
+# --------------------------------------------------------------------------
+# recurrent layers of a hybrid backbone (include/oda_hybrid.h)
+# --------------------------------------------------------------------------
+def make_gdn_dims(num_layers: int, batch: int, heads: int, head_dim: int = 128, conv_width: int = 4) -> oda_gdn_dims:
+    return oda_gdn_dims(num_layers=num_layers, batch=batch, heads=heads, head_dim=head_dim, conv_width=conv_width)
+
+
+def oda_gdn_state_bytes(gd: oda_gdn_dims) -> int:
+    n = int(lib().oda_gdn_state_bytes(ctypes.byref(gd)))
+    if n == 0:
+        raise OdaError(ODA_E_DIMS, "oda_gdn_state_bytes")
+    return n
+
+
+def oda_gdn_conv_offset(gd: oda_gdn_dims) -> int:
+    return int(lib().oda_gdn_conv_offset(ctypes.byref(gd)))
+
+
+def oda_gdn_step(gd, layer, branch, state, slot, flag, x, conv_w, alpha, beta, out, stream=None) -> None:
+    check(lib().oda_gdn_step(ctypes.byref(gd), layer, branch, _p(state), _p(slot), _p(flag), _p(x), _p(conv_w),
+                             _p(alpha), _p(beta), _p(out), _s(stream)), "oda_gdn_step")
+
+
+def oda_gdn_commit(gd, slot, flag, stream=None) -> None:
+    check(lib().oda_gdn_commit(ctypes.byref(gd), _p(slot), _p(flag), _s(stream)), "oda_gdn_commit")

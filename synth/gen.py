@@ -61,6 +61,11 @@ TAG_TRAIN_HL = 19              # training rows: local-branch final hidden states
 TAG_TRAIN_HF = 20              # training rows: full-branch final hidden states (rows that differ)
 TAG_TRAIN_TOK = 21             # training rows: token streams
 TAG_TRAIN_SEL = 22             # training rows: which rows' full state differs
+TAG_GDN_XL, TAG_GDN_XF = 23, 24  # recurrent layers: per-step q|k|v projection, local / full branch
+TAG_GDN_GATE = 25              # recurrent layers: per-step alpha, beta
+TAG_GDN_W = 26                 # recurrent layers: convolution weights
+TAG_GDN_S0 = 27                # recurrent layers: initial recurrent state
+TAG_GDN_C0 = 28                # recurrent layers: initial convolution state
 
 MAX_B = 32          # logical batch stride of the index space
 POS_BITS = 18       # logical position stride 2**18
@@ -198,6 +203,10 @@ def workloads() -> dict:
                     layout="paged", theta=0.0, bernoulli_odd=0.3, t_cap_slack=16)
     w["5-4k"] = Workload("paged-4k-b32", 28, 16, 8, 128, 32, np.full(32, 4096), 64, seed=6,
                          head_seed=106, layout="paged", theta=0.0, t_cap_slack=16)
+    # the attention layers of a hybrid backbone: 6 full-attention layers
+    # between 18 recurrent ones (GdnShape), at the pages' hybrid call rate
+    w["hybrid"] = Workload("hybrid-6attn-18gdn-32k-b8", 6, 16, 8, 128, 8, np.full(8, 32768), 64, seed=7,
+                           head_seed=107, rate=0.443)
     return w
 
 
@@ -552,3 +561,71 @@ def train_hidden(sh: TrainShape, rows=None):
     if np.any(dif):
         hf[dif] = bf16_at(sh.seed, TAG_TRAIN_HF, idx[dif])
     return hl, hf
+
+
+# --------------------------------------------------------------------------
+# recurrent layers of a hybrid backbone (gated delta rule decode layers)
+# --------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class GdnShape:
+    """Recurrent layers of a hybrid backbone: `layers` layers of `heads`
+    heads (d_k = d_v = d), causal convolution of width `conv_width` over the
+    3 H d channels of q | k | v.  `shared_layers` recurrent layers come
+    before the first attention layer: both branches see the same inputs
+    there."""
+    layers: int
+    batch: int
+    heads: int
+    d: int = 128
+    conv_width: int = 4
+    shared_layers: int = 3
+    seed: int = 61
+
+    @property
+    def channels(self) -> int:
+        return 3 * self.heads * self.d
+
+
+GDN_MAX_B = 1024
+
+
+def gdn_x(sh: GdnShape, layer: int, branch: int, step: int) -> np.ndarray:
+    """bf16 bits of the q|k|v projection [B][C] of one layer, branch, step."""
+    tag = TAG_GDN_XL if (branch == 0 or layer < sh.shared_layers) else TAG_GDN_XF
+    C = sh.channels
+    base = ((np.uint64(step) * np.uint64(sh.layers) + np.uint64(layer)) * np.uint64(GDN_MAX_B))
+    idx = ((base + np.arange(sh.batch, dtype=_U64))[:, None] * _U64(C) + np.arange(C, dtype=_U64)[None, :])
+    return bf16_at(sh.seed, tag, idx)
+
+
+def gdn_gates(sh: GdnShape, layer: int, branch: int, step: int):
+    """float32 alpha in [0.9, 1) and beta in [0.05, 0.95) [B][H]."""
+    br = 0 if layer < sh.shared_layers else branch
+    base = (((np.uint64(step) * np.uint64(sh.layers) + np.uint64(layer)) * _U64(2) + _U64(br)) * _U64(GDN_MAX_B))
+    idx = (base + np.arange(sh.batch, dtype=_U64))[:, None] * _U64(2 * sh.heads) + np.arange(2 * sh.heads,
+                                                                                              dtype=_U64)[None, :]
+    u = uniform_at(sh.seed, TAG_GDN_GATE, idx)
+    alpha = (0.9 + 0.1 * u[:, :sh.heads]).astype(np.float32)
+    beta = (0.05 + 0.9 * u[:, sh.heads:]).astype(np.float32)
+    return alpha, beta
+
+
+def gdn_conv_weights(sh: GdnShape, layer: int) -> np.ndarray:
+    """bf16 bits [C][W]: G's unit-variance values halved (exact in bf16)."""
+    n = sh.channels * sh.conv_width
+    idx = np.uint64(layer) * np.uint64(n) + np.arange(n, dtype=_U64)
+    v = bf16_bits_to_f32(bf16_at(sh.seed, TAG_GDN_W, idx)) * np.float32(0.5)
+    return f32_to_bf16_rne(v).reshape(sh.channels, sh.conv_width)
+
+
+def gdn_initial_state(sh: GdnShape, layer: int, b: int):
+    """fp32 recurrent state [H][d][d] (G's values / 4, exact) and bf16
+    convolution state [W-1][C] of sequence b before the first step."""
+    H, d, C = sh.heads, sh.d, sh.channels
+    n = H * d * d
+    base = (np.uint64(layer) * np.uint64(GDN_MAX_B) + np.uint64(b)) * np.uint64(n)
+    S = bf16_bits_to_f32(bf16_at(sh.seed, TAG_GDN_S0, base + np.arange(n, dtype=_U64))) * np.float32(0.25)
+    m = (sh.conv_width - 1) * C
+    cb = (np.uint64(layer) * np.uint64(GDN_MAX_B) + np.uint64(b)) * np.uint64(m)
+    conv = bf16_at(sh.seed, TAG_GDN_C0, cb + np.arange(m, dtype=_U64)).reshape(sh.conv_width - 1, C)
+    return S.reshape(H, d, d), conv
