@@ -7,12 +7,13 @@
 // A step is HBM-bound: each (sequence, head) reads its 128 x 128 fp32 state
 // (64 KB) from the committed slot and writes the updated one to the branch's
 // slot, 2 x 64 KB per head and layer, plus a few hundred bytes of inputs.
-// The grid is (4 row blocks, H, B); a workgroup first rebuilds the head's
-// q^, k^, v in LDS (convolution, SiLU, L2 norms; the row block 0 workgroup
-// also writes the new convolution state), then streams 32 rows of the state:
-// 16 lanes per row, 8 floats per lane, the row's two dot products summed
-// over the 16 lanes with DPP row operations.  The commit moves a per-sequence
-// slot index; no state is copied.
+// The grid is (4 row blocks, H, B); a workgroup issues the loads of its 32
+// state rows first, rebuilds the head's q^, k^, v in LDS meanwhile
+// (convolution, SiLU, L2 norms; the row block 0 workgroup also writes the
+// new convolution state), then updates the rows: 16 lanes per row, 8 floats
+// per lane, the row's two dot products summed over the 16 lanes with DPP row
+// operations.  The commit moves a per-sequence slot index; no state is
+// copied.
 #include <math.h>
 
 #include "oda_hybrid.h"
@@ -53,19 +54,35 @@ __global__ void __launch_bounds__(256) k_gdn_step(GdnArgs a) {
   const uint16_t* cs = a.conv + (lb * 3 + c) * (size_t)Wm1 * C;
   uint16_t* cd = a.conv + (lb * 3 + dst) * (size_t)Wm1 * C;
   const uint16_t* xb = a.x + (size_t)b * C;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 15, g = lane >> 4;
+  const size_t head_off = (size_t)h * kD * kD;
+  const float* Ss = a.S + (lb * 3 + c) * (size_t)a.H * kD * kD + head_off;
+  float* Sd = a.S + (lb * 3 + dst) * (size_t)a.H * kD * kD + head_off;
+  // this workgroup's state rows are loaded first: they do not depend on
+  // q, k, v, so their latency overlaps the convolution below
+  constexpr int kPasses = kRowsPerBlock / 16;
+  float4 rows[kPasses][2];
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int i = blk * kRowsPerBlock + pass * 16 + wave * 4 + g;
+    const float4* src = reinterpret_cast<const float4*>(Ss + (size_t)i * kD + 8 * li);
+    rows[pass][0] = src[0];
+    rows[pass][1] = src[1];
+  }
 
   // q, k, v of head h: channel ch of the head's 3 d -> group ch / d
   for (int ch = tid; ch < 3 * kD; ch += 256) {
-    const int g = ch / kD, i = ch % kD;
-    const int cc = g * Hd + h * kD + i;
+    const int grp = ch / kD, i = ch % kD;
+    const int cc = grp * Hd + h * kD + i;
     const uint16_t* wc = a.w + (size_t)cc * a.W;
     float y = 0.0f;
     for (int j = 0; j < Wm1; ++j) y += bf16_to_f32(wc[j]) * bf16_to_f32(cs[(size_t)j * C + cc]);
     const uint16_t xt = xb[cc];
     y += bf16_to_f32(wc[Wm1]) * bf16_to_f32(xt);
     const float v = silu_f(y);
-    if (g == 0) s_q[i] = v;
-    else if (g == 1) s_k[i] = v;
+    if (grp == 0) s_q[i] = v;
+    else if (grp == 1) s_k[i] = v;
     else s_v[i] = v;
     if (blk == 0) {
       for (int j = 0; j + 1 < Wm1; ++j) cd[(size_t)j * C + cc] = cs[(size_t)(j + 1) * C + cc];
@@ -76,7 +93,6 @@ __global__ void __launch_bounds__(256) k_gdn_step(GdnArgs a) {
   // |q|^2 and |k|^2, each over 128 values (threads 0..127 hold one of each)
   const float qv = tid < kD ? s_q[tid] : 0.0f, kv = tid < kD ? s_k[tid] : 0.0f;
   float sq = row16_sum(qv * qv), sk = row16_sum(kv * kv);
-  const int wave = tid >> 6, lane = tid & 63;
   // lanes 0, 16, 32, 48 of waves 0 and 1 hold the row sums of the first 128 threads
   sq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sq), 0)) +
        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sq), 16)) +
@@ -96,7 +112,6 @@ __global__ void __launch_bounds__(256) k_gdn_step(GdnArgs a) {
 
   // rows of the state: lanes 16 g .. 16 g + 15 of a wave take one row,
   // lane li its columns 8 li .. 8 li + 7
-  const int li = lane & 15, g = lane >> 4;
   float qh[8], kh[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -104,15 +119,11 @@ __global__ void __launch_bounds__(256) k_gdn_step(GdnArgs a) {
     kh[j] = s_k[8 * li + j] * rk;
   }
   const float al = a.alpha[(size_t)b * a.H + h], be = a.beta[(size_t)b * a.H + h];
-  const size_t head_off = (size_t)h * kD * kD;
-  const float* Ss = a.S + (lb * 3 + c) * (size_t)a.H * kD * kD + head_off;
-  float* Sd = a.S + (lb * 3 + dst) * (size_t)a.H * kD * kD + head_off;
   const float inv_sqrt_d = 1.0f / sqrtf((float)kD);
 #pragma unroll
-  for (int pass = 0; pass < kRowsPerBlock / 16; ++pass) {
+  for (int pass = 0; pass < kPasses; ++pass) {
     const int i = blk * kRowsPerBlock + pass * 16 + wave * 4 + g;
-    const float4* src = reinterpret_cast<const float4*>(Ss + (size_t)i * kD + 8 * li);
-    const float4 r0 = src[0], r1 = src[1];
+    const float4 r0 = rows[pass][0], r1 = rows[pass][1];
     float s[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
     float u = 0.0f;
 #pragma unroll
