@@ -122,3 +122,44 @@ def test_decoder_rejects_bad_arguments_before_launching():
     assert lib.oda_dec_layer(ctypes.byref(dd), 0, 0, None, None, None, None, None, None, None, None, None, 0, None,
                              0, None) == C.ODA_E_NULL
     assert lib.oda_dec_next_token(ctypes.byref(dd), None, None, None, None, None, None, None, 0, None) == C.ODA_E_NULL
+
+
+def test_train_entry_points_reject_bad_arguments_before_launching():
+    ok = C.make_train_dims(40, 2048, 151936)
+    assert C.oda_train_workspace_bytes(ok) > 0
+    for bad in (C.make_train_dims(0, 2048, 100), C.make_train_dims(70000, 2048, 100), C.make_train_dims(8, 100, 100),
+                C.make_train_dims(8, 2048, 0), C.make_train_dims(8, 2048, 100, lam=-0.5)):
+        with pytest.raises(C.OdaError):
+            C.oda_train_workspace_bytes(bad)
+    lib = C.lib()
+    td = ctypes.byref(ok)
+    fake = 1 << 20                          # never dereferenced: every call below returns before launching
+    assert lib.oda_train_labels(td, None, fake, fake, fake, fake, fake, fake, fake, fake, 1 << 40, None) == C.ODA_E_NULL
+    assert lib.oda_train_labels(td, fake + 2, fake, fake, fake, fake, fake, fake, fake, fake, 1 << 40,
+                                None) == C.ODA_E_DIMS                    # lm_head not 16-byte aligned
+    assert lib.oda_train_labels(td, fake, fake, fake, fake, fake, fake, fake, fake, fake, 0, None) == C.ODA_E_WORKSPACE
+    args = [fake] * 13
+    assert lib.oda_train_head_step(td, *args[:-1], None, 0, None) == C.ODA_E_NULL
+    assert lib.oda_train_head_step(td, fake + 4, *args[1:], 1 << 40, None) == C.ODA_E_DIMS
+    assert lib.oda_train_head_step(td, *args, 0, None) == C.ODA_E_WORKSPACE
+
+
+def test_gdn_entry_points_reject_bad_arguments_before_launching():
+    gd = C.make_gdn_dims(18, 8, 16)
+    L, B, H, d, W = 18, 8, 16, 128, 4
+    assert C.oda_gdn_state_bytes(gd) == L * B * 3 * H * d * d * 4 + L * B * 3 * (W - 1) * 3 * H * d * 2
+    assert C.oda_gdn_conv_offset(gd) == L * B * 3 * H * d * d * 4
+    for bad in (C.make_gdn_dims(18, 8, 16, head_dim=64), C.make_gdn_dims(18, 8, 16, conv_width=1),
+                C.make_gdn_dims(0, 8, 16), C.make_gdn_dims(18, 0, 16), C.make_gdn_dims(18, 8, 65)):
+        with pytest.raises(C.OdaError):
+            C.oda_gdn_state_bytes(bad)
+    lib = C.lib()
+    g = ctypes.byref(gd)
+    fake = 1 << 20
+    f7 = [fake] * 7
+    assert lib.oda_gdn_step(g, 0, 0, None, fake, None, *f7[:5], None) == C.ODA_E_NULL
+    assert lib.oda_gdn_step(g, 0, 2, fake, fake, fake, *f7[:5], None) == C.ODA_E_DIMS
+    assert lib.oda_gdn_step(g, 0, 1, fake, fake, None, *f7[:5], None) == C.ODA_E_NULL    # FULL needs flags
+    assert lib.oda_gdn_step(g, 18, 0, fake, fake, None, *f7[:5], None) == C.ODA_E_LAYER
+    assert lib.oda_gdn_step(g, 0, 0, fake + 8, fake, None, *f7[:5], None) == C.ODA_E_DIMS  # state not 16-byte aligned
+    assert lib.oda_gdn_commit(g, None, fake, None) == C.ODA_E_NULL
