@@ -7,12 +7,13 @@
 // A step is HBM-bound: each (sequence, head) reads its 128 x 128 fp32 state
 // (64 KB) from the committed slot and writes the updated one to the branch's
 // slot, 2 x 64 KB per head and layer, plus a few hundred bytes of inputs.
-// The grid is (4 row blocks, H, B); a workgroup issues the loads of its 32
-// state rows first, rebuilds the head's q^, k^, v in LDS meanwhile
-// (convolution, SiLU, L2 norms; the row block 0 workgroup also writes the
-// new convolution state), then updates the rows: 16 lanes per row, 8 floats
-// per lane, the row's two dot products summed over the 16 lanes with DPP row
-// operations.  The commit moves a per-sequence slot index; no state is
+// The grid is (8 row blocks, H, B).  A workgroup loads its channels'
+// convolution inputs, then issues the loads of its 16 state rows, rebuilds
+// the head's q^, k^, v in LDS while those are in flight (convolution, SiLU;
+// the row block 0 workgroup also writes the new convolution state; every
+// wave reduces the two L2 norms itself), then updates the rows: 16 lanes per
+// row, 8 floats per lane, the row's two dot products summed over the 16
+// lanes with DPP row operations.  The commit moves a per-sequence slot index; no state is
 // copied.
 #include <math.h>
 
@@ -23,7 +24,7 @@ namespace oda {
 namespace {
 
 constexpr int kD = 128;          // d_k = d_v
-constexpr int kRowBlocks = 4;    // workgroups per (sequence, head)
+constexpr int kRowBlocks = 8;    // workgroups per (sequence, head)
 constexpr int kRowsPerBlock = kD / kRowBlocks;
 constexpr float kNormEps = 1e-6f;
 
@@ -42,25 +43,42 @@ struct GdnArgs {
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + expf(-x)); }
 
-template <int BRANCH>
+template <int BRANCH, int W>
 __global__ void __launch_bounds__(256) k_gdn_step(GdnArgs a) {
   __shared__ float s_q[kD], s_k[kD], s_v[kD];
-  __shared__ float red[4];
   const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   if (BRANCH == ODA_GDN_FULL && a.flag[b] == 0) return;
   const int c = a.slot[b] % 3, dst = (c + 1 + BRANCH) % 3;
-  const int Hd = a.H * kD, C = a.C, Wm1 = a.W - 1;
+  const int Hd = a.H * kD, C = a.C;
   const size_t lb = (size_t)a.layer * a.B + b;
-  const uint16_t* cs = a.conv + (lb * 3 + c) * (size_t)Wm1 * C;
-  uint16_t* cd = a.conv + (lb * 3 + dst) * (size_t)Wm1 * C;
+  const uint16_t* cs = a.conv + (lb * 3 + c) * (size_t)(W - 1) * C;
+  uint16_t* cd = a.conv + (lb * 3 + dst) * (size_t)(W - 1) * C;
   const uint16_t* xb = a.x + (size_t)b * C;
   const int wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, g = lane >> 4;
   const size_t head_off = (size_t)h * kD * kD;
   const float* Ss = a.S + (lb * 3 + c) * (size_t)a.H * kD * kD + head_off;
   float* Sd = a.S + (lb * 3 + dst) * (size_t)a.H * kD * kD + head_off;
-  // this workgroup's state rows are loaded first: they do not depend on
-  // q, k, v, so their latency overlaps the convolution below
+
+  // 1. the convolution inputs of this thread's channels (ch = tid, tid + 256
+  // of the head's 3 d: q, k, v), first, so that the convolution waits for
+  // them alone
+  uint16_t wv[2][W], sv[2][W - 1], xt[2];
+  int ccs[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int ch = tid + 256 * u;
+    const int chc = ch < 3 * kD ? ch : 0;
+    const int cc = (chc / kD) * Hd + h * kD + chc % kD;
+    ccs[u] = cc;
+#pragma unroll
+    for (int j = 0; j < W; ++j) wv[u][j] = a.w[(size_t)cc * W + j];
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) sv[u][j] = cs[(size_t)j * C + cc];
+    xt[u] = xb[cc];
+  }
+  // 2. this workgroup's state rows: they do not depend on q, k, v, so their
+  // latency overlaps the convolution
   constexpr int kPasses = kRowsPerBlock / 16;
   float4 rows[kPasses][2];
 #pragma unroll
@@ -70,47 +88,46 @@ __global__ void __launch_bounds__(256) k_gdn_step(GdnArgs a) {
     rows[pass][0] = src[0];
     rows[pass][1] = src[1];
   }
-
-  // q, k, v of head h: channel ch of the head's 3 d -> group ch / d
-  for (int ch = tid; ch < 3 * kD; ch += 256) {
-    const int grp = ch / kD, i = ch % kD;
-    const int cc = grp * Hd + h * kD + i;
-    const uint16_t* wc = a.w + (size_t)cc * a.W;
-    float y = 0.0f;
-    for (int j = 0; j < Wm1; ++j) y += bf16_to_f32(wc[j]) * bf16_to_f32(cs[(size_t)j * C + cc]);
-    const uint16_t xt = xb[cc];
-    y += bf16_to_f32(wc[Wm1]) * bf16_to_f32(xt);
-    const float v = silu_f(y);
-    if (grp == 0) s_q[i] = v;
-    else if (grp == 1) s_k[i] = v;
-    else s_v[i] = v;
-    if (blk == 0) {
-      for (int j = 0; j + 1 < Wm1; ++j) cd[(size_t)j * C + cc] = cs[(size_t)(j + 1) * C + cc];
-      cd[(size_t)(Wm1 - 1) * C + cc] = xt;
+  // 3. convolution, SiLU; the row block 0 workgroup writes the new
+  // convolution state (s_1, ..., s_{W-2}, x_t)
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int ch = tid + 256 * u;
+    if (ch < 3 * kD) {
+      const int grp = ch / kD, i = ch % kD, cc = ccs[u];
+      float y = 0.0f;
+#pragma unroll
+      for (int j = 0; j < W - 1; ++j) y += bf16_to_f32(wv[u][j]) * bf16_to_f32(sv[u][j]);
+      y += bf16_to_f32(wv[u][W - 1]) * bf16_to_f32(xt[u]);
+      const float v = silu_f(y);
+      if (grp == 0) s_q[i] = v;
+      else if (grp == 1) s_k[i] = v;
+      else s_v[i] = v;
+      if (blk == 0) {
+#pragma unroll
+        for (int j = 0; j + 1 < W - 1; ++j) cd[(size_t)j * C + cc] = sv[u][j + 1];
+        cd[(size_t)(W - 2) * C + cc] = xt[u];
+      }
     }
   }
   __syncthreads();
-  // |q|^2 and |k|^2, each over 128 values (threads 0..127 hold one of each)
-  const float qv = tid < kD ? s_q[tid] : 0.0f, kv = tid < kD ? s_k[tid] : 0.0f;
-  float sq = row16_sum(qv * qv), sk = row16_sum(kv * kv);
-  // lanes 0, 16, 32, 48 of waves 0 and 1 hold the row sums of the first 128 threads
-  sq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sq), 0)) +
-       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sq), 16)) +
-       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sq), 32)) +
-       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sq), 48));
-  sk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sk), 0)) +
-       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sk), 16)) +
-       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sk), 32)) +
-       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sk), 48));
-  if (lane == 0 && wave < 2) {
-    red[wave] = sq;
-    red[2 + wave] = sk;
-  }
-  __syncthreads();
-  const float rq = 1.0f / sqrtf((red[0] + red[1]) + kNormEps);
-  const float rk = 1.0f / sqrtf((red[2] + red[3]) + kNormEps);
+  // |q|^2 and |k|^2 over the 128 LDS values, reduced by every wave itself
+  float sq = s_q[lane] * s_q[lane] + s_q[lane + 64] * s_q[lane + 64];
+  float sk = s_k[lane] * s_k[lane] + s_k[lane + 64] * s_k[lane + 64];
+  sq = row16_sum(sq);
+  sk = row16_sum(sk);
+  sq = (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(sq), 0)) +
+        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sq), 16))) +
+       (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(sq), 32)) +
+        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sq), 48)));
+  sk = (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(sk), 0)) +
+        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sk), 16))) +
+       (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(sk), 32)) +
+        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sk), 48)));
+  const float rq = 1.0f / sqrtf(sq + kNormEps);
+  const float rk = 1.0f / sqrtf(sk + kNormEps);
 
-  // rows of the state: lanes 16 g .. 16 g + 15 of a wave take one row,
+  // 4. rows of the state: lanes 16 g .. 16 g + 15 of a wave take one row,
   // lane li its columns 8 li .. 8 li + 7
   float qh[8], kh[8];
 #pragma unroll
@@ -142,6 +159,21 @@ __global__ void __launch_bounds__(256) k_gdn_step(GdnArgs a) {
     d4[1] = make_float4(s[4], s[5], s[6], s[7]);
     if (li == 0) a.out[((size_t)b * a.H + h) * kD + i] = f32_to_bf16(o * inv_sqrt_d);
   }
+}
+
+template <int BRANCH>
+int launch_gdn(const GdnArgs& a, dim3 grid, hipStream_t st) {
+  switch (a.W) {
+    case 2: hipLaunchKernelGGL((k_gdn_step<BRANCH, 2>), grid, dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((k_gdn_step<BRANCH, 3>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_gdn_step<BRANCH, 4>), grid, dim3(256), 0, st, a); break;
+    case 5: hipLaunchKernelGGL((k_gdn_step<BRANCH, 5>), grid, dim3(256), 0, st, a); break;
+    case 6: hipLaunchKernelGGL((k_gdn_step<BRANCH, 6>), grid, dim3(256), 0, st, a); break;
+    case 7: hipLaunchKernelGGL((k_gdn_step<BRANCH, 7>), grid, dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((k_gdn_step<BRANCH, 8>), grid, dim3(256), 0, st, a); break;
+    default: return ODA_E_UNSUPPORTED;
+  }
+  return ODA_OK;
 }
 
 __global__ void k_gdn_commit(uint8_t* slot, const uint8_t* flag, int B) {
@@ -206,11 +238,9 @@ int oda_gdn_step(const oda_gdn_dims* dims, int32_t layer, int32_t branch, void* 
   a.W = dims->conv_width;
   a.C = 3 * dims->heads * kD;
   dim3 grid(kRowBlocks, dims->heads, dims->batch);
-  if (branch == ODA_GDN_LOCAL) {
-    hipLaunchKernelGGL(k_gdn_step<ODA_GDN_LOCAL>, grid, dim3(256), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL(k_gdn_step<ODA_GDN_FULL>, grid, dim3(256), 0, stream, a);
-  }
+  const int st = branch == ODA_GDN_LOCAL ? launch_gdn<ODA_GDN_LOCAL>(a, grid, stream)
+                                         : launch_gdn<ODA_GDN_FULL>(a, grid, stream);
+  if (st != ODA_OK) return st;
   return hipGetLastError() == hipSuccess ? ODA_OK : ODA_E_LAUNCH;
 }
 

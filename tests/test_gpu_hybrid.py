@@ -126,12 +126,13 @@ def _step_and_check(pr, step, flags, seqs=None):
     return _check(pr, old_slot, before, flags, seqs)
 
 
-def test_transaction_small_three_steps():
+@pytest.mark.parametrize("width", [4, 2])
+def test_transaction_small_three_steps(width):
     """3 recurrent layers (the first shared by both branches), 5 sequences
     with committed slots 0, 1, 2, 0, 1, three steps with different flags:
     outputs, the committed state of each layer and the slot indices against
-    the oracle's save / restore / commit."""
-    sh = synth.GdnShape(layers=3, batch=5, heads=4, shared_layers=1, seed=71)
+    the oracle's save / restore / commit; convolution widths 4 and 2."""
+    sh = synth.GdnShape(layers=3, batch=5, heads=4, shared_layers=1, seed=71, conv_width=width)
     pr = GdnProblem(sh, [0, 1, 2, 0, 1])
     worst = 0.0
     for step, flags in enumerate(([1, 0, 1, 1, 0], [0, 0, 0, 0, 0], [1, 1, 1, 1, 1])):
