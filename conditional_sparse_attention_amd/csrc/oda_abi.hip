@@ -168,7 +168,7 @@ const char* oda_status_str(int status) {
     case ODA_OK: return "ok";
     case ODA_E_NULL: return "a required pointer is NULL";
     case ODA_E_DIMS: return "inconsistent or out-of-range dimensions";
-    case ODA_E_UNSUPPORTED: return "dimensions not supported by this build";
+    case ODA_E_UNSUPPORTED: return "dimensions not supported by liboda";
     case ODA_E_WORKSPACE: return "workspace smaller than oda_workspace_bytes()";
     case ODA_E_LAYER: return "layer index out of range";
     case ODA_E_LAUNCH: return "kernel launch failed";

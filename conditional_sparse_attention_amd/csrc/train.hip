@@ -887,7 +887,8 @@ int sgemm(Sg g, int splits, float* split_buf, hipStream_t st) {
   splits = (g.K + kc - 1) / kc;
   g.kchunk = kc;
   float* dst = g.C;
-  const int64_t ldc = g.ldc;
+  // split partials are summed into a contiguous destination (a gradient tensor)
+  if (splits > 1 && (EPI != kStore || g.ldc != g.N || ((int64_t)g.M * g.N) % 4 != 0)) return ODA_E_UNSUPPORTED;
   if (splits > 1) {
     g.C = split_buf;
     g.ldc = g.N;
@@ -896,8 +897,6 @@ int sgemm(Sg g, int splits, float* split_buf, hipStream_t st) {
   dim3 grid((g.N + kBN - 1) / kBN, (g.M + kBM - 1) / kBM, splits);
   hipLaunchKernelGGL((k_sgemm<AK, BK, EPI>), grid, dim3(256), 0, st, g);
   if (splits > 1) {
-    // the destination is contiguous (a gradient tensor)
-    if (ldc != g.N) return ODA_E_UNSUPPORTED;
     const int64_t n4 = (int64_t)g.M * g.N / 4;
     const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 4096);
     hipLaunchKernelGGL(k_split_sum, dim3(blocks), dim3(256), 0, st, split_buf, splits, g.split_stride, n4, dst);

@@ -65,7 +65,7 @@ extern "C" {
 #define ODA_OK 0
 #define ODA_E_NULL (-1)        /* a required pointer is NULL */
 #define ODA_E_DIMS (-2)        /* inconsistent or out-of-range dimensions */
-#define ODA_E_UNSUPPORTED (-3) /* valid but not supported by this build (head_dim != 128, B > 32, ...) */
+#define ODA_E_UNSUPPORTED (-3) /* valid but not supported by liboda (head_dim != 128, B > 32, ...) */
 #define ODA_E_WORKSPACE (-4)   /* ws_bytes smaller than oda_workspace_bytes(dims) */
 #define ODA_E_LAYER (-5)       /* layer index outside [0, num_layers) */
 #define ODA_E_LAUNCH (-6)      /* the HIP runtime rejected a kernel launch */

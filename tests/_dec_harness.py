@@ -9,7 +9,7 @@ h_prev and cache; after it, the oracle recomputes from that state
   * the recall score from the GPU's h_prev, E(x_t) and h^L, and the rule;
   * the full branch of every flagged sequence: staged K/V, h^F;
   * the logits of the GPU's chosen hidden state and their argmax;
-and compares (tolerances derived in the design doc):
+and compares (the tolerances follow from bf16 storage with fp32 accumulation):
   * h^L, h^F, staged K/V      |gpu - oracle| <= ATOL + RTOL |oracle|
   * scores                    |gpu - oracle| <= 1e-4 (1 + |oracle|)
   * flags                     bit-exact unless |q_oracle - theta| < 1e-3
