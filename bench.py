@@ -485,6 +485,18 @@ def rate_sweep(args, S):
     return {"points": res}
 
 
+def host_cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "" when unknown."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def cpu_baseline(wl, blob, theta, rate):
     """The oracle, untuned, on a bounded sample of the same workload: one
     layer of local attention for one sequence, the recall head for every
@@ -531,7 +543,7 @@ def cpu_baseline(wl, blob, theta, rate):
     step_s = L * B * t_local + t_head + rate * B * L * t_full
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": round(1.0 / step_s, 5), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "host_cpus": os.cpu_count(),
+            "host_cpus": os.cpu_count(), "cpu_model": host_cpu_model(),
             "sample": (f"step 0, layer {l}: local attention of sequence 0 ({t_local:.2f} s), recall head "
                        f"of all {B} ({t_head:.2f} s), full attention of sequence 0 over {t0 + 1} keys "
                        f"({t_full:.2f} s); scaled to {L} layers x {B} sequences and {rate:.3f}*{B} flagged "
@@ -1097,7 +1109,7 @@ def train_cpu_baseline(sh, E, blob, hl, hf, pos, prev, tok, nxt):
     step_s = N * (t_lab + t_head)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": round(N / step_s, 2), "unit": "positions/s", "cores": int(threads), "kind": "oracle",
-            "host_cpus": os.cpu_count(),
+            "host_cpus": os.cpu_count(), "cpu_model": host_cpu_model(),
             "sample": (f"labels of {nl} rows over {sh.vocab} vocabulary rows ({t_lab * nl:.2f} s), head forward "
                        f"and backward on {n} rows ({t_head * n:.2f} s); scaled to {N} rows"),
             "sample_cpu_s": round(t_lab * nl + t_head * n, 2)}
