@@ -190,3 +190,12 @@ def test_hybrid_step_with_the_head_deciding():
         seen.update(flags)
         _check(gp, old_slot, before, flags, range(3))
     assert seen == {0, 1}
+
+
+def test_one_sequence_one_head_widest_convolution():
+    """Degenerate sizes: one sequence, one head, one layer, convolution width
+    8 (the largest supported), committed slot 2, two steps."""
+    sh = synth.GdnShape(layers=1, batch=1, heads=1, shared_layers=0, seed=74, conv_width=8)
+    pr = GdnProblem(sh, [2])
+    for step, flags in enumerate(([1], [0])):
+        _step_and_check(pr, step, flags)

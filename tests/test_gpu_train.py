@@ -149,3 +149,25 @@ def test_full_size_step_sampled():
     valid = np.zeros(sh.rows, dtype=np.uint8)
     valid[rows] = 1
     _step_and_compare(pr, valid, rows)
+
+
+def test_single_row_and_single_token_vocabulary():
+    """Degenerate sizes: one row, and a one-row vocabulary (every log-probability
+    is 0, so the gain is exactly 0 and the label is -log(1 + lambda))."""
+    sh = _small_vocab_shape(vocab=1, rows_per_run=1, first_pos=5000, lam=0.25, seed=53, head_seed=153, embed_seed=253)
+    pr = TrainProblem(sh, nxt=np.zeros(1, np.int32), tok=np.zeros(1, np.int32))
+    pr.labels()
+    torch.cuda.synchronize()
+    assert float(pr.gain.item()) == 0.0
+    assert float(pr.label.item()) == pytest.approx(-np.log1p(0.25), abs=1e-6)
+    assert int(pr.valid.item()) == 1
+    _step_and_compare(pr)
+
+
+def test_single_row_full_head():
+    """One row through the full-size head and the full vocabulary."""
+    sh = dataclasses.replace(synth.train_shapes()["small"], runs=1, rows_per_run=1, first_pos=2100)
+    pr = TrainProblem(sh)
+    pr.labels()
+    check_labels(pr, [0])
+    _step_and_compare(pr)
