@@ -232,25 +232,28 @@ __device__ __forceinline__ void cache_rows(const AttnParams& P, const uint4 (&qv
   if (first >= p_hi) return;
   uint4 kk[DEPTH][U], vv[DEPTH][U];
   bool ok[DEPTH][U];
+  // This wave's stages are first + k * kStride for k < nst.  Every load is
+  // unconditional (rows past p_hi are clamped to p_hi - 1 and masked), so the
+  // same number of loads is outstanding at every wait and the wait before a
+  // stage is consumed leaves the DEPTH - 1 stages after it in flight; the
+  // scheduling barrier keeps each refill ahead of the next stage's arithmetic.
+  const int nst = (p_hi - first + kStride - 1) / kStride;
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) {
-    const int bs = first + d * kStride;
-    if (bs < p_hi) load_stage<PAGED, U>(P, Kbg, Vbg, b, g, bs, p_hi, r, c, kk[d], vv[d], ok[d]);
-  }
-  int cur = first;
-  bool done = false;
-  while (!done) {
+  for (int d = 0; d < DEPTH; ++d)
+    load_stage<PAGED, U>(P, Kbg, Vbg, b, g, first + d * kStride, p_hi, r, c, kk[d], vv[d], ok[d]);
+  int k = 0;
+  for (; k + DEPTH <= nst; k += DEPTH) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
-      if (!done) {
-        block_update<G, U>(qv, st, kk[d], vv[d], ok[d], P.scale_log2);
-        const int refill = cur + DEPTH * kStride;
-        if (refill < p_hi) load_stage<PAGED, U>(P, Kbg, Vbg, b, g, refill, p_hi, r, c, kk[d], vv[d], ok[d]);
-        cur += kStride;
-        done = cur >= p_hi;
-      }
+      block_update<G, U>(qv, st, kk[d], vv[d], ok[d], P.scale_log2);
+      load_stage<PAGED, U>(P, Kbg, Vbg, b, g, first + (k + d + DEPTH) * kStride, p_hi, r, c, kk[d], vv[d], ok[d]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  const int rem = nst - k;
+#pragma unroll
+  for (int d = 0; d + 1 < DEPTH; ++d)
+    if (d < rem) block_update<G, U>(qv, st, kk[d], vv[d], ok[d], P.scale_log2);
 }
 
 // The current token: one staged row, handled by wave 0 / row group 0.
