@@ -567,11 +567,6 @@ __device__ __forceinline__ const uint16_t* lse_row(const LseArgs& a, int r) {
   return r < a.N ? a.hL + (size_t)r * a.D : a.hF + (size_t)(r - a.N) * a.D;
 }
 
-// One stage: 256 hidden rows and 256 vocabulary rows of 32 k each (two
-// 16-byte pieces per thread and operand).  Rows past the ends are clamped to
-// the last row rather than skipped: their logits land in rows that are never
-// written and in columns the epilogue masks, and unconditional loads let the
-// compiler wait for exactly the stage it needs while later ones are in flight.
 // One stage: 256 hidden rows and 256 vocabulary rows of 64 k each, four
 // 16-byte pieces per thread and operand (rows idx / 8 + 64 j).  Named fields
 // rather than arrays keep the pieces in registers.  Rows past the ends are
