@@ -126,12 +126,13 @@ def _step_and_check(pr, step, flags, seqs=None):
     return _check(pr, old_slot, before, flags, seqs)
 
 
-@pytest.mark.parametrize("width", [4, 2])
+@pytest.mark.parametrize("width", [4, 2, 3, 6])
 def test_transaction_small_three_steps(width):
     """3 recurrent layers (the first shared by both branches), 5 sequences
     with committed slots 0, 1, 2, 0, 1, three steps with different flags:
     outputs, the committed state of each layer and the slot indices against
-    the oracle's save / restore / commit; convolution widths 4 and 2."""
+    the oracle's save / restore / commit; convolution widths 4 (the Qwen
+    hybrid family's), 2, 3 and 6."""
     sh = synth.GdnShape(layers=3, batch=5, heads=4, shared_layers=1, seed=71, conv_width=width)
     pr = GdnProblem(sh, [0, 1, 2, 0, 1])
     worst = 0.0
@@ -168,14 +169,17 @@ def test_full_size_sampled_sequences():
     print("worst state error / bound", round(worst, 4))
 
 
-def test_hybrid_step_with_the_head_deciding():
+@pytest.mark.parametrize("layout", ["contig", "paged"])
+def test_hybrid_step_with_the_head_deciding(layout):
     """The whole hybrid step through HybridPlan (pattern GGGA GGGA: 6
     recurrent and 2 attention layers, 3 sequences across the s + w
-    boundary): the attention path, rule, work list and KV commit against the
-    oracle as for the attention-only step, and the recurrent states against
-    the oracle's transaction under the flags the step took (forced full /
-    local at steps 0 and 1, decided by the head at steps 2 and 3)."""
-    wl = synth.Workload("hybrid-small", 2, 16, 8, 128, 3, np.array([60, 2100, 2600]), 4, seed=81, head_seed=181)
+    boundary), with a contiguous and a paged KV cache: the attention path,
+    rule, work list and KV commit against the oracle as for the
+    attention-only step, and the recurrent states against the oracle's
+    transaction under the flags the step took (forced full / local at steps
+    0 and 1, decided by the head at steps 2 and 3)."""
+    wl = synth.Workload("hybrid-small", 2, 16, 8, 128, 3, np.array([60, 2100, 2600]), 4, seed=81, head_seed=181,
+                        layout=layout)
     pr = Problem(wl)
     gp = GdnProblem(synth.GdnShape(layers=6, batch=3, heads=4, seed=82), [0, 1, 2])
     hp = HybridPlan(pr.plan, gp.gd, gp.g, "GGGAGGGA")
