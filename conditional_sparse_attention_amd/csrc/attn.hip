@@ -29,6 +29,8 @@
 // fixed persistent grid whose workgroups walk the device-side work list
 // written by the recall-score step, so the host never learns which
 // sequences were flagged.
+#include <atomic>
+
 #include "oda_internal.h"
 
 namespace oda {
@@ -601,16 +603,18 @@ __global__ void __launch_bounds__(FullWaves<G>::value * 64) k_attn_full(AttnPara
   }
 }
 
+// Compute units of the current device, queried once per device (host
+// threads may race on the first query; each stores the same value).
 int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 // Workgroups per (sequence, KV head) in the local branch: about four per
