@@ -408,6 +408,7 @@ def run(args, wl, stream, torch):
     out["setup_s"] = round(setup_s, 1)
     if args.rate_sweep:
         out["rate_sweep"] = rate_sweep(args, S)
+    out["device_copy"] = device_copy_gbs(torch, stream)
     if args.copy_calibration:
         src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
         dst = torch.empty_like(src)
@@ -432,6 +433,28 @@ def kernel_source_hash() -> str:
         with open(os.path.join(root, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def device_copy_gbs(torch, stream, n_bytes=1 << 30, reps=5):
+    """The box's achievable streaming rate for a plain read + write kernel:
+    a device-to-device copy of an n_bytes buffer (n_bytes read and n_bytes
+    written per copy), timed with HIP events on the bench's stream after
+    every timed region."""
+    src = torch.empty(n_bytes // 2, dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+    with torch.cuda.stream(stream):
+        dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            dst.copy_(src)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return {"gbs": round(2 * n_bytes / (ms * 1e-3) / 1e9, 1), "bytes_per_copy": 2 * n_bytes,
+            "note": "device-to-device copy of 1 GiB (read + write): the measured ceiling of a plain streaming kernel "
+                    "on this box, for reading roofline.frac"}
 
 
 def measured_traffic(bytes_per_launch):
