@@ -18,6 +18,24 @@ def bits(x):
     return f64_to_bf16(np.asarray(x, dtype=np.float64))
 
 
+
+def test_bf16_rounding_is_nearest_even():
+    """bf16 keeps 8 significand bits, so between 1 and 2 its spacing is
+    2^-7.  An exact midpoint goes to the neighbour with an even last bit,
+    anything off the midpoint to the nearer neighbour (decided on the float64
+    value, not on a float32 rounding of it), and the sign is symmetric."""
+    cases = {
+        1.0: 0x3F80,
+        1.0 + 2.0 ** -8: 0x3F80,                      # midpoint of 0x3F80 / 0x3F81 -> even
+        1.0 + 3 * 2.0 ** -8: 0x3F82,                  # midpoint of 0x3F81 / 0x3F82 -> even
+        1.0 + 2.0 ** -8 + 2.0 ** -30: 0x3F81,         # just above a midpoint
+        1.0 + 2.0 ** -8 - 2.0 ** -30: 0x3F80,         # just below it
+        -(1.0 + 3 * 2.0 ** -8): 0xBF82,
+        0.0: 0x0000,
+    }
+    for x, bits in cases.items():
+        assert int(f64_to_bf16(np.array([x]))[0]) == bits, (x, hex(bits))
+
 def test_backbone_size_matches_pages_ratio():
     """The pages put the recall head at about 1.7% of the backbone's
     parameters (ODA notes, §3.3 closing paragraph).  A Qwen3-1.7B-shaped

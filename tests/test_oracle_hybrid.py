@@ -3,6 +3,7 @@
 restored before the full retry, only the chosen update committed; §3.3: the
 recurrent layers keep their native computation).
 
+* SiLU and the L2 normalisation against closed forms.
 * The delta rule: a unit key written with alpha = beta = 1 reads back its
   value exactly; beta = 0 is pure decay; orthogonal keys keep separate
   values; the zero-state step has a closed form.
@@ -82,6 +83,20 @@ def _layer_inputs(rng, H, d):
     alpha = rng.uniform(0.8, 1.0, size=H)
     beta = rng.uniform(0.1, 0.9, size=H)
     return x, w, alpha, beta
+
+
+def test_silu_and_l2_norm_closed_forms():
+    """SiLU(x) = x sigma(x): SiLU(0) = 0, SiLU(ln 3) = (3/4) ln 3 and
+    SiLU(x) - SiLU(-x) = x.  The normalisation's epsilon sits inside the
+    square root: a vector with |x|^2 = eps maps to x / sqrt(2 eps)."""
+    assert HY.silu(np.float64(0.0)) == 0.0
+    assert math.isclose(float(HY.silu(np.float64(math.log(3.0)))), 0.75 * math.log(3.0), rel_tol=1e-15)
+    x = np.linspace(-6.0, 6.0, 25)
+    assert np.allclose(HY.silu(x) - HY.silu(-x), x, rtol=0.0, atol=1e-14)
+    e = HY.GDN_EPS
+    v = np.array([math.sqrt(e), 0.0])
+    assert np.allclose(HY.l2_normalise(v), v / math.sqrt(2.0 * e), rtol=1e-12, atol=0.0)
+    assert np.array_equal(HY.l2_normalise(np.zeros(3)), np.zeros(3))
 
 
 def test_zero_state_step_closed_form():
