@@ -84,8 +84,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "single-GPU build: this benchmark runs on one GPU only; "
-                                   "multi-GPU runs are not part of it", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the step is timed on one GPU's share "
+                                   "of the batch, and runs over several GPUs are not provided", "n_gpus": args.gpus}))
         sys.exit(2)
     if args.matrix:
         return matrix(args)
