@@ -215,12 +215,86 @@ __device__ __forceinline__ void load_stage(const AttnParams& P, const uint16_t* 
   }
 }
 
+// Decoder mode: what a lane needs to form its q / k dims, loaded with the raw
+// q rows before the cache stream starts: the two QK-norm gains (dims 8c ..
+// 8c+7) and the step's (cos, sin) for the 8 angles of those dims.
+struct RopeLane {
+  uint4 gq, gk;
+  uint4 cs[4];
+};
+
+__device__ __forceinline__ void rope_lane_load(const AttnParams& P, int b, int c, RopeLane& rl) {
+  rl.gq = *reinterpret_cast<const uint4*>(P.gq + 8 * c);
+  rl.gk = *reinterpret_cast<const uint4*>(P.gk + 8 * c);
+  const uint4* t = reinterpret_cast<const uint4*>(P.rope + (size_t)b * kHeadDim + 16 * (c & 7));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) rl.cs[j] = t[j];
+}
+
+// QK-norm and RoPE of one head vector held 8 dims per lane (lane c of a
+// 16-lane row holds dims 8c .. 8c+7): y = gamma x / sqrt(mean(x^2) + eps),
+// then each pair (i, i + d/2) rotated by the step's angle i: y_i cos -
+// y_{i+d/2} sin and y_{i+d/2} cos + y_i sin; rounded to bf16.  The partner
+// of a dim sits in lane c ^ 8.
+__device__ __forceinline__ uint4 norm_rope8(const uint4 raw, const uint4 gr, const uint4 (&cs)[4], int c, float eps) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[2 * j] = bf16lo(w[j]);
+    x[2 * j + 1] = bf16hi(w[j]);
+  }
+  float ss = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ss += x[j] * x[j];
+  ss = row16_sum(ss);
+  const float rs = rsqrtf(ss / (float)kHeadDim + eps);
+  const uint32_t gw[4] = {gr.x, gr.y, gr.z, gr.w};
+  float y[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    y[2 * j] = bf16lo(gw[j]) * x[2 * j] * rs;
+    y[2 * j + 1] = bf16hi(gw[j]) * x[2 * j + 1] * rs;
+  }
+  float t[16];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    t[4 * j] = __uint_as_float(cs[j].x);
+    t[4 * j + 1] = __uint_as_float(cs[j].y);
+    t[4 * j + 2] = __uint_as_float(cs[j].z);
+    t[4 * j + 3] = __uint_as_float(cs[j].w);
+  }
+  const bool first = c < 8;
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float v2[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int jj = 2 * j + e;
+      const float partner = __shfl_xor(y[jj], 8, 64);
+      const float co = t[2 * jj], si = t[2 * jj + 1];
+      v2[e] = first ? y[jj] * co - partner * si : y[jj] * co + partner * si;
+    }
+    o[j] = (uint32_t)f32_to_bf16(v2[0]) | ((uint32_t)f32_to_bf16(v2[1]) << 16);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Decoder mode: the G query heads of this lane, raw rows in, QK-normed and
+// rotated rows out.
+template <int G>
+__device__ __forceinline__ void rope_q(const AttnParams& P, uint4 (&qv)[G], const RopeLane& rl, int c) {
+#pragma unroll
+  for (int h = 0; h < G; ++h) qv[h] = norm_rope8(qv[h], rl.gq, rl.cs, c, P.qk_eps);
+}
+
 // Rows [p_lo, p_hi) of the cache.  Wave w takes stages starting at
 // p_lo + (k*NW + w) * 4U.  A ring of DEPTH register stages keeps DEPTH-1
 // stages in flight while one is consumed; its refill is issued right after.
-template <int G, bool PAGED, int NW, int DEPTH, int U>
-__device__ __forceinline__ void cache_rows(const AttnParams& P, const uint4 (&qv)[G], State<G>& st, int b, int g,
-                                           int p_lo, int p_hi, int wave, int r, int c) {
+template <int G, bool PAGED, int NW, int DEPTH, int U, bool ROPE>
+__device__ __forceinline__ void cache_rows(const AttnParams& P, uint4 (&qv)[G], bool& q_ready, const RopeLane& rl,
+                                           State<G>& st, int b, int g, int p_lo, int p_hi, int wave, int r, int c) {
   constexpr int kStage = 4 * U;
   constexpr int kStride = NW * kStage;
   const uint16_t* Kbg = P.K;
@@ -243,6 +317,13 @@ __device__ __forceinline__ void cache_rows(const AttnParams& P, const uint4 (&qv
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d)
     load_stage<PAGED, U>(P, Kbg, Vbg, b, g, first + d * kStride, p_hi, r, c, kk[d], vv[d], ok[d]);
+  // decoder mode: the raw q rows were loaded first; form q while the ring fills
+  if constexpr (ROPE) {
+    if (!q_ready) {
+      rope_q<G>(P, qv, rl, c);
+      q_ready = true;
+    }
+  }
   int k = 0;
   for (; k + DEPTH <= nst; k += DEPTH) {
 #pragma unroll
@@ -258,16 +339,30 @@ __device__ __forceinline__ void cache_rows(const AttnParams& P, const uint4 (&qv
     if (d < rem) block_update<G, U>(qv, st, kk[d], vv[d], ok[d], P.scale_log2);
 }
 
-// The current token: one staged row, handled by wave 0 / row group 0.
-template <int G>
-__device__ __forceinline__ void current_row(const AttnParams& P, const uint4 (&qv)[G], State<G>& st, int b, int g,
-                                            int wave, int r, int c) {
+// The current token: one staged row, handled by wave 0 / row group 0.  In
+// decoder mode the row is formed here from the raw projection and written to
+// the staging buffers, which the commit reads.
+template <int G, bool ROPE>
+__device__ __forceinline__ void current_row(const AttnParams& P, const uint4 (&qv)[G], const RopeLane& rl,
+                                            State<G>& st, int b, int g, int wave, int r, int c) {
   if (wave != 0) return;
   uint4 kk[1], vv[1];
   bool ok[1];
   const size_t base = ((size_t)b * P.Hkv + g) * kHeadDim + c * 8;
-  kk[0] = *reinterpret_cast<const uint4*>(P.kc + base);
-  vv[0] = *reinterpret_cast<const uint4*>(P.vc + base);
+  if constexpr (ROPE) {
+    const size_t nh = (size_t)P.Hq + 2 * P.Hkv;
+    const uint16_t* row = P.kc + (size_t)b * nh * kHeadDim + c * 8;
+    kk[0] = norm_rope8(*reinterpret_cast<const uint4*>(row + ((size_t)P.Hq + g) * kHeadDim), rl.gk, rl.cs, c,
+                       P.qk_eps);
+    vv[0] = *reinterpret_cast<const uint4*>(row + ((size_t)P.Hq + P.Hkv + g) * kHeadDim);
+    if (r == 0) {
+      *reinterpret_cast<uint4*>(P.k_stage + base) = kk[0];
+      *reinterpret_cast<uint4*>(P.v_stage + base) = vv[0];
+    }
+  } else {
+    kk[0] = *reinterpret_cast<const uint4*>(P.kc + base);
+    vv[0] = *reinterpret_cast<const uint4*>(P.vc + base);
+  }
   ok[0] = (r == 0);
   block_update<G, 1>(qv, st, kk, vv, ok, P.scale_log2);
 }
@@ -469,7 +564,7 @@ __device__ __forceinline__ void merge_partials(const AttnParams& P, const float*
 // One unit: keys of S with virtual indices [v_lo, v_hi) where S = [0, n0)
 // followed by [s1, t); the last virtual index (n0 + t - s1 - 1) is the
 // current token and is read from staging.
-template <int G, bool PAGED, int NW, int DEPTH, int U, int MAXS>
+template <int G, bool PAGED, int NW, int DEPTH, int U, int MAXS, bool ROPE>
 __device__ void attn_unit(const AttnParams& P, int b, int g, int split, int nsplit, int v_lo, int v_hi,
                           const LocalSet& S, int32_t* ticket, float* part_bg, float* lds) {
   const int tid = threadIdx.x;
@@ -478,10 +573,16 @@ __device__ void attn_unit(const AttnParams& P, int b, int g, int split, int nspl
   const int r = lane >> 4;
   const int c = lane & 15;
 
+  // decoder mode loads the raw rows here and forms q once the first stages
+  // of the ring are in flight (q_ready)
   uint4 qv[G];
+  bool q_ready = !ROPE;
+  const size_t q_row = ROPE ? (size_t)b * (P.Hq + 2 * P.Hkv) : (size_t)b * P.Hq;
 #pragma unroll
   for (int h = 0; h < G; ++h)
-    qv[h] = *reinterpret_cast<const uint4*>(P.q + ((size_t)b * P.Hq + g * G + h) * kHeadDim + c * 8);
+    qv[h] = *reinterpret_cast<const uint4*>(P.q + (q_row + g * G + h) * kHeadDim + c * 8);
+  RopeLane rl;
+  if constexpr (ROPE) rope_lane_load(P, b, c, rl);
 
   State<G> st;
 #pragma unroll
@@ -498,14 +599,20 @@ __device__ void attn_unit(const AttnParams& P, int b, int g, int split, int nspl
   // first range [0, n0) -> positions equal virtual indices
   if (v_lo < S.n0) {
     const int hi = v_cache_hi < S.n0 ? v_cache_hi : S.n0;
-    if (hi > v_lo) cache_rows<G, PAGED, NW, DEPTH, U>(P, qv, st, b, g, v_lo, hi, wave, r, c);
+    if (hi > v_lo) cache_rows<G, PAGED, NW, DEPTH, U, ROPE>(P, qv, q_ready, rl, st, b, g, v_lo, hi, wave, r, c);
   }
   // second range: virtual n0 + k  ->  position s1 + k
   {
     const int lo = v_lo > S.n0 ? v_lo : S.n0;
-    if (v_cache_hi > lo) cache_rows<G, PAGED, NW, DEPTH, U>(P, qv, st, b, g, S.s1 + (lo - S.n0), S.s1 + (v_cache_hi - S.n0), wave, r, c);
+    if (v_cache_hi > lo) cache_rows<G, PAGED, NW, DEPTH, U, ROPE>(P, qv, q_ready, rl, st, b, g, S.s1 + (lo - S.n0), S.s1 + (v_cache_hi - S.n0), wave, r, c);
   }
-  if (has_current) current_row<G>(P, qv, st, b, g, wave, r, c);
+  if constexpr (ROPE) {
+    if (!q_ready) {  // this wave streamed no cache rows
+      rope_q<G>(P, qv, rl, c);
+      q_ready = true;
+    }
+  }
+  if (has_current) current_row<G, ROPE>(P, qv, rl, st, b, g, wave, r, c);
 
   wg_merge<G, NW>(st, lds, wave, lane, c);
 
@@ -547,7 +654,7 @@ constexpr int lds_floats() {
   return a > b ? a : b;
 }
 
-template <int G, bool PAGED>
+template <int G, bool PAGED, bool ROPE>
 __global__ void __launch_bounds__(kLocalWaves * 64) k_attn_local(AttnParams P) {
   constexpr int NW = kLocalWaves;
   __shared__ float lds[lds_floats<G, NW>()];
@@ -567,7 +674,7 @@ __global__ void __launch_bounds__(kLocalWaves * 64) k_attn_local(AttnParams P) {
   const int v_lo = split * chunk;
   const int v_hi = (v_lo + chunk) < n ? v_lo + chunk : n;
   float* part_bg = P.part + ((size_t)(b * P.Hkv + g) * kLocalMaxSplits) * G * kPartStride;
-  attn_unit<G, PAGED, NW, ODA_LOCAL_DEPTH, ODA_LOCAL_U, kLocalSplitsMax>(P, b, g, split, ns, v_lo, v_hi, S, P.tickets + b * P.Hkv + g, part_bg, lds);
+  attn_unit<G, PAGED, NW, ODA_LOCAL_DEPTH, ODA_LOCAL_U, kLocalSplitsMax, ROPE>(P, b, g, split, ns, v_lo, v_hi, S, P.tickets + b * P.Hkv + g, part_bg, lds);
 }
 
 template <int G, bool PAGED>
@@ -599,7 +706,7 @@ __global__ void __launch_bounds__(FullWaves<G>::value * 64) k_attn_full(AttnPara
     S.s1 = t;
     S.t = t;
     float* part_bg = P.part + ((size_t)(b * P.Hkv + g) * kFullMaxSplits) * G * kPartStride;
-    attn_unit<G, PAGED, NW, FullDepth<G>::value, ODA_FULL_U, kFullMaxSplits>(P, b, g, split, ns, v_lo, v_hi, S, P.tickets + b * P.Hkv + g, part_bg, lds);
+    attn_unit<G, PAGED, NW, FullDepth<G>::value, ODA_FULL_U, kFullMaxSplits, false>(P, b, g, split, ns, v_lo, v_hi, S, P.tickets + b * P.Hkv + g, part_bg, lds);
   }
 }
 
@@ -629,13 +736,13 @@ int local_splits(const AttnParams& p) {
   return ns < kLocalSplitsMin ? kLocalSplitsMin : (ns > kLocalSplitsMax ? kLocalSplitsMax : ns);
 }
 
-template <int G, bool PAGED>
+template <int G, bool PAGED, bool ROPE>
 int launch_local_t(const AttnParams& p_in, hipStream_t s) {
   static_assert(kLocalSplitsMax <= kLocalMaxSplits, "local splits exceed the workspace slots");
   AttnParams p = p_in;
   p.local_splits = local_splits(p);
   dim3 grid(p.local_splits, p.Hkv, p.B);
-  hipLaunchKernelGGL((k_attn_local<G, PAGED>), grid, dim3(kLocalWaves * 64), 0, s, p);
+  hipLaunchKernelGGL((k_attn_local<G, PAGED, ROPE>), grid, dim3(kLocalWaves * 64), 0, s, p);
   return hipGetLastError() == hipSuccess ? ODA_OK : ODA_E_LAUNCH;
 }
 
@@ -654,13 +761,21 @@ int launch_full_t(const AttnParams& p, hipStream_t s) {
 
 }  // namespace
 
-int launch_local_attn(const AttnParams& p, int G, bool paged, hipStream_t s) {
+namespace {
+template <bool ROPE>
+int launch_local_g(const AttnParams& p, int G, bool paged, hipStream_t s) {
   switch (G) {
-    case 1: return paged ? launch_local_t<1, true>(p, s) : launch_local_t<1, false>(p, s);
-    case 2: return paged ? launch_local_t<2, true>(p, s) : launch_local_t<2, false>(p, s);
-    case 4: return paged ? launch_local_t<4, true>(p, s) : launch_local_t<4, false>(p, s);
+    case 1: return paged ? launch_local_t<1, true, ROPE>(p, s) : launch_local_t<1, false, ROPE>(p, s);
+    case 2: return paged ? launch_local_t<2, true, ROPE>(p, s) : launch_local_t<2, false, ROPE>(p, s);
+    case 4: return paged ? launch_local_t<4, true, ROPE>(p, s) : launch_local_t<4, false, ROPE>(p, s);
     default: return ODA_E_UNSUPPORTED;
   }
+}
+
+}  // namespace
+
+int launch_local_attn(const AttnParams& p, int G, bool paged, hipStream_t s, bool rope) {
+  return rope ? launch_local_g<true>(p, G, paged, s) : launch_local_g<false>(p, G, paged, s);
 }
 
 int launch_full_attn(const AttnParams& p, int G, bool paged, hipStream_t s) {

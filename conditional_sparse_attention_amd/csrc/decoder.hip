@@ -291,7 +291,7 @@ __global__ void __launch_bounds__(NW * 64) k_gemm16(GemmArgs A) {
   }
 }
 
-// ---- per-head QK-norm + RoPE; the v heads are copied.  grid (Hq + 2 Hkv, B), one wave.
+// ---- per-head QK-norm + RoPE (the full branch); the v heads are copied.  grid (Hq + 2 Hkv, B), one wave.
 struct RopeArgs {
   const uint16_t* qkv;   // [B][(Hq + 2 Hkv) d]
   const uint16_t* gq;    // [d]
@@ -332,6 +332,19 @@ __global__ void __launch_bounds__(64) k_qk_rope(RopeArgs A) {
   uint16_t* dst = isq ? A.q + ((size_t)b * A.Hq + h) * d : A.k + ((size_t)b * A.Hkv + (h - A.Hq)) * d;
   dst[i] = f32_to_bf16(y1 * c - y2 * sn);
   dst[i + half] = f32_to_bf16(y2 * c + y1 * sn);
+}
+
+// ---- the step's RoPE table: (cos, sin) of pos_b * theta^(-2i/d) for i < d/2,
+// per sequence, read by the local attention kernel's QK-norm + RoPE.  The angle is
+// formed in double: positions reach 1e5 and more, past fp32's resolution.
+// grid (B), d/2 threads.
+__global__ void __launch_bounds__(64) k_rope_table(const int32_t* pos, double theta, float* cs) {
+  constexpr int half = kHeadDim / 2;
+  const int b = blockIdx.x, i = threadIdx.x;
+  const double ang = (double)pos[b] * pow(theta, -2.0 * (double)i / (double)kHeadDim);
+  float* t = cs + ((size_t)b * half + i) * 2;
+  t[0] = (float)cos(ang);
+  t[1] = (float)sin(ang);
 }
 
 // ---- token embedding: x rows (fp32) and the head's E(x_t) (bf16).  grid (B)
@@ -453,7 +466,7 @@ bool dec_derive(const oda_dec_dims* dd, DecDerived* o, int* st) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct DecWs {
-  size_t qkv, act, part, tickets, cand_v, cand_i, total;
+  size_t qkv, act, part, tickets, cand_v, cand_i, rope, total;
 };
 
 // Shape of one GEMM launch: row tiles per workgroup, waves per workgroup,
@@ -501,6 +514,8 @@ DecWs dec_ws(const DecDerived& g) {
   at = align256(at + (size_t)(g.V / 64) * g.B * sizeof(float));
   w.cand_i = at;
   at = align256(at + (size_t)(g.V / 64) * g.B * sizeof(int32_t));
+  w.rope = at;
+  at = align256(at + (size_t)g.B * kHeadDim * sizeof(float));
   w.total = at;
   return w;
 }
@@ -636,27 +651,38 @@ int oda_dec_layer(const oda_dec_dims* dims, int32_t layer, int32_t branch, const
   a.N = g.nqkv;
   a.K = g.D;
   if ((st = launch_gemm<kQkv, 1>(a, shape_qkv(g), stream)) != ODA_OK) return st;
-  // QK-norm + RoPE, v copy: the branch's staged current key / value
-  RopeArgs r{};
-  r.qkv = qkv;
-  r.gq = wl + g.offs[2];
-  r.gk = wl + g.offs[3];
-  r.pos = pos;
-  r.q = q;
-  r.k = k_cur;
-  r.v = v_cur;
-  r.skip = skip;
-  r.Hq = g.Hq;
-  r.Hkv = g.Hkv;
-  r.eps = dims->eps;
-  r.theta = (double)dims->rope_theta;
-  hipLaunchKernelGGL(k_qk_rope, dim3(g.Hq + 2 * g.Hkv, g.B), dim3(64), 0, stream, r);
-  if (hipGetLastError() != hipSuccess) return ODA_E_LAUNCH;
-  // attention of the branch (the ODA path)
-  st = branch == ODA_DEC_LOCAL
-           ? oda_local_attn(&dims->attn, layer, kv, pos, q, k_cur, v_cur, o, nullptr, attn_ws, attn_ws_bytes, stream)
-           : oda_full_attn_if(&dims->attn, layer, kv, pos, q, k_cur, v_cur, o, nullptr, attn_ws, attn_ws_bytes,
-                              stream);
+  // attention of the branch (the ODA path).  The local branch runs the
+  // attention in decoder mode: its kernel applies the QK-norm and RoPE to the
+  // raw q / k rows and stages the current key / value, from the step's RoPE
+  // table, which layer 0 writes.  The full branch's persistent kernel walks
+  // several units per workgroup, each of which would redo that work, so it
+  // keeps a separate QK-norm + RoPE launch.
+  if (branch == ODA_DEC_LOCAL) {
+    float* rope = reinterpret_cast<float*>(dw + W.rope);
+    if (layer == 0) {
+      hipLaunchKernelGGL(k_rope_table, dim3(g.B), dim3(kHeadDim / 2), 0, stream, pos, (double)dims->rope_theta, rope);
+      if (hipGetLastError() != hipSuccess) return ODA_E_LAUNCH;
+    }
+    st = decoder_local_attn(&dims->attn, layer, kv, pos, qkv, wl + g.offs[2], wl + g.offs[3], rope, dims->eps, k_cur,
+                            v_cur, o, attn_ws, attn_ws_bytes, stream);
+  } else {
+    RopeArgs r{};
+    r.qkv = qkv;
+    r.gq = wl + g.offs[2];
+    r.gk = wl + g.offs[3];
+    r.pos = pos;
+    r.q = q;
+    r.k = k_cur;
+    r.v = v_cur;
+    r.skip = skip;
+    r.Hq = g.Hq;
+    r.Hkv = g.Hkv;
+    r.eps = dims->eps;
+    r.theta = (double)dims->rope_theta;
+    hipLaunchKernelGGL(k_qk_rope, dim3(g.Hq + 2 * g.Hkv, g.B), dim3(64), 0, stream, r);
+    if (hipGetLastError() != hipSuccess) return ODA_E_LAUNCH;
+    st = oda_full_attn_if(&dims->attn, layer, kv, pos, q, k_cur, v_cur, o, nullptr, attn_ws, attn_ws_bytes, stream);
+  }
   if (st != ODA_OK) return st;
   // output projection + residual
   a.W0 = wl + g.offs[4];

@@ -155,6 +155,24 @@ static int check_attn_args(const oda_dims* d, int32_t layer, const oda_kv* kv, c
   return ODA_OK;
 }
 
+int decoder_local_attn(const ::oda_dims* d, int32_t layer, const ::oda_kv* kv, const int32_t* pos,
+                       const uint16_t* qkv, const uint16_t* gq, const uint16_t* gk, const float* rope, float qk_eps,
+                       uint16_t* k_stage, uint16_t* v_stage, uint16_t* out, void* ws, size_t ws_bytes,
+                       hipStream_t s) {
+  WsLayout L;
+  const int st = check_attn_args(d, layer, kv, pos, qkv, k_stage, v_stage, out, ws, ws_bytes, &L);
+  if (st != ODA_OK) return st;
+  if (gq == nullptr || gk == nullptr || rope == nullptr) return ODA_E_NULL;
+  AttnParams p = attn_params(d, layer, kv, pos, qkv, qkv, qkv, out, nullptr, ws, L, false);
+  p.gq = gq;
+  p.gk = gk;
+  p.rope = rope;
+  p.k_stage = k_stage;
+  p.v_stage = v_stage;
+  p.qk_eps = qk_eps;
+  return launch_local_attn(p, d->num_q_heads / d->num_kv_heads, d->kv_layout == ODA_KV_PAGED, s, true);
+}
+
 }  // namespace oda
 
 using namespace oda;

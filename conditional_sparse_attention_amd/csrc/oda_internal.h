@@ -72,10 +72,29 @@ struct AttnParams {
   int64_t t_max;
   float scale_log2;         // log2(e) / sqrt(d)
   int32_t local_splits;     // local branch: workgroups per (sequence, KV head), set at launch
+  // Decoder mode only (the local kernel's ROPE instantiation): q and kc point
+  // at the raw projection rows [B][(Hq + 2 Hkv) d] (q heads, then k, then v),
+  // the kernel applies the QK-norm (gains gq / gk, epsilon qk_eps) and RoPE
+  // from the step's table rope [B][d/2][2] (cos, sin), and the workgroup
+  // holding the current token writes the staged key / value [B][Hkv][d] to
+  // k_stage / v_stage.
+  const uint16_t* gq;
+  const uint16_t* gk;
+  const float* rope;
+  uint16_t* k_stage;
+  uint16_t* v_stage;
+  float qk_eps;
 };
 
-int launch_local_attn(const AttnParams& p, int G, bool paged, hipStream_t s);
+int launch_local_attn(const AttnParams& p, int G, bool paged, hipStream_t s, bool rope = false);
 int launch_full_attn(const AttnParams& p, int G, bool paged, hipStream_t s);
+
+// The decoder's local attention call: the ODA local branch of one layer in
+// decoder mode (see AttnParams).  Checks its arguments as oda_local_attn does.
+int decoder_local_attn(const ::oda_dims* d, int32_t layer, const ::oda_kv* kv, const int32_t* pos,
+                       const uint16_t* qkv, const uint16_t* gq, const uint16_t* gk, const float* rope, float qk_eps,
+                       uint16_t* k_stage, uint16_t* v_stage, uint16_t* out, void* ws, size_t ws_bytes,
+                       hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // commit / ranges / init
