@@ -77,16 +77,21 @@ constexpr int kLocalSplitsMax = 8;
 #endif
 constexpr int kLocalWaves = ODA_LOCAL_WAVES;  // local kernel workgroup
 // Full kernel shape per group size: G = 2 (the 16/8-head models) runs 12
-// waves (3 per SIMD) with a 2-stage ring; G = 1 and G = 4 keep more state per
+// waves (3 per SIMD) with a 3-stage ring; G = 1 and G = 4 keep more state per
 // lane and run 8 waves with a 4-stage ring, which keeps a similar number of
-// bytes in flight per CU without spilling.
+// bytes in flight per CU without spilling (FullDepth: one stage less for the
+// paged layout).
 template <int G>
 struct FullWaves {
   static constexpr int value = G == 2 ? ODA_FULL_WAVES_SMALL_G : 8;
 };
-template <int G>
+// The paged layout keeps a block-table row and an address per stage and row
+// in flight as well; a shallower ring there avoids spilling (G = 2: 2 stages,
+// 7% faster per launch than 3 with spills on a paged 4K batch of 32; G = 1
+// and 4: 3 stages).
+template <int G, bool PAGED>
 struct FullDepth {
-  static constexpr int value = G == 2 ? ODA_FULL_DEPTH : 4;
+  static constexpr int value = PAGED ? (G == 2 ? 2 : 3) : (G == 2 ? ODA_FULL_DEPTH : 4);
 };
 
 __device__ __forceinline__ float dot8_bf16(const uint4 a, const uint4 b) {
@@ -706,7 +711,7 @@ __global__ void __launch_bounds__(FullWaves<G>::value * 64) k_attn_full(AttnPara
     S.s1 = t;
     S.t = t;
     float* part_bg = P.part + ((size_t)(b * P.Hkv + g) * kFullMaxSplits) * G * kPartStride;
-    attn_unit<G, PAGED, NW, FullDepth<G>::value, ODA_FULL_U, kFullMaxSplits, false>(P, b, g, split, ns, v_lo, v_hi, S, P.tickets + b * P.Hkv + g, part_bg, lds);
+    attn_unit<G, PAGED, NW, FullDepth<G, PAGED>::value, ODA_FULL_U, kFullMaxSplits, false>(P, b, g, split, ns, v_lo, v_hi, S, P.tickets + b * P.Hkv + g, part_bg, lds);
   }
 }
 
