@@ -54,26 +54,36 @@ def close_report(gpu_bits, ref_bits, what):
 
 
 class DecProblem:
-    """Device state of a decoder workload (contiguous cache)."""
+    """Device state of a decoder workload (contiguous or paged cache)."""
 
     def __init__(self, shape_key: str, t0, *, steps: int, seed: int, perturb: bool = True,
-                 device_weights: bool = False):
+                 device_weights: bool = False, layout: str = "contig"):
         sh = synth.decoder_shapes()[shape_key]
         self.sh = sh
         t0 = np.asarray(t0, dtype=np.int64)
         B = len(t0)
         self.wl = synth.Workload(f"dec-{shape_key}", sh.layers, sh.hq, sh.hkv, sh.head_dim, B, t0, steps, seed=seed,
-                                 head_seed=seed + 100, t_cap_slack=16)
+                                 head_seed=seed + 100, t_cap_slack=16, layout=layout)
         wl = self.wl
         L, Hq, Hkv, d, Dm = sh.layers, sh.hq, sh.hkv, sh.head_dim, sh.hidden
-        self.attn = C.make_dims(L, B, Hq, Hkv, t_cap=wl.t_cap)
-        self.dd = C.make_dec_dims(self.attn, sh.inter, sh.vocab, sh.rope_theta, sh.eps)
-        self.K = torch.zeros((L, B, Hkv, wl.t_cap, d), dtype=torch.int16, device=DEV)
-        self.V = torch.zeros_like(self.K)
         self.t0_dev = torch.from_numpy(t0.astype(np.int32)).to(DEV)
-        sd.fill_cache(self.K, wl, synth.TAG_K, self.t0_dev)
-        sd.fill_cache(self.V, wl, synth.TAG_V, self.t0_dev)
-        self.kv = C.make_kv(self.K, self.V)
+        if layout == "paged":
+            tables, nb = synth.paged_block_tables(wl)
+            self.attn = C.make_dims(L, B, Hq, Hkv, kv_layout=C.ODA_KV_PAGED, block_size=wl.block_size,
+                                    max_blocks_per_seq=tables.shape[1], num_blocks=nb)
+            self.tables = torch.from_numpy(tables).to(DEV)
+            self.K = torch.zeros((L, nb, Hkv, wl.block_size, d), dtype=torch.int16, device=DEV)
+            fill = dict(tables=self.tables, num_blocks=nb)
+        else:
+            self.attn = C.make_dims(L, B, Hq, Hkv, t_cap=wl.t_cap)
+            self.tables = None
+            self.K = torch.zeros((L, B, Hkv, wl.t_cap, d), dtype=torch.int16, device=DEV)
+            fill = {}
+        self.dd = C.make_dec_dims(self.attn, sh.inter, sh.vocab, sh.rope_theta, sh.eps)
+        self.V = torch.zeros_like(self.K)
+        sd.fill_cache(self.K, wl, synth.TAG_K, self.t0_dev, **fill)
+        sd.fill_cache(self.V, wl, synth.TAG_V, self.t0_dev, **fill)
+        self.kv = C.make_kv(self.K, self.V, self.tables)
         numel = C.oda_dec_layer_numel(self.dd)
         layers = torch.zeros((L, numel), dtype=torch.int16, device=DEV)
         embed = torch.zeros((sh.vocab, Dm), dtype=torch.int16, device=DEV)
@@ -117,9 +127,20 @@ class DecProblem:
         return P
 
     def history(self, b, pos):
-        """[L] of ([Hkv][pos][d], [Hkv][pos][d]) bf16 bits of the GPU cache."""
-        Kh = u16(self.K[:, b, :, :pos])
-        Vh = u16(self.V[:, b, :, :pos])
+        """[L] of ([Hkv][pos][d], [Hkv][pos][d]) bf16 bits of the GPU cache
+        (positions 0 .. pos-1 of sequence b, through its block table when
+        the cache is paged)."""
+        if self.tables is None:
+            Kh = u16(self.K[:, b, :, :pos])
+            Vh = u16(self.V[:, b, :, :pos])
+        else:
+            bs = self.wl.block_size
+            p = np.arange(pos)
+            blk = self.tables[b].cpu().numpy()[p // bs]
+            row = p % bs
+            # advanced indices around a slice put the position axis first
+            Kh = u16(self.K)[:, blk, :, row, :].transpose(1, 2, 0, 3)
+            Vh = u16(self.V)[:, blk, :, row, :].transpose(1, 2, 0, 3)
         return [Kh[l] for l in range(self.sh.layers)], [Vh[l] for l in range(self.sh.layers)]
 
 

@@ -120,6 +120,16 @@ def test_decoder_tiny_layerwise_across_the_boundary():
     print("tiny: worst |err| / bound", round(worst, 3))
 
 
+def test_decoder_tiny_layerwise_paged_cache():
+    """The per-layer check with a paged cache (16-row blocks at shuffled
+    physical places): the local branch's attention with its QK-norm and
+    RoPE folded in reads the cache through the block tables, contexts on
+    both sides of t = 2052, half of the sequences flagged."""
+    pr = DecProblem("tiny", [30, 2051, 2600, 4100], steps=1, seed=91, layout="paged")
+    worst = layerwise_check(pr, [1, 0, 1, 0])
+    print("tiny paged: worst |err| / bound", round(worst, 3))
+
+
 def test_decoder_tiny_layerwise_wide_batch():
     """Twenty sequences (two 16-wide column groups in every GEMM) with ragged
     contexts, half of them flagged, checked layer by layer."""
