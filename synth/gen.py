@@ -418,6 +418,9 @@ def decoder_shapes() -> dict:
     return {
         "qwen3-1.7b": DecoderShape("qwen3-1.7b", 2048, 28, 16, 8, 128, 6144, 151936),
         "tiny": DecoderShape("tiny", 1024, 2, 8, 4, 128, 2048, 4096),
+        # the same with one and with four query heads per KV head
+        "tiny-g1": DecoderShape("tiny-g1", 1024, 2, 8, 8, 128, 2048, 4096),
+        "tiny-g4": DecoderShape("tiny-g4", 1024, 2, 8, 2, 128, 2048, 4096),
     }
 
 

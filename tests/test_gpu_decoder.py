@@ -130,6 +130,16 @@ def test_decoder_tiny_layerwise_paged_cache():
     print("tiny paged: worst |err| / bound", round(worst, 3))
 
 
+@pytest.mark.parametrize("shape,layout", [("tiny-g1", "contig"), ("tiny-g4", "paged")])
+def test_decoder_tiny_layerwise_group_sizes(shape, layout):
+    """The per-layer check with one and with four query heads per KV head
+    (the attention kernels' other instantiations, QK-norm and RoPE folded
+    into the local one), contiguous and paged caches."""
+    pr = DecProblem(shape, [40, 2052, 3100], steps=1, seed=95, layout=layout)
+    worst = layerwise_check(pr, [1, 1, 0])
+    print(f"{shape} {layout}: worst |err| / bound", round(worst, 3))
+
+
 def test_decoder_tiny_layerwise_wide_batch():
     """Twenty sequences (two 16-wide column groups in every GEMM) with ragged
     contexts, half of them flagged, checked layer by layer."""
