@@ -317,20 +317,19 @@ def run(args, wl, stream, torch):
     ms_total = S.time_graphs(graphs, args.repeats)
     del graphs
 
-    # ---- the same K steps as three graphs per step (local + score | the L
-    # full-attention launches | commit), a pair of HIP events on the stream
-    # around the middle one: the dominant kernel's average launch duration,
-    # free of host launch gaps; the recorded flags and positions fix its
-    # algorithmic bytes
-    def pre(j):
-        S.plans[j].local()
-        S.plans[j].score()
-    g_pre = S.capture(pre, K)
+    # ---- the same K steps as four graphs per step (the L local launches |
+    # score | the L full-attention launches | commit), a pair of HIP events on
+    # the stream around the first and the third: the attention kernels'
+    # average launch durations, free of host launch gaps; the recorded flags
+    # and positions fix their algorithmic bytes
+    g_loc = S.capture(lambda j: S.plans[j].local(), K)
+    g_score = S.capture(lambda j: S.plans[j].score(), K)
     g_full = S.capture(lambda j: S.plans[j].full(), K)
     g_post = S.capture(lambda j: S.plans[j].commit(), K)
     flags_hist = torch.zeros((K, B), dtype=torch.uint8, device="cuda")
     pos_hist = torch.zeros((K, B), dtype=torch.int32, device="cuda")
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    ev_loc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     S.reset()
     torch.cuda.synchronize()
     e_start = torch.cuda.Event(enable_timing=True)
@@ -338,7 +337,11 @@ def run(args, wl, stream, torch):
     e_start.record(stream)
     for j in range(K):
         pos_hist[j].copy_(S.state.pos)
-        g_pre[j].replay()
+        l0, l1 = ev_loc[j]
+        l0.record(stream)
+        g_loc[j].replay()
+        l1.record(stream)
+        g_score[j].replay()
         e0, e1 = ev[j]
         e0.record(stream)
         g_full[j].replay()
@@ -349,7 +352,8 @@ def run(args, wl, stream, torch):
     torch.cuda.synchronize()
     split_ms = e_start.elapsed_time(e_end)
     full_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev)
-    del g_pre, g_full, g_post
+    local_ms = sum(l0.elapsed_time(l1) for l0, l1 in ev_loc)
+    del g_loc, g_score, g_full, g_post
     fl = flags_hist.cpu().numpy().astype(np.int64)
     ps = pos_hist.cpu().numpy().astype(np.int64)
     full_bytes = float(np.sum(fl * (ps + 1))) * Hkv * d * 2 * 2 * L
@@ -398,6 +402,14 @@ def run(args, wl, stream, torch):
     bytes_per_launch = full_bytes / nlaunch
     achieved = bytes_per_launch / (avg_us * 1e-6) / 1e9
     traffic, traffic_note = measured_traffic(bytes_per_launch)
+    local_bytes = kv_local * Hkv * d * 2 * 2 * L
+    out["attention_kernels"] = {
+        "local_avg_launch_us": round(local_ms * 1e3 / nlaunch, 2),
+        "local_gbs": round(local_bytes / (local_ms * 1e-3) / 1e9, 1),
+        "full_gbs": round(full_bytes / (full_ms * 1e-3) / 1e9, 1),
+        "kv_gbs": round((local_bytes + full_bytes) / ((local_ms + full_ms) * 1e-3) / 1e9, 1),
+        "note": "KV bytes read / summed launch time of the local and the full attention launches (HIP events "
+                "around each step's graph of L launches; local includes the per-launch split hand-off)"}
     out["roofline"] = {"bound": "hbm", "kernel": "k_attn_full (oda_full_attn_if)", "achieved": round(achieved, 1),
                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                        "traffic": traffic, "traffic_note": traffic_note, "avg_launch_us": round(avg_us, 2),
