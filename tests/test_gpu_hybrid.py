@@ -203,3 +203,17 @@ def test_one_sequence_one_head_widest_convolution():
     pr = GdnProblem(sh, [2])
     for step, flags in enumerate(([1], [0])):
         _step_and_check(pr, step, flags)
+
+
+@pytest.mark.parametrize("batch,heads", [(1024, 1), (1, 64)])
+def test_largest_batch_and_head_count(batch, heads):
+    """The largest batch (1024 sequences) and the most heads (64) the
+    library takes, one layer, two steps with complementary flags: slot
+    indices of every sequence, and outputs and states of sampled sequences
+    against the oracle."""
+    sh = synth.GdnShape(layers=1, batch=batch, heads=heads, shared_layers=0, seed=75)
+    pr = GdnProblem(sh, [b % 3 for b in range(batch)])
+    seqs = [0, batch // 2, batch - 1] if batch > 1 else [0]
+    flags0 = [(b * 7 + 1) % 2 for b in range(batch)]
+    for step, flags in enumerate((flags0, [1 - f for f in flags0])):
+        _step_and_check(pr, step, flags, seqs=seqs)
