@@ -93,11 +93,12 @@ int oda_dec_embed(const oda_dec_dims *dims, const oda_bf16 *embed, const int32_t
  * Writes the branch's staged k_cur / v_cur [B][Hkv][d] of this layer (what
  * oda_commit writes if the branch is chosen) and the attention output o
  * [B][Hq][d].  The attention is the ODA local / full branch of oda.h with
- * `attn_ws`, run in a mode that applies the QK-norm and RoPE to the raw
- * projection rows inside the attention kernels; q (device, [B][Hq][d]) must
- * be non-NULL but is not written.  Layer 0 of either branch writes the
- * step's RoPE table into `dws`, which the other layers read, so each branch
- * pass starts at layer 0 (the order below). */
+ * `attn_ws`.  The local branch runs it in a mode that applies the QK-norm
+ * and RoPE to the raw projection rows inside the attention kernel, from a
+ * table of the step's RoPE angles that its layer 0 writes into `dws`, so a
+ * local pass starts at layer 0 (the order below); the full branch applies
+ * them in a kernel of its own.  q (device, [B][Hq][d]) is scratch: the full
+ * branch writes it, the local branch does not, and it must be non-NULL. */
 int oda_dec_layer(const oda_dec_dims *dims, int32_t layer, int32_t branch, const oda_bf16 *w_layer,
                   const oda_kv *kv, const int32_t *pos, float *x, oda_bf16 *q, oda_bf16 *k_cur,
                   oda_bf16 *v_cur, oda_bf16 *o, void *attn_ws, size_t attn_ws_bytes, void *dws,
