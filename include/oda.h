@@ -19,9 +19,10 @@
  *    call only.  The library never allocates or frees memory, never
  *    synchronises a stream and never reads device memory from the host, so
  *    every call may be captured into a hipGraph.
- *  - The library keeps no mutable global state.  Calls that share a
- *    workspace `ws` must be ordered (same stream); calls on different
- *    workspaces may run concurrently.
+ *  - The library keeps no mutable global state beyond a per-device cache of
+ *    the compute-unit count (queried once, used to size grids).  Calls that
+ *    share a workspace `ws` must be ordered (same stream); calls on
+ *    different workspaces may run concurrently.
  *  - Return value: ODA_OK (0) or a negative ODA_E_* code.  On an error
  *    nothing has been launched and no memory has been touched.
  *  - Conditions that can only be seen on the device (a position beyond the
