@@ -533,57 +533,72 @@ def host_cpu_model() -> str:
 
 
 def cpu_baseline(wl, blob, theta, rate):
-    """The oracle, untuned, on a bounded sample of the same workload: one
-    layer of local attention for one sequence, the recall head for every
-    sequence, and one layer of full attention for one sequence; scaled to a
-    whole step as 1 / (L * B * t_local + t_head + rate * B * L * t_full)."""
+    """The oracle, untuned, on a bounded sample of the same workload: local
+    attention of every sequence at the last two layers, the recall head for
+    every sequence, and full attention of sequence 0 at the last layer (timed
+    three times); scaled to a whole step as
+    1 / (L * B * mean t_local + t_head + rate * B * L * mean t_full)."""
     import synth
     import oracle
     from threadpoolctl import threadpool_info
     L, B = wl.layers, wl.batch
     j = 0
-    l = L - 1
-    inp = {k: synth.step_tensor(wl, k, j, l) for k in ("qL", "kL", "vL", "qF", "kF", "vF")}
+    layers = [L - 1, L - 2] if L > 1 else [L - 1]
     emb = synth.embedding(wl, j)
     h0 = synth.h_prev0(wl)
-    t0 = int(wl.t0[0])
-    # committed history of sequence 0 (input generation: not timed); the
-    # local branch reads only the sink and window rows of it
-    t = t0
-    lo = max(0, t - wl.window)
-    Kh = np.zeros((wl.hkv, t, wl.head_dim), np.uint16)
-    Vh = np.zeros((wl.hkv, t, wl.head_dim), np.uint16)
-    for g in range(wl.hkv):
-        Kh[g, :wl.sink] = synth.cache_rows(wl, synth.TAG_K, l, 0, g, 0, min(wl.sink, t))
-        Kh[g, lo:] = synth.cache_rows(wl, synth.TAG_K, l, 0, g, lo, t)
-        Vh[g, :wl.sink] = synth.cache_rows(wl, synth.TAG_V, l, 0, g, 0, min(wl.sink, t))
-        Vh[g, lo:] = synth.cache_rows(wl, synth.TAG_V, l, 0, g, lo, t)
     P = oracle.unpack_head(blob, wl.hidden)
-    c0 = time.perf_counter()
-    oL0 = oracle.decode_attention(inp["qL"][0], Kh, Vh, inp["kL"][0], inp["vL"][0],
-                                  oracle.local_index_set(t + 1, wl.sink, wl.window))
-    t_local = time.perf_counter() - c0
+
+    def history(l, b, lo_rows):
+        # committed rows of sequence b (input generation: not timed); the
+        # local branch reads only the sink and window rows
+        t = int(wl.t0[b])
+        K = np.zeros((wl.hkv, t, wl.head_dim), np.uint16)
+        V = np.zeros((wl.hkv, t, wl.head_dim), np.uint16)
+        lo = max(0, t - wl.window) if lo_rows else 0
+        for g in range(wl.hkv):
+            for buf, tag in ((K, synth.TAG_K), (V, synth.TAG_V)):
+                if lo_rows:
+                    buf[g, :wl.sink] = synth.cache_rows(wl, tag, l, b, g, 0, min(wl.sink, t))
+                buf[g, lo:] = synth.cache_rows(wl, tag, l, b, g, lo, t)
+        return K, V
+
+    t_locals, oL_last = [], {}
+    for l in layers:
+        inp = {k: synth.step_tensor(wl, k, j, l) for k in ("qL", "kL", "vL")}
+        for b in range(B):
+            Kh, Vh = history(l, b, True)
+            t = int(wl.t0[b])
+            c0 = time.perf_counter()
+            o = oracle.decode_attention(inp["qL"][b], Kh, Vh, inp["kL"][b], inp["vL"][b],
+                                        oracle.local_index_set(t + 1, wl.sink, wl.window))
+            t_locals.append(time.perf_counter() - c0)
+            if l == L - 1:
+                oL_last[b] = o
     c0 = time.perf_counter()
     for b in range(B):
-        h_loc = oracle.f64_to_bf16(oL0.reshape(-1))
-        q = oracle.recall_score(P, h0[b], emb[b], h_loc)
+        q = oracle.recall_score(P, h0[b], emb[b], oracle.f64_to_bf16(oL_last[b].reshape(-1)))
         oracle.branch_rule(q, theta)
     t_head = time.perf_counter() - c0
-    # full history of sequence 0 for the full-branch sample
-    Kf = np.stack([synth.cache_rows(wl, synth.TAG_K, l, 0, g, 0, t0) for g in range(wl.hkv)])
-    Vf = np.stack([synth.cache_rows(wl, synth.TAG_V, l, 0, g, 0, t0) for g in range(wl.hkv)])
-    c0 = time.perf_counter()
-    oracle.decode_attention(inp["qF"][0], Kf, Vf, inp["kF"][0], inp["vF"][0], oracle.full_index_set(t0 + 1))
-    t_full = time.perf_counter() - c0
+    l = L - 1
+    inp = {k: synth.step_tensor(wl, k, j, l) for k in ("qF", "kF", "vF")}
+    Kf, Vf = history(l, 0, False)
+    t0 = int(wl.t0[0])
+    t_fulls = []
+    for _ in range(3):
+        c0 = time.perf_counter()
+        oracle.decode_attention(inp["qF"][0], Kf, Vf, inp["kF"][0], inp["vF"][0], oracle.full_index_set(t0 + 1))
+        t_fulls.append(time.perf_counter() - c0)
+    t_local, t_full = float(np.mean(t_locals)), float(np.mean(t_fulls))
     step_s = L * B * t_local + t_head + rate * B * L * t_full
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    sample_s = float(np.sum(t_locals) + t_head + np.sum(t_fulls))
     return {"value": round(1.0 / step_s, 5), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
             "host_cpus": os.cpu_count(), "cpu_model": host_cpu_model(),
-            "sample": (f"step 0, layer {l}: local attention of sequence 0 ({t_local:.2f} s), recall head "
-                       f"of all {B} ({t_head:.2f} s), full attention of sequence 0 over {t0 + 1} keys "
-                       f"({t_full:.2f} s); scaled to {L} layers x {B} sequences and {rate:.3f}*{B} flagged "
-                       f"sequences per step"),
-            "sample_cpu_s": round(t_local + t_head + t_full, 2)}
+            "sample": (f"step 0: local attention of all {B} sequences at layers {layers} ({len(t_locals)} runs, "
+                       f"mean {t_local:.2f} s), recall head of all {B} ({t_head:.2f} s), full attention of "
+                       f"sequence 0 over {t0 + 1} keys at layer {l} (3 runs, mean {t_full:.2f} s); scaled to "
+                       f"{L} layers x {B} sequences and {rate:.3f}*{B} flagged sequences per step"),
+            "sample_cpu_s": round(sample_s, 2)}
 
 
 # ---------------------------------------------------------------------------
