@@ -7,8 +7,8 @@
 // A step is HBM-bound: each (sequence, head) reads its 128 x 128 fp32 state
 // (64 KB) from the committed slot and writes the updated one to the branch's
 // slot, 2 x 64 KB per head and layer, plus a few hundred bytes of inputs.
-// The grid is (8 row blocks, H, B).  A workgroup loads its channels'
-// convolution inputs, then issues the loads of its 16 state rows, rebuilds
+// The grid is (4 row blocks, H, B).  A workgroup loads its channels'
+// convolution inputs, then issues the loads of its 32 state rows, rebuilds
 // the head's q^, k^, v in LDS while those are in flight (convolution, SiLU;
 // the row block 0 workgroup also writes the new convolution state; every
 // wave reduces the two L2 norms itself), then updates the rows: 16 lanes per
@@ -24,7 +24,7 @@ namespace oda {
 namespace {
 
 constexpr int kD = 128;          // d_k = d_v
-constexpr int kRowBlocks = 8;    // workgroups per (sequence, head)
+constexpr int kRowBlocks = 4;    // workgroups per (sequence, head): 4 beat 8 and 2 on the hybrid step
 constexpr int kRowsPerBlock = kD / kRowBlocks;
 constexpr float kNormEps = 1e-6f;
 
