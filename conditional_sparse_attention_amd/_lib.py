@@ -25,6 +25,8 @@ ODA_GDN_LOCAL, ODA_GDN_FULL, ODA_GDN_SLOTS = 0, 1, 3
 ODA_DEC_NTENSORS = 9
 ODA_HEAD_NTENSORS = 22
 ODA_FULL_MIN_CHUNK = 1024
+ODA_FULL_FINE_CHUNK = 256
+ODA_FULL_FILL_UNITS = 128
 ODA_FULL_MAX_SPLITS = 32
 
 EXPORTED = (

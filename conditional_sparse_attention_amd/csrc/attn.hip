@@ -693,16 +693,15 @@ __global__ void __launch_bounds__(FullWaves<G>::value * 64) k_attn_full(AttnPara
     const int item = P.worklist[1 + u / P.Hkv];
     const int g = u % P.Hkv;
     const int b = item >> 20;
-    const int split = item & 0xFFFFF;
-    if (b < 0 || b >= P.B) continue;
+    const int ns = (item >> 10) & 0x3FF;
+    const int split = item & 0x3FF;
+    if (b < 0 || b >= P.B || ns < 1 || ns > kFullMaxSplits || split >= ns) continue;
     const int pos = P.pos[b];
     const int t = pos + 1;
     if (pos < 0 || (int64_t)t > P.t_max) {
       if (split == 0 && g == 0 && threadIdx.x == 0) atomicOr(P.err, ODA_ERR_CAPACITY);
       continue;
     }
-    const int ns = full_nsplit(t);
-    if (split >= ns) continue;
     const int chunk = (t + ns - 1) / ns;
     const int v_lo = split * chunk;
     const int v_hi = (v_lo + chunk) < t ? v_lo + chunk : t;

@@ -278,11 +278,19 @@ struct OutArgs {
   float* score;
   uint8_t* flag;
   int32_t* worklist;  // count, items
-  int B;
+  int B, Hkv;
 };
 
+// Lane b < B of one wave (B <= 32) holds sequence b's flag f and position:
+// the split count of the policy, which depends on how many lanes are flagged.
+__device__ __forceinline__ int split_count(bool f, int pos, int lane, int B, int hkv) {
+  const int nflag = __popcll(__ballot(f && lane < B));
+  return f ? full_nsplit(pos + 1, nflag, hkv) : 0;
+}
+
 // Exclusive scan of the per-sequence split counts (lanes < B of one wave,
-// B <= 32) and the compacted items (b << 20) | split, b ascending.
+// B <= 32) and the compacted items (b << 20) | (nsplit << 10) | split,
+// b ascending.
 __device__ __forceinline__ void write_worklist(int cnt, int lane, int B, int* s_start, const int* s_count,
                                                int32_t* worklist) {
   int incl = cnt;
@@ -296,7 +304,7 @@ __device__ __forceinline__ void write_worklist(int cnt, int lane, int B, int* s_
   __builtin_amdgcn_wave_barrier();
   for (int i = lane; i < B * kFullMaxSplits; i += 64) {
     const int b = i / kFullMaxSplits, s = i % kFullMaxSplits;
-    if (s < s_count[b]) worklist[1 + s_start[b] + s] = (b << 20) | s;
+    if (s < s_count[b]) worklist[1 + s_start[b] + s] = full_item(b, s_count[b], s);
   }
 }
 
@@ -325,28 +333,28 @@ __global__ void __launch_bounds__(kThreads) k_out_rule(OutArgs A) {
   }
   __syncthreads();
   if (wave != 0) return;
-  int cnt = 0;
+  int f = 0, pos = 0;
   if (lane < A.B) {
     const float q = s_q[lane];
     A.score[lane] = q;
     const int fo = A.force != nullptr ? (int)A.force[lane] : -1;
-    const int f = fo >= 0 ? (fo != 0) : ((q > A.theta) || !isfinite(q));
+    f = fo >= 0 ? (fo != 0) : ((q > A.theta) || !isfinite(q));
     A.flag[lane] = (uint8_t)f;
-    cnt = f ? full_nsplit(A.pos[lane] + 1) : 0;
-    s_count[lane] = cnt;
+    pos = A.pos[lane];
   }
+  const int cnt = split_count(f != 0, pos, lane, A.B, A.Hkv);
+  if (lane < A.B) s_count[lane] = cnt;
   write_worklist(cnt, lane, A.B, s_start, s_count, A.worklist);
 }
 
-__global__ void __launch_bounds__(64) k_worklist(const uint8_t* flag, const int32_t* pos, int32_t* worklist, int B) {
+__global__ void __launch_bounds__(64) k_worklist(const uint8_t* flag, const int32_t* pos, int32_t* worklist, int B,
+                                                 int hkv) {
   __shared__ int s_start[kMaxBatch + 1];
   __shared__ int s_count[kMaxBatch];
   const int lane = threadIdx.x;
-  int cnt = 0;
-  if (lane < B) {
-    cnt = flag[lane] ? full_nsplit(pos[lane] + 1) : 0;
-    s_count[lane] = cnt;
-  }
+  const bool f = lane < B && flag[lane] != 0;
+  const int cnt = split_count(f, lane < B ? pos[lane] : 0, lane, B, hkv);
+  if (lane < B) s_count[lane] = cnt;
   write_worklist(cnt, lane, B, s_start, s_count, worklist);
 }
 
@@ -726,6 +734,7 @@ int launch_dense_t(const HeadParams& p, const int64_t* offs, hipStream_t s) {
   oa.flag = p.flag;
   oa.worklist = p.worklist;
   oa.B = B;
+  oa.Hkv = p.Hkv;
   hipLaunchKernelGGL(k_out_rule, dim3(1), dim3(kThreads), 0, s, oa);
   return hipGetLastError() == hipSuccess ? ODA_OK : ODA_E_LAUNCH;
 }
@@ -801,6 +810,7 @@ int launch_head_t(const HeadParams& p, const int64_t* offs, hipStream_t s) {
   oa.flag = p.flag;
   oa.worklist = p.worklist;
   oa.B = B;
+  oa.Hkv = p.Hkv;
   hipLaunchKernelGGL(k_out_rule, dim3(1), dim3(kThreads), 0, s, oa);
   return hipGetLastError() == hipSuccess ? ODA_OK : ODA_E_LAUNCH;
 }
@@ -819,8 +829,8 @@ size_t dense_head_part_floats(int B, int D) {
 }
 
 // offs: host array of the ODA_HEAD_NTENSORS+1 tensor offsets (oda_head_offsets order)
-int launch_worklist(const uint8_t* flag, const int32_t* pos, int32_t* worklist, int B, hipStream_t s) {
-  hipLaunchKernelGGL(k_worklist, dim3(1), dim3(64), 0, s, flag, pos, worklist, B);
+int launch_worklist(const uint8_t* flag, const int32_t* pos, int32_t* worklist, int B, int Hkv, hipStream_t s) {
+  hipLaunchKernelGGL(k_worklist, dim3(1), dim3(64), 0, s, flag, pos, worklist, B, Hkv);
   return hipGetLastError() == hipSuccess ? ODA_OK : ODA_E_LAUNCH;
 }
 

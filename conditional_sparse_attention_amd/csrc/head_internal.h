@@ -56,10 +56,11 @@ struct HeadParams {
   int32_t* worklist;
   int32_t* tickets;   // kHeadTickets, zero between calls
   int32_t B, D;
+  int32_t Hkv;        // KV heads of the attention layers (split policy)
   HeadWs act;
 };
 int launch_recall_head(const HeadParams& p, const int64_t* offs, hipStream_t s);
-int launch_worklist(const uint8_t* flag, const int32_t* pos, int32_t* worklist, int B, hipStream_t s);
+int launch_worklist(const uint8_t* flag, const int32_t* pos, int32_t* worklist, int B, int Hkv, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // device helpers

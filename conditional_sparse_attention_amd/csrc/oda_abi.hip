@@ -277,6 +277,7 @@ int oda_recall_score(const oda_dims* dims, const float* head_w, const oda_bf16* 
   p.worklist = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.worklist);
   p.B = dims->batch;
   p.D = dims->hidden;
+  p.Hkv = dims->num_kv_heads;
   p.tickets = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.tick_head);
   p.act = head_ws(ws, L, dims->batch, dims->hidden);
   return launch_recall_head(p, offs, stream);
@@ -290,7 +291,7 @@ int oda_worklist(const oda_dims* dims, const uint8_t* flag, const int32_t* pos, 
   const WsLayout L = ws_layout(dims);
   if (ws_bytes < L.total) return ODA_E_WORKSPACE;
   return launch_worklist(flag, pos, reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.worklist), dims->batch,
-                         stream);
+                         dims->num_kv_heads, stream);
 }
 
 int oda_commit(const oda_dims* dims, const oda_kv* kv, int32_t* pos, const uint8_t* flag, const oda_bf16* k_cur_L,

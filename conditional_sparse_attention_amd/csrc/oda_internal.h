@@ -19,6 +19,8 @@ constexpr int kPartStride = 132;       // floats per partial: acc[128], m, l, 2 
 constexpr int kTower = ODA_HEAD_TOWER;
 constexpr int kFfn = ODA_HEAD_FFN;
 constexpr int kFullMinChunk = ODA_FULL_MIN_CHUNK;
+constexpr int kFullFineChunk = ODA_FULL_FINE_CHUNK;
+constexpr int kFullFillUnits = ODA_FULL_FILL_UNITS;
 constexpr int kFullMaxSplits = ODA_FULL_MAX_SPLITS;
 
 // ---------------------------------------------------------------------------
@@ -38,11 +40,24 @@ struct WsLayout {
   int64_t t_max;            // capacity of one sequence in positions
 };
 
-// Split count of the full branch for a sequence of t keys.
-__device__ __host__ __forceinline__ int full_nsplit(int t) {
+// Split count of the full branch for a sequence of t keys when nflag
+// sequences with hkv KV heads each are flagged: chunks of kFullMinChunk keys
+// or more, cut finer (not below kFullFineChunk keys) while the launch would
+// hold fewer than kFullFillUnits units.  Every split is non-empty:
+// (n - 1)^2 < t for n <= ceil(t / 256).
+__device__ __host__ __forceinline__ int full_nsplit(int t, int nflag, int hkv) {
   int n = (t + kFullMinChunk - 1) / kFullMinChunk;
-  return n < kFullMaxSplits ? n : kFullMaxSplits;
+  n = n < kFullMaxSplits ? n : kFullMaxSplits;
+  const int per = nflag * hkv;
+  int fine = per > 0 ? kFullFillUnits / per : 0;
+  const int by_chunk = (t + kFullFineChunk - 1) / kFullFineChunk;
+  fine = fine < by_chunk ? fine : by_chunk;
+  fine = fine < kFullMaxSplits ? fine : kFullMaxSplits;
+  return n > fine ? n : fine;
 }
+
+// Work-list items: (b << 20) | (nsplit << 10) | split.
+__device__ __host__ __forceinline__ int32_t full_item(int b, int ns, int s) { return (b << 20) | (ns << 10) | s; }
 
 bool dims_valid(const oda_dims* d, int* status);
 WsLayout ws_layout(const oda_dims* d);

@@ -88,11 +88,19 @@ extern "C" {
 #define ODA_HEAD_FFN 2048
 #define ODA_HEAD_NTENSORS 22
 
-/* Split policy of the full branch: a flagged sequence with t = pos + 1 keys
- * is cut into nsplit(t) = min(ODA_FULL_MAX_SPLITS, ceil(t / ODA_FULL_MIN_CHUNK))
- * contiguous splits of ceil(t / nsplit(t)) keys (the last one shorter); the
- * work list has one item per (flagged sequence, split). */
+/* Split policy of the full branch.  With F flagged sequences in the step
+ * and Hkv KV heads, a flagged sequence with t = pos + 1 keys is cut into
+ *   nsplit(t, F) = max(min(ODA_FULL_MAX_SPLITS, ceil(t / ODA_FULL_MIN_CHUNK)),
+ *                      min(ODA_FULL_MAX_SPLITS, ceil(t / ODA_FULL_FINE_CHUNK),
+ *                          floor(ODA_FULL_FILL_UNITS / (F * Hkv))))
+ * contiguous splits of ceil(t / nsplit) keys (the last one shorter, none
+ * empty): chunks of ODA_FULL_MIN_CHUNK keys or more, cut finer (down to
+ * ODA_FULL_FINE_CHUNK) while the launch would otherwise hold fewer than
+ * ODA_FULL_FILL_UNITS (sequence, split, KV head) units.  The work list has
+ * one item per (flagged sequence, split). */
 #define ODA_FULL_MIN_CHUNK 1024
+#define ODA_FULL_FINE_CHUNK 256
+#define ODA_FULL_FILL_UNITS 128
 #define ODA_FULL_MAX_SPLITS 32
 
 typedef uint16_t oda_bf16;
@@ -149,8 +157,9 @@ int oda_head_offsets(int32_t hidden, int64_t *offsets);
 size_t oda_workspace_bytes(const oda_dims *dims);
 
 /* Byte offset inside the workspace of the full-branch work list: an int32
- * count followed by `count` int32 items, item = (b << 20) | split.  Written
- * by oda_recall_score, read by oda_full_attn_if. */
+ * count followed by `count` int32 items,
+ * item = (b << 20) | (nsplit << 10) | split.  Written by oda_recall_score
+ * and oda_worklist, read by oda_full_attn_if. */
 size_t oda_workspace_worklist_offset(const oda_dims *dims);
 
 /* ---- device work ---- */
@@ -184,14 +193,14 @@ int oda_local_attn(const oda_dims *dims, int32_t layer, const oda_kv *kv, const 
  *                          : (score[b] > theta || score[b] is not finite)
  *    [ODA notes §2.3]; force may be NULL (all decided by the head).
  *  The work list (see oda_workspace_worklist_offset) lists, for each flagged
- *  b in ascending order, the splits 0 .. nsplit(pos[b]+1)-1 (split policy
- *  above). */
+ *  b in ascending order, the splits 0 .. nsplit(pos[b]+1, F)-1, F the
+ *  number of flagged sequences (split policy above). */
 int oda_recall_score(const oda_dims *dims, const float *head_w, const oda_bf16 *h_prev,
                      const oda_bf16 *emb, const oda_bf16 *h_local, float theta, const int8_t *force,
                      const int32_t *pos, float *score, uint8_t *flag, void *ws, size_t ws_bytes,
                      hipStream_t stream);
 
-/* Device-side compaction alone [row A6]: writes the full-branch work list
+/* Device-side compaction alone: writes the full-branch work list
  * of the workspace from caller-given flags (flag[b] != 0 -> sequence b runs
  * the full branch), exactly as oda_recall_score does after its rule.  For
  * schedules decided outside the head (forced calls, an always-full

@@ -164,8 +164,7 @@ class Problem:
         off = C.oda_workspace_worklist_offset(self.dims)
         w = self.ws[off:].view(torch.int32)
         n = int(w[0].item())
-        items = w[1:1 + n].cpu().numpy()
-        return [(int(x) >> 20, int(x) & 0xFFFFF) for x in items]
+        return decode_items(w[1:1 + n].cpu().numpy())
 
     def head_params(self):
         if self.head_P is None:
@@ -173,9 +172,28 @@ class Problem:
         return self.head_P
 
 
-def full_nsplit(t: int) -> int:
-    """Split policy stated in include/oda.h: min(32, ceil(t / 1024))."""
-    return min(C.ODA_FULL_MAX_SPLITS, -(-t // C.ODA_FULL_MIN_CHUNK))
+def full_nsplit(t: int, nflag: int, hkv: int) -> int:
+    """Split policy stated in include/oda.h: chunks of 1024 keys or more (at
+    most 32 splits), cut finer, down to 256 keys, while the F = nflag flagged
+    sequences' Hkv heads would otherwise make fewer than 128 units."""
+    base = min(C.ODA_FULL_MAX_SPLITS, -(-t // C.ODA_FULL_MIN_CHUNK))
+    per = nflag * hkv
+    fine = min(C.ODA_FULL_MAX_SPLITS, -(-t // C.ODA_FULL_FINE_CHUNK), C.ODA_FULL_FILL_UNITS // per) if per else 0
+    return max(base, fine)
+
+
+def decode_items(items) -> list:
+    """Work-list items (b << 20) | (nsplit << 10) | split as (b, nsplit, split)."""
+    return [(int(x) >> 20, (int(x) >> 10) & 0x3FF, int(x) & 0x3FF) for x in items]
+
+
+def want_worklist(flags, ts, hkv: int) -> list:
+    """The oracle's work list (flagged b ascending, splits in order) for the
+    split counts of the policy, as (b, nsplit, split)."""
+    from oracle import full_worklist
+    nflag = int(np.count_nonzero(np.asarray(flags)))
+    ns = [full_nsplit(int(t), nflag, hkv) for t in ts]
+    return [(b, ns[b], s) for b, s in full_worklist([int(f != 0) for f in flags], ns)]
 
 
 def replay_step(pr: Problem, j: int, *, theta: float, force=None, check_layers=None, check_b=None,
@@ -225,7 +243,7 @@ def replay_step(pr: Problem, j: int, *, theta: float, force=None, check_layers=N
         if stats is not None:
             stats.setdefault("q", []).append(q)
     # ---- work list
-    assert pr.worklist() == [(b, s) for b in range(B) if flag[b] for s in range(full_nsplit(int(pos_before[b]) + 1))]
+    assert pr.worklist() == want_worklist(flag, np.asarray(pos_before, np.int64) + 1, wl.hkv)
     # ---- full branch (flagged rows), untouched rows
     for b in range(B):
         if flag[b]:
@@ -331,8 +349,7 @@ class BigProblem:
             f = int(rec["force"][b])
             if f >= 0 or abs(q - rec["theta"]) >= TIE_BAND:
                 assert int(flag[b]) == branch_rule(q, rec["theta"], f), (j, b, q)
-        want = [(b, s) for b in range(B) if flag[b] for s in range(full_nsplit(int(rec["pos"][b]) + 1))]
-        assert rec["worklist"] == want
+        assert rec["worklist"] == want_worklist(flag, np.asarray(rec["pos"], np.int64) + 1, wl.hkv)
         for b in range(B):
             if not flag[b]:
                 assert np.all(rec["oF"][:, b] == 0x7FC1), "unflagged full rows written"

@@ -163,3 +163,33 @@ def test_gdn_entry_points_reject_bad_arguments_before_launching():
     assert lib.oda_gdn_step(g, 18, 0, fake, fake, None, *f7[:5], None) == C.ODA_E_LAYER
     assert lib.oda_gdn_step(g, 0, 0, fake + 8, fake, None, *f7[:5], None) == C.ODA_E_DIMS  # state not 16-byte aligned
     assert lib.oda_gdn_commit(g, None, fake, None) == C.ODA_E_NULL
+
+
+def test_split_policy_constants_and_properties():
+    """The binding's split-policy constants are the header's, and the policy
+    the work-list tests expect keeps its stated properties: between 1 and 32
+    splits, none empty, never coarser than chunks of 1024 keys, finer ones
+    only while the launch holds fewer than 128 units and never below 256
+    keys; sample values by hand."""
+    from _harness import full_nsplit
+    src = open(os.path.join(ROOT, "include", "oda.h")).read()
+    for name in ("ODA_FULL_MIN_CHUNK", "ODA_FULL_FINE_CHUNK", "ODA_FULL_FILL_UNITS", "ODA_FULL_MAX_SPLITS"):
+        m = re.search(r"#define\s+%s\s+(\d+)" % name, src)
+        assert m and int(m.group(1)) == getattr(C, name), name
+    ts = sorted(set([1, 2, 255, 256, 257, 1023, 1024, 1025, 2052, 4096, 4097, 9000, 16384, 32769, 131072, 262144]
+                    + list(range(1, 70000, 997))))
+    for hkv in (1, 2, 4, 8, 16):
+        for nflag in (1, 2, 3, 5, 8, 16, 32):
+            for t in ts:
+                n = full_nsplit(t, nflag, hkv)
+                base = min(32, -(-t // 1024))
+                chunk = -(-t // n)
+                assert 1 <= n <= 32 and n >= base, (t, nflag, hkv, n)
+                assert (n - 1) * chunk < t, (t, nflag, hkv, n)       # the last split is not empty
+                if n > base:
+                    assert nflag * hkv * n <= 128 and -(-t // 256) >= n, (t, nflag, hkv, n)
+                if nflag * hkv * base >= 128:
+                    assert n == base, (t, nflag, hkv, n)
+    assert [full_nsplit(4096, f, 8) for f in (1, 2, 3, 4, 5)] == [16, 8, 5, 4, 4]
+    assert [full_nsplit(t, 1, 8) for t in (1, 300, 8192, 16384, 131072)] == [1, 2, 16, 16, 32]
+    assert full_nsplit(4096, 1, 2) == 16 and full_nsplit(20000, 1, 2) == 32

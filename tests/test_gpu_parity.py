@@ -153,22 +153,31 @@ def test_device_generator_paged_matches_contig():
 
 def test_worklist_entry_point_bitexact():
     """oda_worklist (compaction from caller flags) writes the same list as
-    the oracle's work list for ragged positions and mixed flags."""
-    from oracle import full_worklist
+    the oracle's work list, with the split counts of the policy, for ragged
+    positions (long, and short enough for the finer splits), mixed flags,
+    one flag and none, at 2, 4 and 8 KV heads."""
+    from _harness import decode_items, want_worklist
     rng = np.random.default_rng(5)
+    cases = []
     for B in (1, 7, 32):
-        pos = rng.integers(0, 200000, size=B).astype(np.int32)
-        flags = rng.integers(0, 2, size=B).astype(np.uint8)
-        dims = C.make_dims(2, B, 16, 8, t_cap=1 << 18)
-        ws = torch.zeros(C.oda_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
-        C.oda_workspace_init(dims, ws)
-        C.oda_worklist(dims, torch.from_numpy(flags).cuda(), torch.from_numpy(pos).cuda(), ws)
-        torch.cuda.synchronize()
-        off = C.oda_workspace_worklist_offset(dims)
-        w = ws[off:].view(torch.int32).cpu().numpy()
-        got = [(int(x) >> 20, int(x) & 0xFFFFF) for x in w[1:1 + w[0]]]
-        nsplit = [min(32, -(-(int(p) + 1) // 1024)) for p in pos]
-        assert got == full_worklist(flags, nsplit)
+        for top in (200000, 9000):
+            cases.append((B, rng.integers(0, top, size=B), rng.integers(0, 2, size=B)))
+        one = np.zeros(B, np.int64)
+        one[B // 2] = 1
+        cases.append((B, rng.integers(0, 5000, size=B), one))
+    cases.append((5, rng.integers(0, 5000, size=5), np.zeros(5, np.int64)))
+    for hq, hkv in ((16, 8), (16, 4), (4, 2)):
+        for B, pos, flags in cases:
+            pos = pos.astype(np.int32)
+            flags = flags.astype(np.uint8)
+            dims = C.make_dims(2, B, hq, hkv, t_cap=1 << 18)
+            ws = torch.zeros(C.oda_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+            C.oda_workspace_init(dims, ws)
+            C.oda_worklist(dims, torch.from_numpy(flags).cuda(), torch.from_numpy(pos).cuda(), ws)
+            torch.cuda.synchronize()
+            off = C.oda_workspace_worklist_offset(dims)
+            w = ws[off:].view(torch.int32).cpu().numpy()
+            assert decode_items(w[1:1 + w[0]]) == want_worklist(flags, pos.astype(np.int64) + 1, hkv), (hkv, B)
 
 
 @pytest.mark.parametrize("B,hq", [(1, 16), (4, 16), (5, 8), (8, 16), (9, 8), (16, 32), (17, 16), (32, 8), (32, 32), (24, 16)])
@@ -179,8 +188,7 @@ def test_recall_head_batch_sizes(B, hq):
     and 4096, with a perturbed head so every bias and gain term counts.
     Scores to 1e-4 (1 + |q|); flags bit-exact outside the tie band; the work
     list bit-exact against the oracle's for the GPU's flags."""
-    from oracle import full_worklist
-    from _harness import SCORE_TOL, TIE_BAND
+    from _harness import SCORE_TOL, TIE_BAND, decode_items, want_worklist
     D = hq * 128
     seed = 40 + B
     blob = synth.head_blob(D, seed, perturb=True)
@@ -214,6 +222,4 @@ def test_recall_head_batch_sizes(B, hq):
                 assert f[b] == want, (b, qs[b], theta)
         off = C.oda_workspace_worklist_offset(dims)
         wl_ = ws[off:].view(torch.int32).cpu().numpy()
-        items = [(int(x) >> 20, int(x) & 0xFFFFF) for x in wl_[1:1 + wl_[0]]]
-        nsplit = [min(32, -(-(int(p) + 1) // 1024)) for p in pos]
-        assert items == full_worklist(f, nsplit)
+        assert decode_items(wl_[1:1 + wl_[0]]) == want_worklist(f, pos.astype(np.int64) + 1, 8)
