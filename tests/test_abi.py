@@ -168,9 +168,9 @@ def test_gdn_entry_points_reject_bad_arguments_before_launching():
 def test_split_policy_constants_and_properties():
     """The binding's split-policy constants are the header's, and the policy
     the work-list tests expect keeps its stated properties: between 1 and 32
-    splits, none empty, never coarser than chunks of 1024 keys, finer ones
-    only while the launch holds fewer than 128 units and never below 256
-    keys; sample values by hand."""
+    splits, none empty, never fewer than 1024-key chunks give (capped at 32),
+    more only while the launch holds at most 128 units and then at most
+    ceil(t / 256); sample values by hand."""
     from _harness import full_nsplit
     src = open(os.path.join(ROOT, "include", "oda.h")).read()
     for name in ("ODA_FULL_MIN_CHUNK", "ODA_FULL_FINE_CHUNK", "ODA_FULL_FILL_UNITS", "ODA_FULL_MAX_SPLITS"):
