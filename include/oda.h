@@ -111,7 +111,7 @@ typedef struct oda_dims {
   int32_t num_q_heads;         /* Hq */
   int32_t num_kv_heads;        /* Hkv; Hq % Hkv == 0, Hq / Hkv in {1, 2, 4} */
   int32_t head_dim;            /* d; must be 128 */
-  int32_t hidden;              /* D; must equal Hq * d (the recall-head input width) */
+  int32_t hidden;              /* D; must equal Hq * d (the recall-head input width; oda_recall_score takes 1024, 2048 or 4096) */
   int32_t sink;                /* s >= 0  (4 in [ODA notes §2.1]) */
   int32_t window;              /* w >= 1  (2048; includes the current token) */
   int32_t kv_layout;           /* ODA_KV_CONTIG or ODA_KV_PAGED */

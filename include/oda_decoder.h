@@ -59,12 +59,13 @@ extern "C" {
 
 typedef struct oda_dec_dims {
   oda_dims attn;       /* the attention path's dims (layers, batch, heads, d = 128, D = Hq*d, cache) */
-  int32_t inter;       /* I, MLP hidden width; multiple of 512 */
+  int32_t inter;       /* I, MLP hidden width; multiple of 1024 */
   int32_t vocab;       /* V, rows of the tied embedding; multiple of 64 */
   float rope_theta;    /* RoPE base (1e6 for the Qwen3 family) */
   float eps;           /* RMSNorm epsilon (1e-6) */
 } oda_dec_dims;
-/* Also required: D a multiple of 512, (Hq + 2 Hkv) * d a multiple of 64. */
+/* Also required: D = Hq * d a multiple of 1024 (1024, 2048 or 4096 for the
+ * recall head of the step), B <= 32. */
 
 /* bf16 elements of one layer blob; -1 if dims are invalid. */
 int64_t oda_dec_layer_numel(const oda_dec_dims *dims);

@@ -421,6 +421,8 @@ def decoder_shapes() -> dict:
         # the same with one and with four query heads per KV head
         "tiny-g1": DecoderShape("tiny-g1", 1024, 2, 8, 8, 128, 2048, 4096),
         "tiny-g4": DecoderShape("tiny-g4", 1024, 2, 8, 2, 128, 2048, 4096),
+        # an MLP width that is not a multiple of 2048: 3 K slices in the down projection
+        "tiny-i3k": DecoderShape("tiny-i3k", 1024, 2, 8, 4, 128, 3072, 4096),
     }
 
 

@@ -130,11 +130,12 @@ def test_decoder_tiny_layerwise_paged_cache():
     print("tiny paged: worst |err| / bound", round(worst, 3))
 
 
-@pytest.mark.parametrize("shape,layout", [("tiny-g1", "contig"), ("tiny-g4", "paged")])
+@pytest.mark.parametrize("shape,layout", [("tiny-g1", "contig"), ("tiny-g4", "paged"), ("tiny-i3k", "contig")])
 def test_decoder_tiny_layerwise_group_sizes(shape, layout):
     """The per-layer check with one and with four query heads per KV head
     (the attention kernels' other instantiations, QK-norm and RoPE folded
-    into the local one), contiguous and paged caches."""
+    into the local one), contiguous and paged caches, and with an MLP width
+    of 3072 (three K slices in the down projection)."""
     pr = DecProblem(shape, [40, 2052, 3100], steps=1, seed=95, layout=layout)
     worst = layerwise_check(pr, [1, 1, 0])
     print(f"{shape} {layout}: worst |err| / bound", round(worst, 3))
