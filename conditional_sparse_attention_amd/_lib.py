@@ -27,6 +27,7 @@ ODA_HEAD_NTENSORS = 22
 ODA_FULL_MIN_CHUNK = 1024
 ODA_FULL_FINE_CHUNK = 256
 ODA_FULL_FILL_UNITS = 128
+ODA_FULL_ROUND_UNITS = 256
 ODA_FULL_MAX_SPLITS = 32
 
 EXPORTED = (

@@ -21,6 +21,7 @@ constexpr int kFfn = ODA_HEAD_FFN;
 constexpr int kFullMinChunk = ODA_FULL_MIN_CHUNK;
 constexpr int kFullFineChunk = ODA_FULL_FINE_CHUNK;
 constexpr int kFullFillUnits = ODA_FULL_FILL_UNITS;
+constexpr int kFullRoundUnits = ODA_FULL_ROUND_UNITS;
 constexpr int kFullMaxSplits = ODA_FULL_MAX_SPLITS;
 
 // ---------------------------------------------------------------------------
@@ -43,8 +44,9 @@ struct WsLayout {
 // Split count of the full branch for a sequence of t keys when nflag
 // sequences with hkv KV heads each are flagged: chunks of kFullMinChunk keys
 // or more, cut finer (not below kFullFineChunk keys) while the launch would
-// hold fewer than kFullFillUnits units.  Every split is non-empty:
-// (n - 1)^2 < t for n <= ceil(t / 256).
+// hold fewer than kFullFillUnits units, coarser where more than
+// kFullRoundUnits units would not fit one round of the persistent grid.
+// Every split is non-empty: (n - 1)^2 < t for n <= ceil(t / 256).
 __device__ __host__ __forceinline__ int full_nsplit(int t, int nflag, int hkv) {
   int n = (t + kFullMinChunk - 1) / kFullMinChunk;
   n = n < kFullMaxSplits ? n : kFullMaxSplits;
@@ -53,7 +55,12 @@ __device__ __host__ __forceinline__ int full_nsplit(int t, int nflag, int hkv) {
   const int by_chunk = (t + kFullFineChunk - 1) / kFullFineChunk;
   fine = fine < by_chunk ? fine : by_chunk;
   fine = fine < kFullMaxSplits ? fine : kFullMaxSplits;
-  return n > fine ? n : fine;
+  n = n > fine ? n : fine;
+  if (per > 0 && per * n > kFullRoundUnits) {
+    const int fit = kFullRoundUnits / per;
+    n = fit > 1 ? fit : 1;
+  }
+  return n;
 }
 
 // Work-list items: (b << 20) | (nsplit << 10) | split.

@@ -89,18 +89,24 @@ extern "C" {
 #define ODA_HEAD_NTENSORS 22
 
 /* Split policy of the full branch.  With F flagged sequences in the step
- * and Hkv KV heads, a flagged sequence with t = pos + 1 keys is cut into
- *   nsplit(t, F) = max(min(ODA_FULL_MAX_SPLITS, ceil(t / ODA_FULL_MIN_CHUNK)),
- *                      min(ODA_FULL_MAX_SPLITS, ceil(t / ODA_FULL_FINE_CHUNK),
- *                          floor(ODA_FULL_FILL_UNITS / (F * Hkv))))
- * contiguous splits of ceil(t / nsplit) keys (the last one shorter, none
- * empty): chunks of ODA_FULL_MIN_CHUNK keys or more, cut finer (down to
- * ODA_FULL_FINE_CHUNK) while the launch would otherwise hold fewer than
- * ODA_FULL_FILL_UNITS (sequence, split, KV head) units.  The work list has
- * one item per (flagged sequence, split). */
+ * and Hkv KV heads (P = F * Hkv units per split index), a flagged sequence
+ * with t = pos + 1 keys is cut into nsplit(t, F) contiguous splits of
+ * ceil(t / nsplit) keys (the last one shorter, none empty):
+ *   n0 = max(min(ODA_FULL_MAX_SPLITS, ceil(t / ODA_FULL_MIN_CHUNK)),
+ *            min(ODA_FULL_MAX_SPLITS, ceil(t / ODA_FULL_FINE_CHUNK),
+ *                floor(ODA_FULL_FILL_UNITS / P)))
+ *   nsplit = P * n0 <= ODA_FULL_ROUND_UNITS ? n0
+ *                                           : max(1, floor(ODA_FULL_ROUND_UNITS / P))
+ * Chunks of ODA_FULL_MIN_CHUNK keys or more, cut finer (down to
+ * ODA_FULL_FINE_CHUNK) while the launch would hold fewer than
+ * ODA_FULL_FILL_UNITS units, and coarser where more than
+ * ODA_FULL_ROUND_UNITS units would not fit one round of the full kernel's
+ * persistent grid (one workgroup per compute unit of an MI355X).  The work
+ * list has one item per (flagged sequence, split). */
 #define ODA_FULL_MIN_CHUNK 1024
 #define ODA_FULL_FINE_CHUNK 256
 #define ODA_FULL_FILL_UNITS 128
+#define ODA_FULL_ROUND_UNITS 256
 #define ODA_FULL_MAX_SPLITS 32
 
 typedef uint16_t oda_bf16;

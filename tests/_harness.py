@@ -175,11 +175,15 @@ class Problem:
 def full_nsplit(t: int, nflag: int, hkv: int) -> int:
     """Split policy stated in include/oda.h: chunks of 1024 keys or more (at
     most 32 splits), cut finer, down to 256 keys, while the F = nflag flagged
-    sequences' Hkv heads would otherwise make fewer than 128 units."""
+    sequences' Hkv heads would otherwise make fewer than 128 units, and
+    coarser where more than 256 units would not fit one round."""
     base = min(C.ODA_FULL_MAX_SPLITS, -(-t // C.ODA_FULL_MIN_CHUNK))
     per = nflag * hkv
     fine = min(C.ODA_FULL_MAX_SPLITS, -(-t // C.ODA_FULL_FINE_CHUNK), C.ODA_FULL_FILL_UNITS // per) if per else 0
-    return max(base, fine)
+    n = max(base, fine)
+    if per and per * n > C.ODA_FULL_ROUND_UNITS:
+        n = max(1, C.ODA_FULL_ROUND_UNITS // per)
+    return n
 
 
 def decode_items(items) -> list:

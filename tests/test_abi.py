@@ -168,28 +168,37 @@ def test_gdn_entry_points_reject_bad_arguments_before_launching():
 def test_split_policy_constants_and_properties():
     """The binding's split-policy constants are the header's, and the policy
     the work-list tests expect keeps its stated properties: between 1 and 32
-    splits, none empty, never fewer than 1024-key chunks give (capped at 32),
-    more only while the launch holds at most 128 units and then at most
+    splits, none empty; never more units than one round (256) unless a
+    single split already makes more; never fewer splits than 1024-key
+    chunks give (capped at 32) unless those would overflow the round; more
+    only while the launch holds at most 128 units and then at most
     ceil(t / 256); sample values by hand."""
     from _harness import full_nsplit
     src = open(os.path.join(ROOT, "include", "oda.h")).read()
-    for name in ("ODA_FULL_MIN_CHUNK", "ODA_FULL_FINE_CHUNK", "ODA_FULL_FILL_UNITS", "ODA_FULL_MAX_SPLITS"):
+    for name in ("ODA_FULL_MIN_CHUNK", "ODA_FULL_FINE_CHUNK", "ODA_FULL_FILL_UNITS", "ODA_FULL_ROUND_UNITS",
+                 "ODA_FULL_MAX_SPLITS"):
         m = re.search(r"#define\s+%s\s+(\d+)" % name, src)
         assert m and int(m.group(1)) == getattr(C, name), name
     ts = sorted(set([1, 2, 255, 256, 257, 1023, 1024, 1025, 2052, 4096, 4097, 9000, 16384, 32769, 131072, 262144]
                     + list(range(1, 70000, 997))))
     for hkv in (1, 2, 4, 8, 16):
         for nflag in (1, 2, 3, 5, 8, 16, 32):
+            per = nflag * hkv
             for t in ts:
                 n = full_nsplit(t, nflag, hkv)
                 base = min(32, -(-t // 1024))
                 chunk = -(-t // n)
-                assert 1 <= n <= 32 and n >= base, (t, nflag, hkv, n)
+                assert 1 <= n <= 32, (t, nflag, hkv, n)
                 assert (n - 1) * chunk < t, (t, nflag, hkv, n)       # the last split is not empty
+                assert per * n <= 256 or n == 1, (t, nflag, hkv, n)
+                if per * base <= 256:
+                    assert n >= base, (t, nflag, hkv, n)
+                else:
+                    assert n == max(1, 256 // per), (t, nflag, hkv, n)
                 if n > base:
-                    assert nflag * hkv * n <= 128 and -(-t // 256) >= n, (t, nflag, hkv, n)
-                if nflag * hkv * base >= 128:
-                    assert n == base, (t, nflag, hkv, n)
+                    assert per * n <= 128 and -(-t // 256) >= n, (t, nflag, hkv, n)
     assert [full_nsplit(4096, f, 8) for f in (1, 2, 3, 4, 5)] == [16, 8, 5, 4, 4]
     assert [full_nsplit(t, 1, 8) for t in (1, 300, 8192, 16384, 131072)] == [1, 2, 16, 16, 32]
+    assert [full_nsplit(131072, f, 8) for f in (1, 2, 3, 4, 32)] == [32, 16, 10, 8, 1]
+    assert full_nsplit(16384, 3, 8) == 10 and full_nsplit(131072, 32, 16) == 1
     assert full_nsplit(4096, 1, 2) == 16 and full_nsplit(20000, 1, 2) == 32
