@@ -80,3 +80,14 @@ def test_workload5_4k_subbatch():
     run_workload("5-4k", steps,
                  lambda wl, j: [(27, 31, 3), (0, 0, 0)],
                  lambda wl, j: [(27, 0, 1), (27, 3, 6)])
+
+
+def test_workload5_4k_all_flagged_whole_sequence_units():
+    """Every sequence of the paged 4K batch flagged: 32 sequences x 8 KV heads
+    fill the 256-unit round, so each sequence is a single split (whole
+    sequence per unit, no partial merge)."""
+    B = 32
+    steps = [(0.0, _force(B, full=range(B)))]
+    run_workload("5-4k", steps,
+                 lambda wl, j: [(27, 31, 3)],
+                 lambda wl, j: [(27, 0, 1), (13, 17, 12), (27, 31, 15)])
