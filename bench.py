@@ -53,10 +53,20 @@ def parse():
     ap.add_argument("--repeats", type=int, default=3)
     ap.add_argument("--workload", default="3", help="workload key (default 3: 128K, B=4, 12.5%% recall)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--rate-sweep", default="", help="comma list of forced full-branch rates to time as well")
-    ap.add_argument("--always-full", action="store_true",
-                    help="also time the always-full baseline: every sequence takes the full branch, no local "
-                         "attention and no recall head (the feed, the work list, the full attention, the commit)")
+    ap.add_argument("--rate-sweep", default="0,0.125,0.25,0.5,1",
+                    help="comma list of forced full-branch rates to time as well (per-step graphs, exact counts); "
+                         "empty to skip")
+    ap.add_argument("--no-always-full", action="store_true",
+                    help="skip the always-full baseline (every sequence takes the full branch, no local attention "
+                         "and no recall head: the work list, the full attention and the commit)")
+    ap.add_argument("--no-first-request", action="store_true",
+                    help="skip the first-request timings (a fresh process per measurement: capture plus the "
+                         "first K steps, ODA and always-full)")
+    ap.add_argument("--first-request-cell", default="", help=argparse.SUPPRESS)  # child: oda | always-full
+    ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
+                    help="summarise a rocprofv3 --kernel-trace (csv) of a bench run: per-kernel durations over "
+                         "the whole run and over the split-graph region its JSON line names (trace_window), and "
+                         "the roofline fraction those durations give; prints markdown")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--matrix", action="store_true",
@@ -83,6 +93,8 @@ def parse():
 
 def main():
     args = parse()
+    if args.trace_summary:
+        return trace_summary(*args.trace_summary)
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the step is timed on one GPU's share "
                                    "of the batch, and runs over several GPUs are not provided", "n_gpus": args.gpus}))
@@ -126,14 +138,15 @@ def main():
         with torch.cuda.stream(stream):
             decoder_bench(args, wl, stream, torch)
         return
-    if wl.bernoulli_odd is not None:
-        raise SystemExit("the bench runs head-decided schedules; this workload forces per-step flags")
     if max(args.steps, args.warmup) > wl.steps:
         # more steps than the workload defines: the same workload with room
         # for them (every step's inputs come from the seeded generator)
         wl = wl.replace(steps=max(args.steps, args.warmup))
     stream = torch.cuda.Stream()  # a non-default stream, so the steps can be graph-captured
     with torch.cuda.stream(stream):
+        if args.first_request_cell:
+            print(json.dumps(first_request_cell(args, wl, stream, torch)), flush=True)
+            return
         run(args, wl, stream, torch)
 
 
@@ -141,7 +154,10 @@ class Session:
     """Device state of one workload: the cache, the workspace, every step's
     synthetic inputs (written into HBM here, before any timing) and one
     StepPlan per step bound to that step's inputs.  ``force_table`` (host
-    [steps][B] int8) bakes per-step forced flags into the plans."""
+    [steps][B] int8, default all -1: every decision by the head) sets the
+    per-step forced flags; each step's plan reads its row of the device copy,
+    so rewriting ``force_dev`` changes the schedule of graphs already
+    captured."""
 
     def __init__(self, wl, nsteps, stream, theta, force_table=None):
         import torch
@@ -182,7 +198,10 @@ class Session:
         for j in range(nsteps):
             pos_j.copy_(self.t0 + j)
             sd.fill_step({k: v[j] for k, v in self.inp.items()}, wl, pos_j, self.t0)
-        self.force_dev = None if force_table is None else torch.from_numpy(np.asarray(force_table, np.int8)).to(dev)
+        if force_table is None:
+            force_table = np.full((nsteps, B), -1, np.int8)
+        self.force_table = np.asarray(force_table, np.int8)
+        self.force_dev = torch.from_numpy(self.force_table).to(dev)
         self.state = StepBuffers(pos=self.t0.clone(), qL=None, kL=None, vL=None, qF=None, kF=None, vF=None, emb=None,
                                  h_prev=self.h0.clone(), head_w=torch.from_numpy(self.blob).to(dev),
                                  oL=z(L, B, Hq, d), oF=z(L, B, Hq, d), score=z(B, dt=torch.float32),
@@ -192,7 +211,7 @@ class Session:
             b = dataclasses.replace(self.state, qL=self.inp["qL"][j], kL=self.inp["kL"][j], vL=self.inp["vL"][j],
                                     qF=self.inp["qF"][j], kF=self.inp["kF"][j], vF=self.inp["vF"][j],
                                     emb=self.inp["e"][j],
-                                    force=self.state.force if self.force_dev is None else self.force_dev[j])
+                                    force=self.force_dev[j])
             self.plans.append(StepPlan(self.dims, self.kv, self.ws, b, theta=theta, stream=stream))
         self.flag_all = torch.ones(B, dtype=torch.uint8, device=dev)
         # one plan on fixed step buffers, for a single graph that serves every
@@ -211,8 +230,7 @@ class Session:
         j = (self.state.pos[:1] - self.t0[:1]).clamp(0, self.nsteps - 1).long()
         for k, v in self.inp.items():
             torch.index_select(v, 0, j, out=self.buf[k].unsqueeze(0))
-        if self.force_dev is not None:
-            torch.index_select(self.force_dev, 0, j, out=self.state.force.unsqueeze(0))
+        torch.index_select(self.force_dev, 0, j, out=self.state.force.unsqueeze(0))
 
     def fixed_step(self, always_full=False):
         self.feed_fixed()
@@ -283,28 +301,57 @@ class Session:
         return int(self.ws[:4].view(self.torch.int32).item())
 
 
-def run(args, wl, stream, torch):
-    L, B, Hq, Hkv, d, D = wl.layers, wl.batch, wl.hq, wl.hkv, wl.head_dim, wl.hidden
-    t_setup = time.time()
-    nsteps = max(args.steps, args.warmup, 1)
-    S = Session(wl, nsteps, stream, theta=math.inf)
-    setup_s = time.time() - t_setup
-    K = args.steps
+BASELINE_METRIC = "ODA decode steps/s + KV HBM GB/s (% peak) at 128K ctx, 12.5% recall, 1 GPU"
 
-    # ---- calibration: all-local scores -> theta for the target rate
+
+def metric_label(wl) -> str:
+    """The metric text for a workload: context and recall schedule.  For the
+    128K batch of 4 at a 12.5% rate this is exactly the headline metric."""
+    if np.all(wl.t0 == wl.t0[0]):
+        ctx = f"{int(wl.t0[0]) // 1024}K ctx"
+    else:
+        ctx = f"ragged {int(np.min(wl.t0)) // 1024}K-{int(np.max(wl.t0)) // 1024}K ctx"
+    if wl.rate is not None:
+        sched = f"{wl.rate * 100:g}% recall"
+    elif wl.bernoulli_odd is not None:
+        sched = f"recall by the head (theta {wl.theta:g}) on even and Bernoulli({wl.bernoulli_odd:g}) on odd sequences"
+    else:
+        sched = f"recall by the head at theta {wl.theta:g}"
+    return f"ODA decode steps/s + KV HBM GB/s (% peak) at {ctx}, {sched}, 1 GPU"
+
+
+def calibrated_theta(S, K, torch):
+    """theta for the workload's rate from an all-local pass over the K steps
+    (theta = +inf), or the workload's fixed theta; the state is reset."""
+    from conditional_sparse_attention_amd.step import tune_theta
+    wl = S.wl
+    if wl.rate is None:
+        return float(wl.theta), False
+    S.set_theta(math.inf)
     S.reset()
-    scores = torch.zeros((K, B), dtype=torch.float32, device="cuda")
+    scores = torch.zeros((K, wl.batch), dtype=torch.float32, device="cuda")
     for j in range(K):
         S.plans[j].run()
         scores[j].copy_(S.state.score)
     torch.cuda.synchronize()
-    sc = np.sort(scores.cpu().numpy().reshape(-1))[::-1]
-    rate = wl.rate
-    if rate is not None:
-        k = int(round(rate * sc.size))
-        theta = float((sc[k - 1] + sc[k]) / 2) if 0 < k < sc.size else (math.inf if k == 0 else -math.inf)
-    else:
-        theta = float(wl.theta)
+    S.reset()
+    return tune_theta(scores.cpu().numpy(), wl.rate), True
+
+
+def run(args, wl, stream, torch):
+    import synth
+    L, B, Hq, Hkv, d, D = wl.layers, wl.batch, wl.hq, wl.hkv, wl.head_dim, wl.hidden
+    t_setup = time.time()
+    nsteps = max(args.steps, args.warmup, 1)
+    force_table = None
+    if wl.bernoulli_odd is not None:
+        force_table = np.stack([synth.bernoulli_force(wl, j) for j in range(nsteps)])
+    S = Session(wl, nsteps, stream, theta=math.inf, force_table=force_table)
+    setup_s = time.time() - t_setup
+    K = args.steps
+
+    # ---- calibration: all-local scores -> theta for the target rate
+    theta, calibrated = calibrated_theta(S, K, torch)
     S.set_theta(theta)
 
     # ---- warm-up
@@ -317,7 +364,6 @@ def run(args, wl, stream, torch):
     # same start state, REPEATS times; the median is the reported throughput
     graphs = S.capture(lambda j: S.plans[j].run(), K)
     ms_total = S.time_graphs(graphs, args.repeats)
-    del graphs
 
     # ---- the same K steps as four graphs per step (the L local launches |
     # score | the L full-attention launches | commit), a pair of HIP events on
@@ -332,6 +378,7 @@ def run(args, wl, stream, torch):
     pos_hist = torch.zeros((K, B), dtype=torch.int32, device="cuda")
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     ev_loc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    ev_sc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     S.reset()
     torch.cuda.synchronize()
     e_start = torch.cuda.Event(enable_timing=True)
@@ -343,7 +390,10 @@ def run(args, wl, stream, torch):
         l0.record(stream)
         g_loc[j].replay()
         l1.record(stream)
+        s0, s1 = ev_sc[j]
+        s0.record(stream)
         g_score[j].replay()
+        s1.record(stream)
         e0, e1 = ev[j]
         e0.record(stream)
         g_full[j].replay()
@@ -355,6 +405,7 @@ def run(args, wl, stream, torch):
     split_ms = e_start.elapsed_time(e_end)
     full_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev)
     local_ms = sum(l0.elapsed_time(l1) for l0, l1 in ev_loc)
+    score_ms = sum(s0.elapsed_time(s1) for s0, s1 in ev_sc)
     del g_loc, g_score, g_full, g_post
     fl = flags_hist.cpu().numpy().astype(np.int64)
     ps = pos_hist.cpu().numpy().astype(np.int64)
@@ -370,14 +421,10 @@ def run(args, wl, stream, torch):
             t = int(wl.t0[b]) + j + 1
             kv_local += min(t, wl.sink + wl.window)
     kv_bytes_step = (kv_local + float(np.sum(fl * (ps + 1)))) * Hkv * d * 2 * 2 * L / K
-    always_full = None
-    if args.always_full:
-        g_af = S.capture(S.always_full_step, K)
-        m = S.time_graphs(g_af, args.repeats) / K
-        del g_af
-        always_full = {"steps_per_s": round(1000.0 / m, 2), "ms_per_step": round(m, 4)}
+    ctx = int(wl.t0[0]) if np.all(wl.t0 == wl.t0[0]) else f"ragged {int(np.min(wl.t0))}-{int(np.max(wl.t0))}, " \
+                                                             f"mean {float(np.mean(wl.t0)):.0f}"
     out = {
-        "metric": "ODA decode steps/s + KV HBM GB/s (% peak) at 128K ctx, 12.5% recall, 1 GPU",
+        "metric": metric_label(wl),
         "value": round(steps_per_s, 2),
         "unit": "steps/s",
         "n_gpus": 1,
@@ -390,38 +437,63 @@ def run(args, wl, stream, torch):
         "dtype": "bf16",
         "data": "synthetic (seeded generator, inputs device-generated into HBM before timing; random-init Xavier "
                 "recall head)",
-        "config": {"workload": wl.name, "layers": L, "batch": B, "context": int(wl.t0[0]) if np.all(wl.t0 == wl.t0[0])
-                   else f"ragged mean {float(np.mean(wl.t0)):.0f}", "q_heads": Hq,
-                   "kv_heads": Hkv, "head_dim": d, "kv_layout": wl.layout, "recall_rate_target": rate,
-                   "recall_rate_realised": realised, "theta": theta, "tokens_per_s": round(steps_per_s * B, 1),
+        "config": {"workload": wl.name, "layers": L, "batch": B, "context": ctx, "q_heads": Hq,
+                   "kv_heads": Hkv, "head_dim": d, "kv_layout": wl.layout, "recall_rate_target": wl.rate,
+                   "recall_rate_realised": realised, "theta": theta, "theta_calibrated": calibrated,
+                   "tokens_per_s": round(steps_per_s * B, 1),
                    "repeats": args.repeats, "timing": "per-step hip-graph replay, median of repeats",
                    "split_graph_steps_per_s": round(1000.0 * K / split_ms, 2)},
         "kv_gbs": round(kv_bytes_step / (ms_step * 1e-3) / 1e9, 1),
         "kv_frac_peak": round(kv_bytes_step / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
     }
+    if wl.bernoulli_odd is not None:
+        even = np.arange(B) % 2 == 0
+        out["config"]["recall_rate_realised_head_half"] = round(float(fl[:, even].mean()), 4)
+        out["config"]["recall_rate_realised_forced_half"] = round(float(fl[:, ~even].mean()), 4)
     nlaunch = K * L
     avg_us = full_ms * 1e3 / nlaunch
     bytes_per_launch = full_bytes / nlaunch
     achieved = bytes_per_launch / (avg_us * 1e-6) / 1e9
-    traffic, traffic_note = measured_traffic(bytes_per_launch)
+    traffic, traffic_note = measured_traffic(wl.name, bytes_per_launch)
     local_bytes = kv_local * Hkv * d * 2 * 2 * L
+    both_gbs = (local_bytes + full_bytes) / ((local_ms + full_ms) * 1e-3) / 1e9
     out["attention_kernels"] = {
         "local_avg_launch_us": round(local_ms * 1e3 / nlaunch, 2),
         "local_gbs": round(local_bytes / (local_ms * 1e-3) / 1e9, 1),
+        "local_frac": round(local_bytes / (local_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "full_gbs": round(full_bytes / (full_ms * 1e-3) / 1e9, 1),
-        "kv_gbs": round((local_bytes + full_bytes) / ((local_ms + full_ms) * 1e-3) / 1e9, 1),
+        "kv_gbs": round(both_gbs, 1),
+        "kv_frac_peak": round(both_gbs / HBM_PEAK_GBS, 4),
         "note": "KV bytes read / summed launch time of the local and the full attention launches (HIP events "
                 "around each step's graph of L launches; local includes the per-launch split hand-off)"}
+    head_bytes = 4 * synth_head_params(D)
+    out["recall_head"] = {"avg_us_per_step": round(score_ms * 1e3 / K, 2),
+                          "weight_gbs": round(head_bytes / (score_ms * 1e-3 / K) / 1e9, 1),
+                          "frac": round(head_bytes / (score_ms * 1e-3 / K) / 1e9 / HBM_PEAK_GBS, 4),
+                          "note": "oda_recall_score per step (HIP events around its graph): fp32 head weights "
+                                  "streamed once / time"}
+    # dispatch windows of the split region, in this process's launch order,
+    # so a kernel trace of the same command can be cut to the same launches
+    before = (K if calibrated else 0) + args.warmup + args.repeats * K
     out["roofline"] = {"bound": "hbm", "kernel": "k_attn_full (oda_full_attn_if)", "achieved": round(achieved, 1),
                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                        "traffic": traffic, "traffic_note": traffic_note, "avg_launch_us": round(avg_us, 2),
-                       "algorithmic_bytes_per_launch": int(bytes_per_launch), "launches": nlaunch}
-    if always_full is not None:
-        out["always_full"] = always_full
-        out["always_full"]["oda_speedup"] = round(steps_per_s / always_full["steps_per_s"], 3)
+                       "algorithmic_bytes_per_launch": int(bytes_per_launch), "launches": nlaunch,
+                       "duration_source": "HIP events on the launch stream around each step's graph of the L "
+                                          "full-attention launches (empty launches included, with zero bytes)",
+                       "attention_kernels_frac": out["attention_kernels"]["kv_frac_peak"],
+                       "trace_window": {"k_attn_full": [before * L, nlaunch], "k_attn_local": [before * L, nlaunch],
+                                        "k_out_rule": [before, K]}}
+    if args.rate_sweep and wl.bernoulli_odd is None:
+        out["rate_sweep"] = rate_sweep(args, S, graphs)
+    del graphs
+    if not args.no_always_full:
+        g_af = S.capture(S.always_full_step, K)
+        m = S.time_graphs(g_af, args.repeats) / K
+        del g_af
+        out["always_full"] = {"steps_per_s": round(1000.0 / m, 2), "ms_per_step": round(m, 4),
+                              "oda_speedup": round(steps_per_s / (1000.0 / m), 3)}
     out["setup_s"] = round(setup_s, 1)
-    if args.rate_sweep:
-        out["rate_sweep"] = rate_sweep(args, S)
     out["device_copy"] = device_copy_gbs(torch, stream)
     if args.copy_calibration:
         src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
@@ -430,12 +502,74 @@ def run(args, wl, stream, torch):
             dst.copy_(src)
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = 2 * src.numel() * src.element_size()
+    blob = S.blob
+    del S
+    torch.cuda.empty_cache()
+    if not args.no_first_request:
+        out["first_request"] = first_request(args, wl, theta)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, S.blob, theta, realised)
+        out["cpu_baseline"] = cpu_baseline(wl, blob, theta, realised)
     print(json.dumps(out), flush=True)
 
 
-TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "k_attn_full_traffic.json")
+def synth_head_params(hidden: int) -> int:
+    """Recall-head parameter count for input width `hidden` (from the
+    library's packed layout)."""
+    import conditional_sparse_attention_amd as C
+    return C.oda_head_param_count(hidden)
+
+
+def first_request(args, wl, theta):
+    """The pages' first-request protocol (capture included), next to the warm
+    one: each measurement runs in a fresh process (setup untimed), capturing
+    one graph that serves every step and timing capture plus the first K
+    steps; the same process then times the warm median of REPEATS replays of
+    K steps.  ODA with the run's theta, and always-full."""
+    import subprocess
+    res = {"protocol": "fresh process per measurement; cold = capture + first K steps (host clock); warm = median "
+                       "of repeats of K replays of the same single graph; the step's inputs are selected on the "
+                       "device from a resident per-step table inside the graph"}
+    for mode in ("oda", "always-full"):
+        cmd = [sys.executable, os.path.abspath(__file__), "--workload", str(args.workload), "--steps",
+               str(args.steps), "--warmup", str(args.warmup), "--repeats", str(args.repeats),
+               "--first-request-cell", f"{mode}:{theta!r}"]
+        cp = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+        if cp.returncode != 0:
+            raise SystemExit(f"first-request cell {mode} failed ({cp.returncode}): {cp.stderr[-2000:]}")
+        res[mode.replace("-", "_")] = json.loads(cp.stdout.strip().splitlines()[-1])
+    res["speedup_cold"] = round(res["oda"]["cold_steps_per_s"] / res["always_full"]["cold_steps_per_s"], 3)
+    res["speedup_warm"] = round(res["oda"]["warm_steps_per_s"] / res["always_full"]["warm_steps_per_s"], 3)
+    return res
+
+
+def first_request_cell(args, wl, stream, torch):
+    """Child process of first_request(): mode oda:THETA or always-full:THETA."""
+    import synth
+    mode, theta = args.first_request_cell.split(":", 1)
+    K = args.steps
+    nsteps = max(K, args.warmup, 1)
+    force_table = None
+    if wl.bernoulli_odd is not None:
+        force_table = np.stack([synth.bernoulli_force(wl, j) for j in range(nsteps)])
+    S = Session(wl, nsteps, stream, theta=float(theta), force_table=force_table)
+    af = mode == "always-full"
+    S.reset()
+    torch.cuda.synchronize()
+    c0 = time.perf_counter()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        S.fixed_step(always_full=af)
+    for _ in range(K):
+        g.replay()
+    torch.cuda.synchronize()
+    cold_ms = (time.perf_counter() - c0) * 1e3
+    warm_ms = S.time_graphs([g] * K, args.repeats)
+    assert S.error_bits() == 0, "device error bits set"
+    return {"mode": mode, "cold_ms_per_step": round(cold_ms / K, 4), "cold_steps_per_s": round(1e3 * K / cold_ms, 2),
+            "warm_ms_per_step": round(warm_ms / K, 4), "warm_steps_per_s": round(1e3 * K / warm_ms, 2)}
+
+
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = ("conditional_sparse_attention_amd/csrc/attn.hip", "conditional_sparse_attention_amd/csrc/oda_internal.h")
 
 
@@ -471,55 +605,149 @@ def device_copy_gbs(torch, stream, n_bytes=1 << 30, reps=5):
                     "on this box, for reading roofline.frac"}
 
 
-def measured_traffic(bytes_per_launch):
-    """HBM bytes per launch of k_attn_full from the committed rocprofv3 PMC
-    measurement (FETCH_SIZE + WRITE_SIZE, each normalised on a 1 GiB copy),
-    as its ratio to the algorithmic bytes of the measured launches times this
-    run's algorithmic bytes per launch; None if the kernel source changed
-    since the counters were taken."""
+def measured_traffic(workload, bytes_per_launch):
+    """HBM bytes per launch of k_attn_full on this workload from the
+    committed rocprofv3 PMC measurement (FETCH_SIZE + WRITE_SIZE, each
+    normalised on a 1 GiB copy), as its ratio to the algorithmic bytes of the
+    measured launches times this run's algorithmic bytes per launch; None
+    when this kernel and workload were not counted, or the kernel source
+    changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None, "no counter measurement"
-    if rec.get("kernel_source_sha256") != kernel_source_hash():
+    ent = rec.get("k_attn_full", {}).get(workload)
+    if ent is None:
+        return None, f"k_attn_full not counted on {workload}"
+    if ent.get("kernel_source_sha256") != kernel_source_hash():
         return None, "kernel changed since the counters were taken"
-    ratio = rec["hbm_bytes_per_launch"] / rec["algorithmic_bytes_per_launch"]
+    ratio = ent["hbm_bytes_per_launch"] / ent["algorithmic_bytes_per_launch"]
     return int(ratio * bytes_per_launch), f"PMC ratio {ratio:.5f} of algorithmic bytes ({os.path.basename(TRAFFIC_FILE)})"
 
 
-def rate_sweep(args, S):
-    """Step time at forced full-branch rates (exact counts placed by seeded
-    uniforms), to show step time scaling with the recall rate.  Eager
-    launches; the state's force buffer is set before each step."""
+def rate_sweep(args, S, graphs):
+    """Step time at forced full-branch rates: exact counts round(rate * K * B)
+    placed by seeded uniforms (the pages' hand-scheduled calls), replaying
+    the run's per-step graphs with the force table rewritten; then the run's
+    own table is restored."""
     import synth
     torch = S.torch
     wl = S.wl
     res = []
-    saved = S.state.force.clone()
+    saved = S.force_dev.clone()
     for r in [float(x) for x in args.rate_sweep.split(",") if x]:
         flags = synth.forced_rate_flags(wl.seed, args.steps, wl.batch, r)
-        fdev = torch.from_numpy(flags).to("cuda")
-        S.reset()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(S.stream)
-        for j in range(args.steps):
-            S.state.force.copy_(fdev[j])
-            S.plans[j].run()
-        e1.record(S.stream)
-        torch.cuda.synchronize()
-        res.append({"rate": r, "ms_per_step": round(e0.elapsed_time(e1) / args.steps, 4)})
-    S.state.force.copy_(saved)
+        S.force_dev[:args.steps].copy_(torch.from_numpy(flags).to("cuda"))
+        ms = S.time_graphs(graphs, args.repeats) / args.steps
+        res.append({"rate": r, "ms_per_step": round(ms, 4), "steps_per_s": round(1000.0 / ms, 2)})
+    S.force_dev.copy_(saved)
+    torch.cuda.synchronize()
     x = np.array([q["rate"] for q in res])
     y = np.array([q["ms_per_step"] for q in res])
     if len(res) >= 2:
         slope, icpt = np.polyfit(x, y, 1)
         pred = slope * x + icpt
         r2 = 1 - np.sum((y - pred) ** 2) / max(np.sum((y - y.mean()) ** 2), 1e-30)
-        return {"points": res, "fit_ms_per_step": {"slope_per_unit_rate": round(float(slope), 4),
-                                                   "intercept": round(float(icpt), 4), "r2": round(float(r2), 5)}}
+        return {"points": res, "timing": "per-step hip-graph replay, median of repeats",
+                "fit_ms_per_step": {"slope_per_unit_rate": round(float(slope), 4),
+                                    "intercept": round(float(icpt), 4), "r2": round(float(r2), 5)}}
     return {"points": res}
+
+
+def _short_kernel_name(name: str) -> str:
+    """'void ns::(anonymous namespace)::k_x<2, false>(ns::P)' -> 'k_x<2, false>'."""
+    n = name.strip().strip('"')
+    depth, cut = 0, len(n)
+    for i in range(len(n) - 1, -1, -1):  # drop the trailing parameter list
+        c = n[i]
+        if c == ")":
+            depth += 1
+        elif c == "(":
+            depth -= 1
+            if depth == 0:
+                cut = i
+                break
+    n = n[:cut]
+    depth, start = 0, 0
+    for i, c in enumerate(n):  # last '::' outside template brackets
+        if c == "<":
+            depth += 1
+        elif c == ">":
+            depth -= 1
+        elif c == ":" and depth == 0 and i + 1 < len(n) and n[i + 1] == ":":
+            start = i + 2
+    n = n[start:]
+    return n[5:] if n.startswith("void ") else n
+
+
+def trace_summary(trace_dir: str, bench_json: str) -> None:
+    """Markdown summary of a rocprofv3 kernel trace of one bench run.  The
+    process with the most k_attn_full dispatches is the bench itself (its
+    first-request children trace separately).  Its kernels are listed over
+    the whole run and over the split-graph region: the time span from the
+    first k_attn_local to the last k_attn_full dispatch of the windows the
+    bench's JSON line gives (dispatch order within the process)."""
+    import csv
+    import glob
+    with open(bench_json) as f:
+        line = [l for l in f.read().splitlines() if l.strip().startswith("{")][-1]
+    rec = json.loads(line)
+    win = rec["roofline"]["trace_window"]
+    per_file = {}
+    for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path, newline="") as f:
+            rows = [(r["Kernel_Name"], int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in csv.DictReader(f)]
+        per_file[path] = rows
+    if not per_file:
+        raise SystemExit(f"no *kernel_trace.csv under {trace_dir}")
+    path, rows = max(per_file.items(), key=lambda kv: sum("k_attn_full" in r[0] for r in kv[1]))
+    rows.sort(key=lambda r: r[1])
+
+    def stats(sel):
+        agg = {}
+        for name, t0, t1 in sel:
+            a = agg.setdefault(_short_kernel_name(name), [0, 0.0, math.inf, 0.0])
+            us = (t1 - t0) / 1e3
+            a[0] += 1
+            a[1] += us
+            a[2] = min(a[2], us)
+            a[3] = max(a[3], us)
+        return sorted(agg.items(), key=lambda kv: -kv[1][1])
+
+    def window(kernel):
+        first, n = win[kernel]
+        ds = [r for r in rows if kernel in r[0]]
+        return ds[first:first + n]
+
+    wl_full, wl_local = window("k_attn_full"), window("k_attn_local")
+    t_lo, t_hi = wl_local[0][1], wl_full[-1][2]
+    region = [r for r in rows if r[1] >= t_lo and r[2] <= t_hi]
+    K = rec["steps"]
+    full_avg = sum((t1 - t0) for _, t0, t1 in wl_full) / len(wl_full) / 1e3
+    local_avg = sum((t1 - t0) for _, t0, t1 in wl_local) / len(wl_local) / 1e3
+    bpl = rec["roofline"]["algorithmic_bytes_per_launch"]
+    frac = bpl / (full_avg * 1e-6) / 1e9 / HBM_PEAK_GBS
+    cfg = rec["config"]
+    out = [f"# Kernel trace of one bench run: {cfg['workload']}", "",
+           f"Trace file: `{os.path.relpath(path, trace_dir)}` (the bench process). JSON line: `{rec['metric']}`, "
+           f"value {rec['value']} {rec['unit']}, {K} steps, warm-up {rec['warmup']}.", "",
+           "## Split-graph region (the launches the line's roofline and attention_kernels time)", "",
+           f"{len(region)} dispatches, {K} steps; `k_attn_full` dispatches {win['k_attn_full'][0]}.."
+           f"{win['k_attn_full'][0] + win['k_attn_full'][1] - 1} of the process.", "",
+           "| kernel | calls | total (us) | avg (us) | min (us) | max (us) | per step (us) |", "|---|---|---|---|---|---|---|"]
+    for name, (n, tot, mn, mx) in stats(region):
+        out.append(f"| `{name}` | {n} | {tot:.1f} | {tot / n:.2f} | {mn:.2f} | {mx:.2f} | {tot / K:.2f} |")
+    out += ["", "| quantity | kernel trace | the line (HIP events) |", "|---|---|---|",
+            f"| `k_attn_full` avg launch (us) | {full_avg:.2f} | {rec['roofline']['avg_launch_us']} |",
+            f"| `k_attn_full` frac of 8 TB/s ({bpl} algorithmic B per launch) | {frac:.4f} | "
+            f"{rec['roofline']['frac']} |",
+            f"| `k_attn_local` avg launch (us) | {local_avg:.2f} | {rec['attention_kernels']['local_avg_launch_us']} |",
+            "", "## Whole process", "",
+            "| kernel | calls | total (us) | avg (us) | min (us) | max (us) |", "|---|---|---|---|---|---|"]
+    for name, (n, tot, mn, mx) in stats(rows)[:25]:
+        out.append(f"| `{name}` | {n} | {tot:.1f} | {tot / n:.2f} | {mn:.2f} | {mx:.2f} |")
+    print("\n".join(out))
 
 
 def host_cpu_model() -> str:

@@ -40,15 +40,6 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const v4u_t gv4_t;
 
-// How splits of one (b, g) hand their partials to the last one:
-//  1 (default): partials are written and read with agent-scope coherent
-//    accesses (no L2 write-back / invalidate); the ticket is taken after the
-//    workgroup's stores have been acknowledged;
-//  0: plain stores and a device-wide fence around the ticket.
-#ifndef ODA_SPLIT_SYNC
-#define ODA_SPLIT_SYNC 1
-#endif
-
 #ifndef ODA_LOCAL_DEPTH
 #define ODA_LOCAL_DEPTH 2
 #endif
@@ -374,52 +365,46 @@ __device__ __forceinline__ void current_row(const AttnParams& P, const uint4 (&q
 
 __device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(x, m, 64); }
 
-// Partials cross workgroups (and XCDs, whose L2s are not coherent with each
-// other): store / load them with agent-scope coherent accesses.
+// Split hand-off.  The workgroups of one (b, g) may run on different XCDs,
+// whose L2 caches are not coherent with each other, so partials never go
+// through a cached path: they are stored and loaded with agent-scope atomic
+// accesses.  On gfx950 those loads and stores carry the device-scope cache
+// policy (sc1: coherent across the XCDs, not served from a stale L2 line),
+// and atomic read-modify-writes at agent scope are device coherent.  The
+// ordering argument, in hardware terms:
+//  1. each thread's partial stores are issued, then s_waitcnt vmcnt(0) waits
+//     until all of them are acknowledged (gfx9 counts stores in vmcnt, and a
+//     device-scope store is acknowledged once it is visible device-wide);
+//  2. a workgroup barrier, so every wave of the workgroup has passed 1;
+//  3. one thread takes the ticket with a returning agent-scope atomic add
+//     (performed at the coherence point; it is issued only after 2);
+//  4. the workgroup that reads nsplit - 1 uses the returned value (so its
+//     wave waited for the atomic to complete), publishes it through LDS and a
+//     barrier, and only then issues its agent-scope loads of the partials.
+// Every other workgroup's atomic preceded the last one's, and followed that
+// workgroup's acknowledged stores, so the loads of 4 observe every partial.
+// No float atomics: the merge adds the partials in split order.
 __device__ __forceinline__ void part_store(float* p, float v) {
-#if ODA_SPLIT_SYNC
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#else
-  *p = v;
-#endif
 }
 __device__ __forceinline__ float part_load(const float* p) {
-#if ODA_SPLIT_SYNC
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#else
-  return *p;
-#endif
 }
 
-// Takes the (b, g) ticket after this workgroup's partial is visible;
-// returns true in the workgroup that completes the set.
+// Takes the (b, g) ticket after this workgroup's partial is visible (steps 1
+// to 4 above); returns true in the workgroup that completes the set.
 __device__ __forceinline__ bool take_ticket(int32_t* ticket, int nsplit) {
   __shared__ int s_last;
-#if ODA_SPLIT_SYNC
-  // every coherent store of this wave has been acknowledged (gfx9 counts
-  // stores in vmcnt), then all waves meet, then one thread takes the ticket
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0)
     s_last = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
   __syncthreads();
   return s_last;
-#else
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(ticket, 1) == nsplit - 1;
-  __syncthreads();
-  if (s_last) __threadfence();
-  return s_last;
-#endif
 }
 
 __device__ __forceinline__ void reset_ticket(int32_t* ticket) {
-#if ODA_SPLIT_SYNC
   __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#else
-  atomicExch(ticket, 0);
-#endif
 }
 
 // Merge the 4 row groups of each wave (shuffles), then the NW waves (LDS).

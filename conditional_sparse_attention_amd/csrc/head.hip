@@ -571,7 +571,14 @@ __global__ void __launch_bounds__(NW * 64) k_dense(DenseArgs A) {
     }
   }
 
-  // ---- hand-off: the last workgroup of the row block finishes it
+  // ---- hand-off: the last workgroup of the row block finishes it.  The
+  // partial tiles were stored with agent-scope atomic stores, which gfx950
+  // issues with the device-scope cache policy (coherent across the XCDs);
+  // s_waitcnt vmcnt(0) waits for their acknowledgement (gfx9 counts stores in
+  // vmcnt), the barrier makes that hold for every wave, and only then is the
+  // returning agent-scope ticket taken.  The workgroup that completes the set
+  // uses the returned value before it issues its agent-scope partial loads,
+  // so every earlier workgroup's acknowledged stores precede them.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0)

@@ -104,3 +104,23 @@ class StepPlan:
         self.score()
         self.full()
         self.commit()
+
+
+def tune_theta(scores, rate: float) -> float:
+    """Threshold that sends a fraction `rate` of the given recall scores to
+    the full branch under the strict rule q > theta [On-Demand Attention
+    notes §2.3]: the midpoint between the k-th and (k+1)-th largest score,
+    k = round(rate * n).  k = 0 gives +inf (never full), k = n gives -inf.
+    The pages treat the threshold as a tunable knob; this is how a target
+    call rate is turned into one from a calibration pass (all-local scores)."""
+    import math
+
+    import numpy as np
+
+    sc = np.sort(np.asarray(scores, dtype=np.float64).reshape(-1))[::-1]
+    k = int(round(rate * sc.size))
+    if k <= 0:
+        return math.inf
+    if k >= sc.size:
+        return -math.inf
+    return float((sc[k - 1] + sc[k]) / 2)

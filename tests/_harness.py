@@ -14,6 +14,8 @@ sequences, and the commit with the GPU's flags, and compares:
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 import torch
 
@@ -38,6 +40,9 @@ def from_dev_u16(t: torch.Tensor) -> np.ndarray:
 
 
 def assert_close_bf16(gpu_bits: np.ndarray, ref: np.ndarray, what: str) -> None:
+    gpu_bits, ref = np.asarray(gpu_bits), np.asarray(ref)
+    if gpu_bits.size == 0 or gpu_bits.shape != ref.shape:
+        raise AssertionError(f"{what}: nothing compared (gpu shape {gpu_bits.shape}, oracle shape {ref.shape})")
     g = synth.bf16_bits_to_f32(gpu_bits).astype(np.float64)
     err = np.abs(g - ref)
     bad = err > ATOL + RTOL * np.abs(ref)
@@ -291,9 +296,26 @@ class BigProblem:
         self.feed = {"qL": self.pr.bufs.qL, "qF": self.pr.bufs.qF, "kL": self.pr.bufs.kL, "vL": self.pr.bufs.vL,
                      "kF": self.pr.bufs.kF, "vF": self.pr.bufs.vF, "e": self.pr.bufs.emb}
 
+    def reset(self) -> None:
+        """Back to the state before step 0 (pos = t0, h_prev = its initial
+        value).  Slots written by earlier passes lie at positions >= t0 and are
+        rewritten by the new pass before any step reads them."""
+        self.pr.bufs.pos.copy_(self.pr.t0_dev)
+        self.pr.bufs.h_prev.copy_(to_dev_u16(synth.h_prev0(self.wl)))
+        self.flags = []
+
+    def calibrate_theta(self, steps: int, rate: float) -> float:
+        """The benchmark's threshold for a target call rate: the steps run
+        all-local (theta = +inf), the threshold sends round(rate * B * steps)
+        of their scores to the full branch; then the state is reset."""
+        from conditional_sparse_attention_amd.step import tune_theta
+        B = self.wl.batch
+        scores = [self.run_step(j, math.inf, np.full(B, -1, np.int8))["score"] for j in range(steps)]
+        self.reset()
+        return tune_theta(np.concatenate(scores), rate)
+
     def run_step(self, j: int, theta: float, force) -> dict:
         pr, wl = self.pr, self.wl
-        L, B, Hq, d = wl.layers, wl.batch, wl.hq, wl.head_dim
         pos_before = pr.bufs.pos.cpu().numpy().copy()
         assert np.all(pos_before == wl.t0 + j)
         self.sd.fill_step(self.feed, wl, pr.bufs.pos, pr.t0_dev)
@@ -315,34 +337,45 @@ class BigProblem:
     def history(self, l: int, b: int, g: int, j: int, rows: np.ndarray):
         """K, V bits [len(rows)][d] of logical positions `rows` as committed
         before step j."""
+        return self._history(l, b, g, j, rows, self.flags, None)
+
+    def _history(self, l, b, g, j, rows, flags, base):
+        """As history(), with the GPU flags of steps < j given, and optionally
+        a cached (lo, K, V) block of the initial cache covering the old rows."""
         wl = self.wl
         t0 = int(wl.t0[b])
+        rows = np.asarray(rows, dtype=np.int64)
         K = np.zeros((len(rows), wl.head_dim), np.uint16)
         V = np.zeros_like(K)
         old = rows < t0
         if np.any(old):
             idx = np.nonzero(old)[0]
             r = rows[idx]
-            # contiguous runs of positions
-            cuts = np.nonzero(np.diff(r) != 1)[0] + 1
-            for seg_i, seg_r in zip(np.split(idx, cuts), np.split(r, cuts)):
-                lo, hi = int(seg_r[0]), int(seg_r[-1]) + 1
-                K[seg_i] = synth.cache_rows(wl, synth.TAG_K, l, b, g, lo, hi)
-                V[seg_i] = synth.cache_rows(wl, synth.TAG_V, l, b, g, lo, hi)
+            if base is not None:
+                lo, Kb, Vb = base
+                assert r.min() >= lo and r.max() < lo + len(Kb)
+                K[idx] = Kb[r - lo]
+                V[idx] = Vb[r - lo]
+            else:
+                cuts = np.nonzero(np.diff(r) != 1)[0] + 1
+                for seg_i, seg_r in zip(np.split(idx, cuts), np.split(r, cuts)):
+                    lo, hi = int(seg_r[0]), int(seg_r[-1]) + 1
+                    K[seg_i] = synth.cache_rows(wl, synth.TAG_K, l, b, g, lo, hi)
+                    V[seg_i] = synth.cache_rows(wl, synth.TAG_V, l, b, g, lo, hi)
         for i in np.nonzero(~old)[0]:
             jj = int(rows[i]) - t0
             assert jj < j
-            br = "F" if self.flags[jj][b] else "L"
+            br = "F" if flags[jj][b] else "L"
             K[i] = synth.step_tensor(wl, "k" + br, jj, l)[b, g]
             V[i] = synth.step_tensor(wl, "v" + br, jj, l)[b, g]
         return K, V
 
-    def check(self, rec: dict, samples, full_samples) -> None:
-        """Checks every score / flag / work-list entry / commit of the step,
-        and the attention outputs of the sampled (l, b, g)."""
+    def check_step(self, rec: dict) -> None:
+        """Every score, flag (outside the tie band), the work list, the
+        untouched full rows of unflagged sequences, every h_prev and pos, and
+        the committed slots of the first and the last layer."""
         wl, pr = self.wl, self.pr
-        L, B, Hq, Hkv, d = wl.layers, wl.batch, wl.hq, wl.hkv, wl.head_dim
-        G = Hq // Hkv
+        L, B = wl.layers, wl.batch
         j = rec["j"]
         P = pr.head_params()
         emb = synth.embedding(wl, j)
@@ -357,7 +390,6 @@ class BigProblem:
         for b in range(B):
             if not flag[b]:
                 assert np.all(rec["oF"][:, b] == 0x7FC1), "unflagged full rows written"
-        # commit, all b, sampled layers
         assert np.array_equal(rec["pos_after"], rec["pos"] + 1)
         for b in range(B):
             o_last = rec["oF"][L - 1, b] if flag[b] else rec["oL"][L - 1, b]
@@ -368,22 +400,107 @@ class BigProblem:
                 ks, vs = pr.cache_slot(l, b, p)
                 assert np.array_equal(ks, synth.step_tensor(wl, "k" + br, j, l)[b])
                 assert np.array_equal(vs, synth.step_tensor(wl, "v" + br, j, l)[b])
-        # attention outputs
-        for kind, smp in (("L", samples), ("F", full_samples)):
-            for (l, b, g) in smp:
-                if kind == "F" and not flag[b]:
-                    continue
-                p = int(rec["pos"][b])
-                S = local_index_set(p + 1, wl.sink, wl.window) if kind == "L" else full_index_set(p + 1)
-                rows = S[S < p]
-                K, V = self.history(l, b, g, j, rows)
-                Kh = np.zeros((1, p, d), np.uint16)
-                Vh = np.zeros_like(Kh)
-                Kh[0, rows] = K
-                Vh[0, rows] = V
-                qv = synth.step_tensor(wl, "q" + kind, j, l)[b, g * G:(g + 1) * G]
-                kc = synth.step_tensor(wl, "k" + kind, j, l)[b, g:g + 1]
-                vc = synth.step_tensor(wl, "v" + kind, j, l)[b, g:g + 1]
-                ref = decode_attention(qv, Kh, Vh, kc, vc, S)
-                got = (rec["oL"] if kind == "L" else rec["oF"])[l, b, g * G:(g + 1) * G]
-                assert_close_bf16(got, ref, f"{wl.name} step {j} {kind} l={l} b={b} g={g} pos={p}")
+
+    def resolve_full(self, rec: dict, samples):
+        """Full-branch samples of a step: (l, b, g) with an unflagged b is
+        moved to the flagged sequence flagged[b % F]; none when F = 0."""
+        flagged = [int(b) for b in np.nonzero(rec["flag"])[0]]
+        out = []
+        for (l, b, g) in samples:
+            self._guard(l, b, g)
+            if not flagged:
+                continue
+            out.append((l, b if rec["flag"][b] else flagged[b % len(flagged)], g))
+        return out
+
+    def _guard(self, l, b, g) -> None:
+        wl = self.wl
+        if not (0 <= l < wl.layers and 0 <= b < wl.batch and 0 <= g < wl.hkv):
+            raise AssertionError(f"sample (l={l}, b={b}, g={g}) outside L={wl.layers}, B={wl.batch}, "
+                                 f"Hkv={wl.hkv}")
+
+    def check(self, rec: dict, samples, full_samples):
+        """check_step(), then the attention outputs of the sampled (l, b, g)
+        (local) and full_samples (full branch; see resolve_full).  Returns
+        the numbers of local and full outputs compared."""
+        self.check_step(rec)
+        loc = []
+        for (l, b, g) in samples:
+            self._guard(l, b, g)
+            loc.append((rec["j"], "L", l, b, g))
+        full = [(rec["j"], "F", l, b, g) for (l, b, g) in self.resolve_full(rec, full_samples)]
+        recs = {rec["j"]: rec}
+        return (check_outputs(self, recs, loc, flags=self.flags, workers=1),
+                check_outputs(self, recs, full, flags=self.flags, workers=1))
+
+
+def check_outputs(bp: BigProblem, recs: dict, picks, *, flags, workers: int = None) -> int:
+    """Attention outputs of `picks` = (j, kind, l, b, g), kind "L" or "F",
+    against the oracle computed one by one from the regenerated history
+    (the initial cache from G, later slots from the branch the GPU flags of
+    earlier steps chose).  Picks are grouped by (l, b, g) so each history is
+    generated once; groups run on a thread pool.  Returns the number of
+    outputs compared (a full pick of an unflagged sequence is an error)."""
+    import os
+    from collections import defaultdict
+    from concurrent.futures import ThreadPoolExecutor
+
+    wl = bp.wl
+    G = wl.hq // wl.hkv
+    d = wl.head_dim
+    by = defaultdict(list)
+    for (j, kind, l, b, g) in picks:
+        bp._guard(l, b, g)
+        rec = recs[j]
+        assert kind in ("L", "F")
+        if kind == "F":
+            assert rec["flag"][b], f"full sample of unflagged sequence {b} at step {j}"
+        by[(l, b, g)].append((j, kind))
+
+    def work(key):
+        l, b, g = key
+        items = sorted(set(by[key]))
+        t0 = int(wl.t0[b])
+        if any(k == "F" for _, k in items):
+            lo, hi = 0, t0
+        else:
+            lo, hi = max(0, t0 - wl.window), t0
+        # rows of the initial cache this group reads: all of them for a full
+        # pick, else the sink and the last window before t0
+        Kb = np.zeros((t0, d), np.uint16)
+        Vb = np.zeros_like(Kb)
+        have = np.zeros(t0, bool)
+        for r0, r1 in ((0, min(wl.sink, t0)), (lo, hi)):
+            if r1 > r0 and not have[r0:r1].all():
+                Kb[r0:r1] = synth.cache_rows(wl, synth.TAG_K, l, b, g, r0, r1)
+                Vb[r0:r1] = synth.cache_rows(wl, synth.TAG_V, l, b, g, r0, r1)
+                have[r0:r1] = True
+        n = 0
+        for j, kind in items:
+            rec = recs[j]
+            p = int(rec["pos"][b])
+            assert p == t0 + j
+            S = local_index_set(p + 1, wl.sink, wl.window) if kind == "L" else full_index_set(p + 1)
+            rows = S[S < p]
+            assert have[rows[rows < t0]].all()
+            K, V = bp._history(l, b, g, j, rows, flags, (0, Kb, Vb))
+            Kh = np.zeros((1, p, d), np.uint16)
+            Vh = np.zeros_like(Kh)
+            Kh[0, rows] = K
+            Vh[0, rows] = V
+            qv = synth.step_tensor(wl, "q" + kind, j, l)[b, g * G:(g + 1) * G]
+            kc = synth.step_tensor(wl, "k" + kind, j, l)[b, g:g + 1]
+            vc = synth.step_tensor(wl, "v" + kind, j, l)[b, g:g + 1]
+            ref = decode_attention(qv, Kh, Vh, kc, vc, S)
+            got = (rec["oL"] if kind == "L" else rec["oF"])[l, b, g * G:(g + 1) * G]
+            assert_close_bf16(got, ref, f"{wl.name} step {j} {kind} l={l} b={b} g={g} pos={p}")
+            n += 1
+        return n
+
+    keys = sorted(by)
+    if workers is None:
+        workers = min(16, os.cpu_count() or 1)
+    if workers <= 1 or len(keys) <= 1:
+        return sum(work(k) for k in keys)
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        return sum(ex.map(work, keys))
