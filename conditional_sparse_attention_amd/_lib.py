@@ -29,6 +29,8 @@ ODA_FULL_FINE_CHUNK = 256
 ODA_FULL_FILL_UNITS = 128
 ODA_FULL_ROUND_UNITS = 256
 ODA_FULL_MAX_SPLITS = 32
+ODA_FULL_RAGGED_ROUNDS = 4
+ODA_FULL_UNIT_COST_KEYS = 128
 
 EXPORTED = (
     "oda_abi_version", "oda_status_str", "oda_head_param_count", "oda_head_offsets",

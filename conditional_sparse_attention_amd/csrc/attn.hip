@@ -667,35 +667,62 @@ __global__ void __launch_bounds__(kLocalWaves * 64) k_attn_local(AttnParams P) {
   attn_unit<G, PAGED, NW, ODA_LOCAL_DEPTH, ODA_LOCAL_U, kLocalSplitsMax, ROPE>(P, b, g, split, ns, v_lo, v_hi, S, P.tickets + b * P.Hkv + g, part_bg, lds);
 }
 
+// The persistent grid walks units u = (work-list item) * Hkv + KV head.
+// Workgroup i takes unit i; when the list holds more units than the grid,
+// the rest are handed out in list order (largest units first) through an
+// atomic counter, each workgroup asking for its next unit while it streams
+// the current one.  Once every workgroup has found the list exhausted, the
+// last one to finish clears the counters, so each launch starts from zero.
 template <int G, bool PAGED>
 __global__ void __launch_bounds__(FullWaves<G>::value * 64) k_attn_full(AttnParams P) {
   constexpr int NW = FullWaves<G>::value;
   __shared__ float lds[lds_floats<G, NW>()];
+  __shared__ int s_next;
   int count = P.worklist[0];
   count = count < 0 ? 0 : (count > P.B * kFullMaxSplits ? P.B * kFullMaxSplits : count);
   const int units = count * P.Hkv;
-  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+  const int grid = (int)gridDim.x;
+  const bool queued = units > grid;
+  int u = blockIdx.x;
+  while (u < units) {
+    int next = 0;
+    if (queued && threadIdx.x == 0)
+      next = grid + __hip_atomic_fetch_add(P.queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int item = P.worklist[1 + u / P.Hkv];
     const int g = u % P.Hkv;
     const int b = item >> 20;
     const int ns = (item >> 10) & 0x3FF;
     const int split = item & 0x3FF;
-    if (b < 0 || b >= P.B || ns < 1 || ns > kFullMaxSplits || split >= ns) continue;
-    const int pos = P.pos[b];
+    const int pos = (b >= 0 && b < P.B) ? P.pos[b] : -1;
     const int t = pos + 1;
-    if (pos < 0 || (int64_t)t > P.t_max) {
+    if (b < 0 || b >= P.B || ns < 1 || ns > kFullMaxSplits || split >= ns) {
+      // malformed item: skipped
+    } else if (pos < 0 || (int64_t)t > P.t_max) {
       if (split == 0 && g == 0 && threadIdx.x == 0) atomicOr(P.err, ODA_ERR_CAPACITY);
-      continue;
+    } else {
+      const int chunk = (t + ns - 1) / ns;
+      const int v_lo = split * chunk;
+      const int v_hi = (v_lo + chunk) < t ? v_lo + chunk : t;
+      LocalSet S;
+      S.n0 = t;
+      S.s1 = t;
+      S.t = t;
+      float* part_bg = P.part + ((size_t)(b * P.Hkv + g) * kFullMaxSplits) * G * kPartStride;
+      attn_unit<G, PAGED, NW, FullDepth<G, PAGED>::value, ODA_FULL_U, kFullMaxSplits, false>(P, b, g, split, ns, v_lo, v_hi, S, P.tickets + b * P.Hkv + g, part_bg, lds);
     }
-    const int chunk = (t + ns - 1) / ns;
-    const int v_lo = split * chunk;
-    const int v_hi = (v_lo + chunk) < t ? v_lo + chunk : t;
-    LocalSet S;
-    S.n0 = t;
-    S.s1 = t;
-    S.t = t;
-    float* part_bg = P.part + ((size_t)(b * P.Hkv + g) * kFullMaxSplits) * G * kPartStride;
-    attn_unit<G, PAGED, NW, FullDepth<G, PAGED>::value, ODA_FULL_U, kFullMaxSplits, false>(P, b, g, split, ns, v_lo, v_hi, S, P.tickets + b * P.Hkv + g, part_bg, lds);
+    if (!queued) break;
+    if (threadIdx.x == 0) s_next = next;
+    __syncthreads();
+    u = s_next;
+    __syncthreads();
+  }
+  if (queued && threadIdx.x == 0) {
+    if (__hip_atomic_fetch_add(P.queue + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == grid - 1) {
+      // every other workgroup has drawn past the end and will not touch the
+      // counters again in this launch
+      __hip_atomic_store(P.queue, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(P.queue + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 

@@ -282,29 +282,85 @@ struct OutArgs {
 };
 
 // Lane b < B of one wave (B <= 32) holds sequence b's flag f and position:
-// the split count of the policy, which depends on how many lanes are flagged.
+// its split count under the policy stated in oda.h, which depends on every
+// flagged lane (their number, their keys together, and the cost of the two
+// candidate cuts summed or maximised over the wave).
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
+  return x;
+}
+__device__ __forceinline__ int wave_max_i32(int x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const int y = __shfl_xor(x, d, 64);
+    x = x > y ? x : y;
+  }
+  return x;
+}
+__device__ __forceinline__ int wave_min_i32(int x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const int y = __shfl_xor(x, d, 64);
+    x = x < y ? x : y;
+  }
+  return x;
+}
 __device__ __forceinline__ int split_count(bool f, int pos, int lane, int B, int hkv) {
-  const int nflag = __popcll(__ballot(f && lane < B));
-  return f ? full_nsplit(pos + 1, nflag, hkv) : 0;
+  const bool on = f && lane < B;
+  const int nflag = __popcll(__ballot(on));
+  const int t = pos + 1;
+  const int64_t total = wave_sum_i64(on ? (int64_t)t : 0);
+  const int na = on ? full_nsplit_round(t, nflag, hkv, total) : 0;
+  const int nb = on ? full_nsplit_rounds(t, hkv, total) : 0;
+  const int64_t units_a = wave_sum_i64((int64_t)na * hkv);
+  const int64_t units_b = wave_sum_i64((int64_t)nb * hkv);
+  const int ua = na > 0 ? (t + na - 1) / na : 0;
+  const int ub = nb > 0 ? (t + nb - 1) / nb : 0;
+  const int long_a = wave_max_i32(ua), long_b = wave_max_i32(ub);
+  const int short_a = wave_min_i32(on ? ua : 0x7FFFFFFF), short_b = wave_min_i32(on ? ub : 0x7FFFFFFF);
+  const int64_t cost_a = full_split_cost(units_a, long_a, short_a, total, hkv);
+  const int64_t cost_b = full_split_cost(units_b, long_b, short_b, total, hkv);
+  return cost_b < cost_a ? nb : na;
 }
 
-// Exclusive scan of the per-sequence split counts (lanes < B of one wave,
-// B <= 32) and the compacted items (b << 20) | (nsplit << 10) | split,
-// b ascending.
-__device__ __forceinline__ void write_worklist(int cnt, int lane, int B, int* s_start, const int* s_count,
+// The compacted work list in the policy's order: flagged sequences by
+// descending unit length ceil(t / nsplit) (ties by ascending b), each with
+// its items (b << 20) | (nsplit << 10) | split for split = 0 .. nsplit-1.
+// Lanes < B of one wave (B <= 32) hold cnt = nsplit (0 when unflagged) and
+// t = pos + 1.  Each lane ranks itself against every other lane, the counts
+// are placed in rank order in LDS, an exclusive scan over ranks gives the
+// start of each sequence's items.
+__device__ __forceinline__ void write_worklist(int cnt, int t, int lane, int B, int* s_start, int* s_count,
                                                int32_t* worklist) {
-  int incl = cnt;
+  const int unit = cnt > 0 ? (t + cnt - 1) / cnt : 0;
+  // every lane of the wave runs this loop (the shuffles need them all)
+  int rank = 0, rank_unflagged = 0;
+  for (int o = 0; o < kMaxBatch; ++o) {
+    const int c_o = __shfl(cnt, o, 64);
+    const int u_o = __shfl(unit, o, 64);
+    const bool flagged_o = o < B && c_o > 0;
+    if (flagged_o && (u_o > unit || (u_o == unit && o < lane))) ++rank;
+    if (o < B && !flagged_o && o < lane) ++rank_unflagged;
+  }
+  // unflagged lanes rank after every flagged one, in lane order
+  const int nflag = __popcll(__ballot(cnt > 0 && lane < B));
+  if (cnt == 0) rank = nflag + rank_unflagged;
+  if (lane < B) s_count[rank] = cnt;
+  __builtin_amdgcn_wave_barrier();
+  const int c_r = lane < B ? s_count[lane] : 0;  // count of the sequence ranked `lane`
+  int incl = c_r;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const int v = __shfl_up(incl, d, 64);
     if (lane >= d) incl += v;
   }
-  if (lane < B) s_start[lane] = incl - cnt;
+  if (lane < B) s_start[lane] = incl - c_r;  // start of rank `lane`
   if (lane == B - 1) worklist[0] = incl;
   __builtin_amdgcn_wave_barrier();
-  for (int i = lane; i < B * kFullMaxSplits; i += 64) {
-    const int b = i / kFullMaxSplits, s = i % kFullMaxSplits;
-    if (s < s_count[b]) worklist[1 + s_start[b] + s] = full_item(b, s_count[b], s);
+  if (lane < B && cnt > 0) {
+    const int st = s_start[rank];
+    for (int s = 0; s < cnt; ++s) worklist[1 + st + s] = full_item(lane, cnt, s);
   }
 }
 
@@ -343,8 +399,7 @@ __global__ void __launch_bounds__(kThreads) k_out_rule(OutArgs A) {
     pos = A.pos[lane];
   }
   const int cnt = split_count(f != 0, pos, lane, A.B, A.Hkv);
-  if (lane < A.B) s_count[lane] = cnt;
-  write_worklist(cnt, lane, A.B, s_start, s_count, A.worklist);
+  write_worklist(cnt, pos + 1, lane, A.B, s_start, s_count, A.worklist);
 }
 
 __global__ void __launch_bounds__(64) k_worklist(const uint8_t* flag, const int32_t* pos, int32_t* worklist, int B,
@@ -353,9 +408,9 @@ __global__ void __launch_bounds__(64) k_worklist(const uint8_t* flag, const int3
   __shared__ int s_count[kMaxBatch];
   const int lane = threadIdx.x;
   const bool f = lane < B && flag[lane] != 0;
-  const int cnt = split_count(f, lane < B ? pos[lane] : 0, lane, B, hkv);
-  if (lane < B) s_count[lane] = cnt;
-  write_worklist(cnt, lane, B, s_start, s_count, worklist);
+  const int p = lane < B ? pos[lane] : 0;
+  const int cnt = split_count(f, p, lane, B, hkv);
+  write_worklist(cnt, p + 1, lane, B, s_start, s_count, worklist);
 }
 
 // ------------------------------------------------ dense batches: fp32 MFMA

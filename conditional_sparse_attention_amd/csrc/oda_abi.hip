@@ -101,9 +101,9 @@ static int head_offsets_impl(int32_t hidden, int64_t* offs) {
   return ODA_OK;
 }
 
-static AttnParams attn_params(const oda_dims* d, int32_t layer, const oda_kv* kv, const int32_t* pos,
-                              const oda_bf16* q, const oda_bf16* kc, const oda_bf16* vc, oda_bf16* out, float* lse,
-                              void* ws, const WsLayout& L, bool full) {
+AttnParams attn_params_at(const oda_dims* d, int32_t layer, const oda_kv* kv, const int32_t* pos, const oda_bf16* q,
+                          const oda_bf16* kc, const oda_bf16* vc, oda_bf16* out, float* lse, float* part,
+                          int32_t* tickets, int32_t* header, const int32_t* worklist) {
   AttnParams p;
   memset(&p, 0, sizeof(p));
   size_t layer_stride;
@@ -125,31 +125,49 @@ static AttnParams attn_params(const oda_dims* d, int32_t layer, const oda_kv* kv
   p.vc = vc;
   p.out = out;
   p.lse = lse;
-  char* w = static_cast<char*>(ws);
-  p.part = reinterpret_cast<float*>(w + (full ? L.part_full : L.part_local));
-  p.tickets = reinterpret_cast<int32_t*>(w + (full ? L.tick_full : L.tick_local));
-  p.err = reinterpret_cast<int32_t*>(w + L.header);
-  p.worklist = reinterpret_cast<const int32_t*>(w + L.worklist);
+  p.part = part;
+  p.tickets = tickets;
+  p.err = header;
+  p.queue = header + 1;
+  p.worklist = worklist;
   p.B = d->batch;
   p.Hq = d->num_q_heads;
   p.Hkv = d->num_kv_heads;
   p.sink = d->sink;
   p.window = d->window;
-  p.t_max = L.t_max;
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d->head_dim));
+  p.t_max = d->kv_layout == ODA_KV_CONTIG ? d->t_cap : (int64_t)d->block_size * d->max_blocks_per_seq;
   return p;
+}
+
+static AttnParams attn_params(const oda_dims* d, int32_t layer, const oda_kv* kv, const int32_t* pos,
+                              const oda_bf16* q, const oda_bf16* kc, const oda_bf16* vc, oda_bf16* out, float* lse,
+                              void* ws, const WsLayout& L, bool full) {
+  char* w = static_cast<char*>(ws);
+  return attn_params_at(d, layer, kv, pos, q, kc, vc, out, lse,
+                        reinterpret_cast<float*>(w + (full ? L.part_full : L.part_local)),
+                        reinterpret_cast<int32_t*>(w + (full ? L.tick_full : L.tick_local)),
+                        reinterpret_cast<int32_t*>(w + L.header), reinterpret_cast<const int32_t*>(w + L.worklist));
+}
+
+int check_attn_operands(const oda_dims* d, int32_t layer, const oda_kv* kv, const int32_t* pos, const oda_bf16* q,
+                        const oda_bf16* kc, const oda_bf16* vc, const oda_bf16* out) {
+  int st;
+  if (!dims_valid(d, &st)) return st;
+  if (kv == nullptr || kv->k == nullptr || kv->v == nullptr || pos == nullptr || q == nullptr || kc == nullptr ||
+      vc == nullptr || out == nullptr)
+    return ODA_E_NULL;
+  if (d->kv_layout == ODA_KV_PAGED && kv->block_tables == nullptr) return ODA_E_NULL;
+  if (layer < 0 || layer >= d->num_layers) return ODA_E_LAYER;
+  return ODA_OK;
 }
 
 static int check_attn_args(const oda_dims* d, int32_t layer, const oda_kv* kv, const int32_t* pos, const oda_bf16* q,
                            const oda_bf16* kc, const oda_bf16* vc, oda_bf16* out, void* ws, size_t ws_bytes,
                            WsLayout* L) {
-  int st;
-  if (!dims_valid(d, &st)) return st;
-  if (kv == nullptr || kv->k == nullptr || kv->v == nullptr || pos == nullptr || q == nullptr || kc == nullptr ||
-      vc == nullptr || out == nullptr || ws == nullptr)
-    return ODA_E_NULL;
-  if (d->kv_layout == ODA_KV_PAGED && kv->block_tables == nullptr) return ODA_E_NULL;
-  if (layer < 0 || layer >= d->num_layers) return ODA_E_LAYER;
+  const int st = check_attn_operands(d, layer, kv, pos, q, kc, vc, out);
+  if (st != ODA_OK) return st;
+  if (ws == nullptr) return ODA_E_NULL;
   *L = ws_layout(d);
   if (ws_bytes < L->total) return ODA_E_WORKSPACE;
   return ODA_OK;

@@ -23,12 +23,14 @@ constexpr int kFullFineChunk = ODA_FULL_FINE_CHUNK;
 constexpr int kFullFillUnits = ODA_FULL_FILL_UNITS;
 constexpr int kFullRoundUnits = ODA_FULL_ROUND_UNITS;
 constexpr int kFullMaxSplits = ODA_FULL_MAX_SPLITS;
+constexpr int kFullRaggedRounds = ODA_FULL_RAGGED_ROUNDS;
+constexpr int kFullUnitCostKeys = ODA_FULL_UNIT_COST_KEYS;
 
 // ---------------------------------------------------------------------------
 // workspace layout (byte offsets, each region 256-B aligned)
 // ---------------------------------------------------------------------------
 struct WsLayout {
-  size_t header;       // int32[64]: [0] error bits
+  size_t header;       // int32[64]: [0] error bits, [1] [2] the full kernel's unit queue and exit count
   size_t worklist;     // int32 count, then int32 items[B * kFullMaxSplits]
   size_t tick_local;   // int32[B * Hkv]
   size_t tick_full;    // int32[B * Hkv]
@@ -41,13 +43,15 @@ struct WsLayout {
   int64_t t_max;            // capacity of one sequence in positions
 };
 
-// Split count of the full branch for a sequence of t keys when nflag
-// sequences with hkv KV heads each are flagged: chunks of kFullMinChunk keys
-// or more, cut finer (not below kFullFineChunk keys) while the launch would
-// hold fewer than kFullFillUnits units, coarser where more than
-// kFullRoundUnits units would not fit one round of the persistent grid.
-// Every split is non-empty: (n - 1)^2 < t for n <= ceil(t / 256).
-__device__ __host__ __forceinline__ int full_nsplit(int t, int nflag, int hkv) {
+// Candidate A of the full branch's split policy (one round) for a sequence
+// of t keys when nflag sequences with hkv KV heads each are flagged, holding
+// `total` keys together: chunks of kFullMinChunk keys or more, cut finer (not
+// below kFullFineChunk keys) while the launch would hold fewer than
+// kFullFillUnits units; and at most the sequence's share of one round of
+// kFullRoundUnits units in proportion to its length, floor(kFullRoundUnits
+// t / (total hkv)), but at least 1.  Every split is non-empty: (n - 1)^2 < t
+// for n <= ceil(t / 256).
+__device__ __host__ __forceinline__ int full_nsplit_round(int t, int nflag, int hkv, int64_t total) {
   int n = (t + kFullMinChunk - 1) / kFullMinChunk;
   n = n < kFullMaxSplits ? n : kFullMaxSplits;
   const int per = nflag * hkv;
@@ -56,11 +60,38 @@ __device__ __host__ __forceinline__ int full_nsplit(int t, int nflag, int hkv) {
   fine = fine < by_chunk ? fine : by_chunk;
   fine = fine < kFullMaxSplits ? fine : kFullMaxSplits;
   n = n > fine ? n : fine;
-  if (per > 0 && per * n > kFullRoundUnits) {
-    const int fit = kFullRoundUnits / per;
-    n = fit > 1 ? fit : 1;
+  if (per > 0 && total > 0) {
+    const int64_t share = ((int64_t)kFullRoundUnits * t) / (total * hkv);
+    const int cap = share < 1 ? 1 : (share > kFullMaxSplits ? kFullMaxSplits : (int)share);
+    n = n < cap ? n : cap;
   }
   return n;
+}
+
+// Candidate B (several rounds of smaller units): chunks of
+// max(kFullMinChunk, ceil(total hkv / (kFullRaggedRounds kFullRoundUnits)))
+// keys, at most kFullMaxSplits splits.
+__device__ __host__ __forceinline__ int full_nsplit_rounds(int t, int hkv, int64_t total) {
+  const int64_t units = (int64_t)kFullRaggedRounds * kFullRoundUnits;
+  int64_t c = (total * hkv + units - 1) / units;
+  c = c > kFullMinChunk ? c : kFullMinChunk;
+  const int64_t n = (t + c - 1) / c;
+  return n < 1 ? 1 : (n > kFullMaxSplits ? kFullMaxSplits : (int)n);
+}
+
+// Estimated time of a candidate cut, in keys: with N units whose longest is
+// U and shortest u over a grid of kFullRoundUnits workgroups (largest units
+// first), the smaller of two estimates, ceil(N / grid) rounds of the longest
+// unit, and the even share of all keys plus one shortest unit when units
+// remain after the first round (never below U); each round adds a unit's
+// fixed cost.
+__device__ __host__ __forceinline__ int64_t full_split_cost(int64_t units, int64_t longest, int64_t shortest,
+                                                            int64_t total, int hkv) {
+  const int64_t rounds = (units + kFullRoundUnits - 1) / kFullRoundUnits;
+  const int64_t by_rounds = rounds * (longest + kFullUnitCostKeys);
+  int64_t even = (total * hkv + kFullRoundUnits - 1) / kFullRoundUnits + (units > kFullRoundUnits ? shortest : 0);
+  even = (even > longest ? even : longest) + rounds * kFullUnitCostKeys;
+  return by_rounds < even ? by_rounds : even;
 }
 
 // Work-list items: (b << 20) | (nsplit << 10) | split.
@@ -90,6 +121,7 @@ struct AttnParams {
   int32_t* tickets;
   int32_t* err;
   const int32_t* worklist;  // count at [0], items from [1]
+  int32_t* queue;           // full branch: [0] next unit past the first round, [1] workgroups done (zero between launches)
   int32_t B, Hq, Hkv, sink, window;
   int64_t t_max;
   float scale_log2;         // log2(e) / sqrt(d)
@@ -107,6 +139,17 @@ struct AttnParams {
   uint16_t* v_stage;
   float qk_eps;
 };
+
+// Attention parameters of one layer with the split partials, tickets, the
+// header (error word, then the full kernel's queue counters) and the work
+// list at the given device addresses.
+AttnParams attn_params_at(const ::oda_dims* d, int32_t layer, const ::oda_kv* kv, const int32_t* pos,
+                          const uint16_t* q, const uint16_t* kc, const uint16_t* vc, uint16_t* out, float* lse,
+                          float* part, int32_t* tickets, int32_t* header, const int32_t* worklist);
+// The argument checks every attention call makes (dims, non-NULL operands,
+// block tables of a paged cache, layer range); ODA_OK or an error code.
+int check_attn_operands(const ::oda_dims* d, int32_t layer, const ::oda_kv* kv, const int32_t* pos,
+                        const uint16_t* q, const uint16_t* kc, const uint16_t* vc, const uint16_t* out);
 
 int launch_local_attn(const AttnParams& p, int G, bool paged, hipStream_t s, bool rope = false);
 int launch_full_attn(const AttnParams& p, int G, bool paged, hipStream_t s);

@@ -88,26 +88,50 @@ extern "C" {
 #define ODA_HEAD_FFN 2048
 #define ODA_HEAD_NTENSORS 22
 
-/* Split policy of the full branch.  With F flagged sequences in the step
- * and Hkv KV heads (P = F * Hkv units per split index), a flagged sequence
- * with t = pos + 1 keys is cut into nsplit(t, F) contiguous splits of
- * ceil(t / nsplit) keys (the last one shorter, none empty):
+/* Split policy of the full branch.  With F flagged sequences holding T keys
+ * together (t = pos + 1 keys each) and Hkv KV heads (P = F * Hkv units per
+ * split index), each flagged sequence is cut into nsplit(t) contiguous
+ * splits of ceil(t / nsplit) keys (the last one shorter, none empty).  Two
+ * candidate cuts are formed:
+ *  A, one round:
  *   n0 = max(min(ODA_FULL_MAX_SPLITS, ceil(t / ODA_FULL_MIN_CHUNK)),
  *            min(ODA_FULL_MAX_SPLITS, ceil(t / ODA_FULL_FINE_CHUNK),
  *                floor(ODA_FULL_FILL_UNITS / P)))
- *   nsplit = P * n0 <= ODA_FULL_ROUND_UNITS ? n0
- *                                           : max(1, floor(ODA_FULL_ROUND_UNITS / P))
- * Chunks of ODA_FULL_MIN_CHUNK keys or more, cut finer (down to
- * ODA_FULL_FINE_CHUNK) while the launch would hold fewer than
- * ODA_FULL_FILL_UNITS units, and coarser where more than
- * ODA_FULL_ROUND_UNITS units would not fit one round of the full kernel's
- * persistent grid (one workgroup per compute unit of an MI355X).  The work
- * list has one item per (flagged sequence, split). */
+ *   share = max(1, floor(ODA_FULL_ROUND_UNITS * t / (T * Hkv)))
+ *   nA = min(n0, share)
+ *   -- chunks of ODA_FULL_MIN_CHUNK keys or more, cut finer (down to
+ *   ODA_FULL_FINE_CHUNK) while the launch would hold fewer than
+ *   ODA_FULL_FILL_UNITS units, and at most the sequence's share, in
+ *   proportion to its length, of one round of ODA_FULL_ROUND_UNITS units of
+ *   the full kernel's persistent grid (one workgroup per compute unit of an
+ *   MI355X); for equal lengths the share is floor(ODA_FULL_ROUND_UNITS / P);
+ *  B, several rounds of smaller units:
+ *   C = max(ODA_FULL_MIN_CHUNK,
+ *           ceil(T * Hkv / (ODA_FULL_RAGGED_ROUNDS * ODA_FULL_ROUND_UNITS)))
+ *   nB = min(ODA_FULL_MAX_SPLITS, ceil(t / C)).
+ * Each candidate X has N_X = Hkv * sum(nX) units, R_X =
+ * ceil(N_X / ODA_FULL_ROUND_UNITS) rounds, the longest unit U_X and the
+ * shortest u_X (units of ceil(t / nX) keys), and the estimated time in keys
+ *   cost_X = min(R_X * (U_X + K0),
+ *                max(U_X, ceil(T * Hkv / ODA_FULL_ROUND_UNITS)
+ *                         + (N_X > ODA_FULL_ROUND_UNITS ? u_X : 0)) + R_X * K0)
+ * with K0 = ODA_FULL_UNIT_COST_KEYS, a unit's fixed cost in keys (the first
+ * term is exact for equal units; the second, for units of mixed size handed
+ * out largest first, is the even share of all keys plus a short unit left
+ * over).  B is used when cost_B < cost_A, else A: equal lengths that divide
+ * into one round keep A; ragged lengths, whose one-round shares round to
+ * units of unequal size, take B.  The work list has one item per (flagged
+ * sequence, split); sequences are listed longest unit first
+ * (ceil(t / nsplit) descending, ties by ascending b), their splits in
+ * order.  Units past the first round are handed out by the kernel in list
+ * order (largest first) as workgroups become free. */
 #define ODA_FULL_MIN_CHUNK 1024
 #define ODA_FULL_FINE_CHUNK 256
 #define ODA_FULL_FILL_UNITS 128
 #define ODA_FULL_ROUND_UNITS 256
 #define ODA_FULL_MAX_SPLITS 32
+#define ODA_FULL_RAGGED_ROUNDS 4
+#define ODA_FULL_UNIT_COST_KEYS 128
 
 typedef uint16_t oda_bf16;
 
@@ -164,8 +188,9 @@ size_t oda_workspace_bytes(const oda_dims *dims);
 
 /* Byte offset inside the workspace of the full-branch work list: an int32
  * count followed by `count` int32 items,
- * item = (b << 20) | (nsplit << 10) | split.  Written by oda_recall_score
- * and oda_worklist, read by oda_full_attn_if. */
+ * item = (b << 20) | (nsplit << 10) | split, in the order the split policy
+ * above states.  Written by oda_recall_score and oda_worklist, read by
+ * oda_full_attn_if. */
 size_t oda_workspace_worklist_offset(const oda_dims *dims);
 
 /* ---- device work ---- */
@@ -199,8 +224,7 @@ int oda_local_attn(const oda_dims *dims, int32_t layer, const oda_kv *kv, const 
  *                          : (score[b] > theta || score[b] is not finite)
  *    [ODA notes §2.3]; force may be NULL (all decided by the head).
  *  The work list (see oda_workspace_worklist_offset) lists, for each flagged
- *  b in ascending order, the splits 0 .. nsplit(pos[b]+1, F)-1, F the
- *  number of flagged sequences (split policy above). */
+ *  b, the splits 0 .. nsplit(pos[b]+1)-1 (split policy and order above). */
 int oda_recall_score(const oda_dims *dims, const float *head_w, const oda_bf16 *h_prev,
                      const oda_bf16 *emb, const oda_bf16 *h_local, float theta, const int8_t *force,
                      const int32_t *pos, float *score, uint8_t *flag, void *ws, size_t ws_bytes,

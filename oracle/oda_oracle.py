@@ -271,15 +271,23 @@ def branch_rule(q: float, theta: float = THETA_DEFAULT, force: int = -1) -> int:
 # ---------------------------------------------------------------------------
 # work list for the conditional full branch
 # ---------------------------------------------------------------------------
-def full_worklist(flags: Sequence[int], nsplit: Sequence[int]) -> List[Tuple[int, int]]:
-    """Compacted work list of the conditional full branch: for every flagged
-    sequence b in ascending order, its splits 0..nsplit[b]-1.  (How many
-    splits a sequence is cut into is a kernel policy, passed in.)"""
+def full_worklist(flags: Sequence[int], nsplit: Sequence[int],
+                  lengths: Sequence[int] = None) -> List[Tuple[int, int]]:
+    """Compacted work list of the conditional full branch: the splits
+    0..nsplit[b]-1 of every flagged sequence b.  How many splits a sequence
+    is cut into, and the order in which sequences are listed, are kernel
+    scheduling choices, not the method: the counts are passed in, and with
+    `lengths` (t_b = keys of sequence b) the sequences are listed longest
+    unit first, by ceil(t_b / nsplit[b]) descending with ties by ascending
+    b; without it, by ascending b.  Pinned by brute force (tests)."""
+    seqs = [b for b, f in enumerate(flags) if f]
+    if lengths is not None:
+        unit = {b: -(-int(lengths[b]) // int(nsplit[b])) if int(nsplit[b]) > 0 else 0 for b in seqs}
+        seqs.sort(key=lambda b: (-unit[b], b))
     items: List[Tuple[int, int]] = []
-    for b, f in enumerate(flags):
-        if f:
-            for s in range(int(nsplit[b])):
-                items.append((b, s))
+    for b in seqs:
+        for s in range(int(nsplit[b])):
+            items.append((b, s))
     return items
 
 

@@ -177,18 +177,53 @@ class Problem:
         return self.head_P
 
 
-def full_nsplit(t: int, nflag: int, hkv: int) -> int:
-    """Split policy stated in include/oda.h: chunks of 1024 keys or more (at
-    most 32 splits), cut finer, down to 256 keys, while the F = nflag flagged
-    sequences' Hkv heads would otherwise make fewer than 128 units, and
-    coarser where more than 256 units would not fit one round."""
+def full_nsplit(t: int, nflag: int, hkv: int, total: int = None) -> int:
+    """Candidate A of the split policy stated in include/oda.h (one round):
+    chunks of 1024 keys or more (at most 32 splits), cut finer, down to 256
+    keys, while the F = nflag flagged sequences' Hkv heads would otherwise
+    make fewer than 128 units; and at most the sequence's length-proportional
+    share of one 256-unit round, floor(256 t / (total hkv)) but at least 1,
+    where total is the flagged sequences' keys together (nflag * t when
+    omitted: equal lengths)."""
+    if total is None:
+        total = nflag * t
     base = min(C.ODA_FULL_MAX_SPLITS, -(-t // C.ODA_FULL_MIN_CHUNK))
     per = nflag * hkv
     fine = min(C.ODA_FULL_MAX_SPLITS, -(-t // C.ODA_FULL_FINE_CHUNK), C.ODA_FULL_FILL_UNITS // per) if per else 0
     n = max(base, fine)
-    if per and per * n > C.ODA_FULL_ROUND_UNITS:
-        n = max(1, C.ODA_FULL_ROUND_UNITS // per)
+    if per and total > 0:
+        share = (C.ODA_FULL_ROUND_UNITS * t) // (total * hkv)
+        n = min(n, max(1, min(C.ODA_FULL_MAX_SPLITS, share)))
     return n
+
+
+def full_nsplit_rounds(t: int, hkv: int, total: int) -> int:
+    """Candidate B (several rounds): chunks of max(1024, ceil(total hkv /
+    (4 * 256))) keys, at most 32 splits."""
+    c = max(C.ODA_FULL_MIN_CHUNK, -(-total * hkv // (C.ODA_FULL_RAGGED_ROUNDS * C.ODA_FULL_ROUND_UNITS)))
+    return max(1, min(C.ODA_FULL_MAX_SPLITS, -(-t // c)))
+
+
+def full_splits(flags, ts, hkv: int) -> list:
+    """Split counts of a step (0 for unflagged sequences): candidate B when
+    its estimated time (include/oda.h) is below candidate A's, else A."""
+    on = [int(f != 0) for f in flags]
+    nflag = sum(on)
+    total = sum(int(t) for f, t in zip(on, ts) if f)
+    na = [full_nsplit(int(t), nflag, hkv, total) if f else 0 for f, t in zip(on, ts)]
+    nb = [full_nsplit_rounds(int(t), hkv, total) if f else 0 for f, t in zip(on, ts)]
+
+    R, K0 = C.ODA_FULL_ROUND_UNITS, C.ODA_FULL_UNIT_COST_KEYS
+
+    def cost(ns):
+        units = hkv * sum(ns)
+        sizes = [-(-int(t) // n) for n, t in zip(ns, ts) if n > 0]
+        longest, shortest = max(sizes, default=0), min(sizes, default=0)
+        rounds = -(-units // R)
+        even = -(-total * hkv // R) + (shortest if units > R else 0)
+        return min(rounds * (longest + K0), max(even, longest) + rounds * K0)
+
+    return nb if cost(nb) < cost(na) else na
 
 
 def decode_items(items) -> list:
@@ -197,12 +232,13 @@ def decode_items(items) -> list:
 
 
 def want_worklist(flags, ts, hkv: int) -> list:
-    """The oracle's work list (flagged b ascending, splits in order) for the
-    split counts of the policy, as (b, nsplit, split)."""
+    """The oracle's work list (flagged sequences longest unit first, splits
+    in order) for the split counts of the policy, as (b, nsplit, split)."""
     from oracle import full_worklist
-    nflag = int(np.count_nonzero(np.asarray(flags)))
-    ns = [full_nsplit(int(t), nflag, hkv) for t in ts]
-    return [(b, ns[b], s) for b, s in full_worklist([int(f != 0) for f in flags], ns)]
+    flags = [int(f != 0) for f in flags]
+    ts = [int(t) for t in ts]
+    ns = full_splits(flags, ts, hkv)
+    return [(b, ns[b], s) for b, s in full_worklist(flags, ns, ts)]
 
 
 def replay_step(pr: Problem, j: int, *, theta: float, force=None, check_layers=None, check_b=None,

@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import conditional_sparse_attention_amd as C
@@ -176,7 +177,7 @@ def test_split_policy_constants_and_properties():
     from _harness import full_nsplit
     src = open(os.path.join(ROOT, "include", "oda.h")).read()
     for name in ("ODA_FULL_MIN_CHUNK", "ODA_FULL_FINE_CHUNK", "ODA_FULL_FILL_UNITS", "ODA_FULL_ROUND_UNITS",
-                 "ODA_FULL_MAX_SPLITS"):
+                 "ODA_FULL_MAX_SPLITS", "ODA_FULL_RAGGED_ROUNDS", "ODA_FULL_UNIT_COST_KEYS"):
         m = re.search(r"#define\s+%s\s+(\d+)" % name, src)
         assert m and int(m.group(1)) == getattr(C, name), name
     ts = sorted(set([1, 2, 255, 256, 257, 1023, 1024, 1025, 2052, 4096, 4097, 9000, 16384, 32769, 131072, 262144]
@@ -202,3 +203,43 @@ def test_split_policy_constants_and_properties():
     assert [full_nsplit(131072, f, 8) for f in (1, 2, 3, 4, 32)] == [32, 16, 10, 8, 1]
     assert full_nsplit(16384, 3, 8) == 10 and full_nsplit(131072, 32, 16) == 1
     assert full_nsplit(4096, 1, 2) == 16 and full_nsplit(20000, 1, 2) == 32
+    # the step's split counts: candidate A (one round) unless candidate B
+    # (chunks of at least 1024 keys, four rounds' worth of units) costs less
+    # in rounds x longest unit; every split non-empty
+    from _harness import full_splits, full_nsplit_rounds
+    rng = np.random.default_rng(3)
+    for _ in range(300):
+        hkv = int(rng.choice([2, 4, 8]))
+        F = int(rng.integers(1, 33))
+        ts = [int(t) for t in np.rint(np.exp(rng.uniform(np.log(1), np.log(262144), F)))]
+        T = sum(ts)
+        ns = full_splits([1] * F, ts, hkv)
+        na = [full_nsplit(t, F, hkv, T) for t in ts]
+        nb = [full_nsplit_rounds(t, hkv, T) for t in ts]
+        assert ns in (na, nb)
+        for t, n in zip(ts, ns):
+            assert 1 <= n <= 32 and (n - 1) * -(-t // n) < t, (t, n)
+        for t, n in zip(ts, nb):   # B: chunks of at least 1024 keys, so no split is tiny
+            assert n == 1 or -(-t // n) >= min(1024, t) // 2
+    # equal lengths that fill one round exactly keep A; three 128K sequences
+    # (one round of 10 splits would leave units 6% longer than even) take B
+    assert full_splits([1], [131073], 8) == [32]
+    assert full_splits([1, 1], [131073] * 2, 8) == [16, 16]
+    assert full_splits([1] * 3, [131073] * 3, 8) == [32] * 3
+    assert full_splits([1] * 8, [16385] * 8, 8) == [4] * 8
+    assert full_splits([1], [4097], 8) == [16]
+    # a ragged mix: units handed out largest first to 256 workgroups finish
+    # within 15% of the even share of all keys (one split per sequence per
+    # head-round would leave the longest unit 40% over it)
+    import heapq
+    ts = [124661, 4388, 33000, 9000, 60000, 15000, 5000, 90000]
+    ns = full_splits([1] * 8, ts, 8)
+    units = sorted([-(-t // n) for t, n in zip(ts, ns) for _ in range(8 * n)], reverse=True)
+    loads = [0] * 256
+    for u in units:
+        heapq.heapreplace(loads, loads[0] + u)
+    even = sum(ts) * 8 / 256
+    assert max(loads) <= 1.15 * even, (max(loads), even)
+    na = [full_nsplit(t, 8, 8, sum(ts)) for t in ts]
+    assert max(-(-t // n) for t, n in zip(ts, na)) > 1.4 * even
+

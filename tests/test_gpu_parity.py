@@ -53,6 +53,22 @@ def test_ragged_batch_forced_and_head(layout, hq, hkv):
     replay_step(pr, 2, theta=0.0)
 
 
+def test_full_branch_units_past_one_round():
+    """17 flagged sequences x 16 KV heads make more units than one round of
+    the full kernel's persistent grid, even at one split each: the units past
+    the first round come from the kernel's device-side queue, largest first.
+    Two layers and two all-flagged steps check that the queue starts from
+    zero at every launch (ragged lengths across t = 2052 / 2053)."""
+    wl = small_wl([2600, 2100, 300, 2052, 2053, 1500, 900, 2400, 64, 1999, 2222, 777, 1234, 2500, 1800, 1,
+                   2049], hq=16, hkv=16)
+    pr = Problem(wl, head_perturb=True)
+    B = wl.batch
+    for j in range(2):
+        replay_step(pr, j, theta=0.0, force=np.ones(B, np.int8))
+    units = sum(n for (_, n, s) in pr.worklist() if s == 0) * wl.hkv
+    assert units > 256, units
+
+
 def test_single_key_output_is_value_exactly():
     """t = 1: the index set holds only the current token, so o = v_cur
     exactly (bit-exact after the bf16 round trip)."""

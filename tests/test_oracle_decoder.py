@@ -260,3 +260,96 @@ def test_step_takes_the_chosen_branch():
     assert recs[0]["score"] == recs[1]["score"] == recall_score(head_P, h_prev, erow, recs[0]["hL"])
     for r in recs:
         assert r["token"] == D.argmax_first(D.logits(E, r["h"]))
+
+
+# ---------------------------------------------------------------------------
+# the oracle's rounded layer against the textbook float64 layer
+# ---------------------------------------------------------------------------
+U_BF16 = 2.0 ** -9      # unit roundoff of round-to-nearest bf16 (8 significand bits)
+
+
+def _textbook_layer(x, P, hq, hkv, d, pos, Kf, Vf, S, theta, eps, *, pert=None, mlp_norm_from=None,
+                    rope_shift=0, v_rotated=False):
+    """The standard pre-norm decoder layer in float64: RMSNorm before each
+    projection, QK-norm, RoPE, softmax attention over S of the history plus
+    the current row, residuals, SwiGLU.  With pert=None nothing is rounded.
+    pert(y) is applied wherever a backbone stores an activation (the
+    normalised input, the q/k/v projection, the rotated q and k, the
+    attention output, the normalised MLP input, gate, up and their product).
+    mlp_norm_from / rope_shift / v_rotated plant plausible mistakes (the MLP
+    norm of the pre-attention stream; RoPE one position off; v rotated like
+    k).  Returns (x2, k, v, o)."""
+    f = pert if pert is not None else (lambda y: y)
+    rms = lambda v: 1.0 / math.sqrt(float(np.mean(v * v)) + eps)
+    a = f(P["gamma_in"] * x) * rms(x)
+    qkv = f(P["W_qkv"] @ a)
+    half = d // 2
+    ang = (pos + rope_shift) * theta ** (-2.0 * np.arange(half) / d)
+    c, s = np.cos(ang), np.sin(ang)
+
+    def norm_rope(v, gamma):
+        y = gamma * v * rms(v)
+        return f(np.concatenate([y[:half] * c - y[half:] * s, y[half:] * c + y[:half] * s]))
+
+    q = np.stack([norm_rope(qkv[h * d:(h + 1) * d], P["gamma_q"]) for h in range(hq)])
+    k = np.stack([norm_rope(qkv[(hq + g) * d:(hq + g + 1) * d], P["gamma_k"]) for g in range(hkv)])
+    v = np.stack([qkv[(hq + hkv + g) * d:(hq + hkv + g + 1) * d] for g in range(hkv)])
+    if v_rotated:
+        v = np.concatenate([v[:, :half] * c - v[:, half:] * s, v[:, half:] * c + v[:, :half] * s], axis=1)
+    G = hq // hkv
+    o = np.zeros((hq, d))
+    for h in range(hq):
+        g = h // G
+        keys = np.stack([Kf[g][i] if i < pos else k[g] for i in S])
+        vals = np.stack([Vf[g][i] if i < pos else v[g] for i in S])
+        sc = keys @ q[h] / math.sqrt(d)
+        p = np.exp(sc - sc.max())
+        o[h] = f((p / p.sum()) @ vals)
+    x1 = x + P["W_o"] @ o.reshape(-1)
+    xm = x if mlp_norm_from == "x" else x1
+    a2 = f(P["gamma_post"] * xm) * rms(xm)
+    gt, ut = f(P["W_gate"] @ a2), f(P["W_up"] @ a2)
+    m = f(gt / (1.0 + np.exp(-gt)) * ut)
+    return x1 + P["W_down"] @ m, k, v, o
+
+
+@pytest.mark.parametrize("seed,pos,S", [(21, 9, [0, 1, 2, 3, 7, 8, 9]), (22, 30, list(range(31))),
+                                        (23, 40, [0, 1, 38, 39, 40])])
+def test_rounded_layer_is_the_textbook_layer_within_the_bf16_budget(seed, pos, S):
+    """The oracle's decoder layer rounds to bf16 where the backbone stores
+    activations and applies each RMSNorm scale to the finished dot product.
+    Without rounding that is exactly the textbook pre-norm layer.  The
+    budget for one bf16 rounding per stored activation: the textbook layer
+    is re-run 300 times with every stored activation multiplied by
+    (1 + delta), delta uniform in [-u, u] (u = 2^-9, the bound of
+    round-to-nearest), and the oracle's distance from the unrounded layer
+    must lie within 1.5x the largest distance seen.  The budget is small
+    against the layer's own update, and plausible misreadings (the MLP norm
+    from the pre-attention stream; RoPE one position off; v rotated like k)
+    lie far outside it."""
+    Dm, hq, hkv, d, I, eps, theta = 64, 4, 2, 16, 96, 1e-6, 10000.0
+    rng = np.random.default_rng(seed)
+    w = lambda n, k: bf16_to_f64(bits(rng.standard_normal((n, k)) / math.sqrt(k)))
+    gain = lambda n: bf16_to_f64(bits(1 + 0.1 * rng.standard_normal(n)))
+    P = {"gamma_in": gain(Dm), "W_qkv": w((hq + 2 * hkv) * d, Dm), "gamma_q": gain(d), "gamma_k": gain(d),
+         "W_o": w(Dm, hq * d), "gamma_post": gain(Dm), "W_gate": w(I, Dm), "W_up": w(I, Dm), "W_down": w(Dm, I)}
+    x = rng.standard_normal(Dm)
+    K = bits(rng.standard_normal((hkv, pos, d)))
+    V = bits(rng.standard_normal((hkv, pos, d)))
+    Kf, Vf = bf16_to_f64(K), bf16_to_f64(V)
+    got = D.decoder_layer(x, P, hq, hkv, d, pos, K, V, S, theta, eps)
+    got = (got[0], bf16_to_f64(got[1]), bf16_to_f64(got[2]), bf16_to_f64(got[3]))
+    exact = _textbook_layer(x, P, hq, hkv, d, pos, Kf, Vf, S, theta, eps)
+    prng = np.random.default_rng(seed + 1000)
+    pert = lambda y: y * (1.0 + prng.uniform(-U_BF16, U_BF16, np.shape(y)))
+    budget = np.zeros(4)
+    for _ in range(300):
+        smp = _textbook_layer(x, P, hq, hkv, d, pos, Kf, Vf, S, theta, eps, pert=pert)
+        budget = np.maximum(budget, [np.max(np.abs(a - b)) for a, b in zip(smp, exact)])
+    dist = np.array([np.max(np.abs(a - b)) for a, b in zip(got, exact)])
+    assert np.all(dist <= 1.5 * budget), (dist, budget)
+    update = np.max(np.abs(exact[0] - x))
+    assert budget[0] < 0.02 * update, (budget[0], update)
+    for mistake in ({"mlp_norm_from": "x"}, {"rope_shift": 1}, {"v_rotated": True}):
+        wrong = _textbook_layer(x, P, hq, hkv, d, pos, Kf, Vf, S, theta, eps, **mistake)
+        assert np.max(np.abs(wrong[0] - exact[0])) > 5.0 * budget[0], mistake

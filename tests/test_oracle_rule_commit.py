@@ -73,6 +73,18 @@ def test_worklist_brute_force():
                  if flags[b] and s * chunk < pos[b] + 1]
         assert items == brute
         assert len(items) == sum(int(f) * n for f, n in zip(flags, nsplit))
+        # with lengths: the same pairs, each sequence's splits contiguous and
+        # in order, sequences longest unit first (ties: ascending b)
+        t = pos + 1
+        nsplit = [int(rng.integers(1, 33)) for _ in range(B)]
+        items = full_worklist(flags, nsplit, t)
+        assert sorted(items) == [(b, s) for b in range(B) if flags[b] for s in range(nsplit[b])]
+        order = [b for i, (b, s) in enumerate(items) if s == 0]
+        for i, (b, s) in enumerate(items):
+            assert s == 0 or items[i - 1] == (b, s - 1)
+        unit = lambda b: -(-int(t[b]) // nsplit[b])
+        for x, y in zip(order, order[1:]):
+            assert unit(x) > unit(y) or (unit(x) == unit(y) and x < y)
 
 
 def test_commit_invariants():
