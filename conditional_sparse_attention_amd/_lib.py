@@ -31,6 +31,7 @@ ODA_FULL_ROUND_UNITS = 256
 ODA_FULL_MAX_SPLITS = 32
 ODA_FULL_RAGGED_ROUNDS = 4
 ODA_FULL_UNIT_COST_KEYS = 128
+ODA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 EXPORTED = (
     "oda_abi_version", "oda_status_str", "oda_head_param_count", "oda_head_offsets",
@@ -40,6 +41,7 @@ EXPORTED = (
     "oda_dec_embed", "oda_dec_layer", "oda_dec_final_norm", "oda_dec_next_token",
     "oda_train_workspace_bytes", "oda_train_workspace_init", "oda_train_labels", "oda_train_head_step",
     "oda_gdn_state_bytes", "oda_gdn_conv_offset", "oda_gdn_step", "oda_gdn_commit",
+    "oda_local_attn_noalloc",
 )
 
 
@@ -105,6 +107,7 @@ def lib() -> ctypes.CDLL:
             "oda_workspace_init": (ctypes.c_int, [dp, vp, sz, vp]),
             "oda_local_ranges": (ctypes.c_int, [dp, vp, vp, vp]),
             "oda_local_attn": (ctypes.c_int, [dp, i32, kp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "oda_local_attn_noalloc": (ctypes.c_int, [dp, i32, kp, vp, vp, vp, vp, vp, vp, vp, vp]),
             "oda_recall_score": (ctypes.c_int, [dp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, sz, vp]),
             "oda_worklist": (ctypes.c_int, [dp, vp, vp, vp, sz, vp]),
             "oda_full_attn_if": (ctypes.c_int, [dp, i32, kp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
@@ -223,6 +226,11 @@ def oda_local_ranges(dims, pos, ranges, stream=None) -> None:
 def oda_local_attn(dims, layer, kv: oda_kv, pos, q, k_cur, v_cur, out, lse, ws, stream=None) -> None:
     check(lib().oda_local_attn(ctypes.byref(dims), layer, ctypes.byref(kv), _p(pos), _p(q), _p(k_cur), _p(v_cur),
                                 _p(out), _p(lse), _p(ws), _bytes(ws), _s(stream)), "oda_local_attn")
+
+
+def oda_local_attn_noalloc(dims, layer, kv: oda_kv, pos, q, k_cur, v_cur, out, lse, err, stream=None) -> None:
+    check(lib().oda_local_attn_noalloc(ctypes.byref(dims), layer, ctypes.byref(kv), _p(pos), _p(q), _p(k_cur),
+                                       _p(v_cur), _p(out), _p(lse), _p(err), _s(stream)), "oda_local_attn_noalloc")
 
 
 def oda_recall_score(dims, head_w, h_prev, emb, h_local, theta, force, pos, score, flag, ws, stream=None) -> None:

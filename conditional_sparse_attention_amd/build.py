@@ -12,7 +12,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["oda_abi.hip", "attn.hip", "head.hip", "commit.hip", "decoder.hip", "train.hip", "hybrid.hip"]
+SOURCES = ["oda_abi.hip", "attn.hip", "head.hip", "commit.hip", "decoder.hip", "train.hip", "hybrid.hip", "noalloc.hip"]
 LIB = os.path.join(PKG, "liboda.so")
 
 HIPCC_FLAGS = [

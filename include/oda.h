@@ -263,6 +263,31 @@ int oda_commit(const oda_dims *dims, const oda_kv *kv, int32_t *pos, const uint8
                const oda_bf16 *v_cur_F, const oda_bf16 *out_last_L, const oda_bf16 *out_last_F,
                oda_bf16 *h_prev, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---- for callers that cannot allocate ---- */
+
+/* Bytes of the library's fixed per-GPU scratch array used by
+ * oda_local_attn_noalloc: 16 MiB, held on each GPU the library runs on until
+ * the process ends. */
+#define ODA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* oda_local_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, kernels and results as oda_local_attn, with the
+ * split partials and completion tickets in the library's fixed scratch array
+ * of ODA_NOALLOC_SCRATCH_BYTES instead of a caller workspace.  The caller
+ * still passes every input and output.  err: device int32 that receives the
+ * sticky device-side error bits (ODA_ERR_*), or NULL to drop them.
+ * Returns ODA_E_WORKSPACE, launching nothing, when dims need more scratch
+ * than the array holds (split partials of B * Hkv * 16 * (Hq / Hkv) * 528
+ * bytes, plus tickets and a 256-byte header).  Calls no allocator.  The
+ * first call on a GPU looks the array up and clears its tickets with a fill
+ * kernel on `stream`; later calls find them cleared by the kernels.  Every
+ * call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (different streams without ordering, or several host threads) race. */
+int oda_local_attn_noalloc(const oda_dims *dims, int32_t layer, const oda_kv *kv, const int32_t *pos,
+                           const oda_bf16 *q, const oda_bf16 *k_cur, const oda_bf16 *v_cur, oda_bf16 *out,
+                           float *lse, int32_t *err, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

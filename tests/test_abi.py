@@ -86,6 +86,14 @@ def test_entry_points_reject_bad_arguments_without_launching():
     assert lib.oda_workspace_init(dp, None, ws_bytes, None) == C.ODA_E_NULL
     assert lib.oda_local_ranges(None, fake, fake, None) == C.ODA_E_NULL
     assert C.status_str(C.ODA_E_WORKSPACE).startswith("workspace")
+    # the variant without a workspace: the same argument checks, and dims
+    # whose split partials exceed the library's fixed scratch are refused
+    assert lib.oda_local_attn_noalloc(dp, 0, kp, *([None] * 7), None) == C.ODA_E_NULL
+    assert lib.oda_local_attn_noalloc(dp, 2, ctypes.byref(kv2), *args, None, None, None) == C.ODA_E_LAYER
+    big = C.make_dims(1, 32, 64, 16, t_cap=64)   # 32 * 16 pairs x 16 splits x G 4 x 528 B = 17.3 MB
+    assert 32 * 16 * 16 * 4 * 528 > C.ODA_NOALLOC_SCRATCH_BYTES
+    assert lib.oda_local_attn_noalloc(ctypes.byref(big), 0, ctypes.byref(kv2), *args, None, None,
+                                      None) == C.ODA_E_WORKSPACE
 
 
 def test_decoder_layout_agrees_with_oracle_and_generator():
