@@ -482,8 +482,7 @@ def run(args, wl, stream, torch):
                        "duration_source": "HIP events on the launch stream around each step's graph of the L "
                                           "full-attention launches (empty launches included, with zero bytes)",
                        "attention_kernels_frac": out["attention_kernels"]["kv_frac_peak"],
-                       "trace_window": {"k_attn_full": [before * L, nlaunch], "k_attn_local": [before * L, nlaunch],
-                                        "k_out_rule": [before, K]}}
+                       "trace_window": {"k_attn_full": [before * L, nlaunch], "k_attn_local": [before * L, nlaunch]}}
     if args.rate_sweep and wl.bernoulli_odd is None:
         out["rate_sweep"] = rate_sweep(args, S, graphs)
     del graphs

@@ -48,11 +48,14 @@ typedef __attribute__((address_space(1))) const v4u_t gv4_t;
 #endif
 // Workgroups per (sequence, KV head) in the local branch, between these
 // bounds (see local_splits()).
-constexpr int kLocalSplitsMin = 4;
+constexpr int kLocalSplitsMin = 1;
 constexpr int kLocalSplitsMax = 8;
-#ifndef ODA_LOCAL_WAVES
-#define ODA_LOCAL_WAVES 4
-#endif
+// Waves per workgroup of the local kernel: kLocalWaves, or kLocalWavesWide
+// when a (sequence, KV head) is cut into at most kLocalWideMax splits (each
+// workgroup then streams a larger share alone).
+constexpr int kLocalWaves = 4;
+constexpr int kLocalWavesWide = 8;
+constexpr int kLocalWideMax = 2;
 #ifndef ODA_FULL_WAVES_SMALL_G
 #define ODA_FULL_WAVES_SMALL_G 12
 #endif
@@ -66,7 +69,6 @@ constexpr int kLocalSplitsMax = 8;
 #ifndef ODA_FULL_U
 #define ODA_FULL_U 2
 #endif
-constexpr int kLocalWaves = ODA_LOCAL_WAVES;  // local kernel workgroup
 // Full kernel shape per group size: G = 2 (the 16/8-head models) runs 12
 // waves (3 per SIMD) with a 3-stage ring; G = 1 and G = 4 keep more state per
 // lane and run 8 waves with a 4-stage ring, which keeps a similar number of
@@ -644,9 +646,8 @@ constexpr int lds_floats() {
   return a > b ? a : b;
 }
 
-template <int G, bool PAGED, bool ROPE>
-__global__ void __launch_bounds__(kLocalWaves * 64) k_attn_local(AttnParams P) {
-  constexpr int NW = kLocalWaves;
+template <int G, bool PAGED, bool ROPE, int NW>
+__global__ void __launch_bounds__(NW * 64) k_attn_local(AttnParams P) {
   __shared__ float lds[lds_floats<G, NW>()];
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int pos = P.pos[b];
@@ -740,15 +741,21 @@ int device_cus() {
   return n;
 }
 
-// Workgroups per (sequence, KV head) in the local branch: about four per
-// compute unit over the whole batch, within [kLocalSplitsMin,
-// kLocalSplitsMax].  The local set is small (at most sink + window keys), so
-// past 8 splits the cross-workgroup merge costs more than the extra streaming
-// parallelism gains, and below 4 a workgroup streams too much alone.  At 8 KV
-// heads: 8 splits up to 16 sequences, 4 at 32.
-int local_splits(const AttnParams& p) {
+// Workgroups per (sequence, KV head) in the local branch: enough for one per
+// compute unit over the whole batch, ceil(CUs / (B Hkv)), two per compute
+// unit for the paged layout (its block-table walk streams slower per
+// workgroup), within [kLocalSplitsMin, kLocalSplitsMax].  The local set is
+// small (at most sink + window keys), so past 8 splits the cross-workgroup
+// merge costs more than the extra streaming parallelism gains.  At 8 KV
+// heads, contiguous: 8 splits up to 4 sequences, 4 at 8, 2 at 16, 1 (no
+// merge at all) at 32; paged: 2 at 32.  Measured per launch against four
+// per compute unit (at least 4 splits): 16.2 / 17.2 us at 8 x 16K, 28.9 /
+// 33.0 us at 16 x 64K with group size 4, 43.4 / 48.8 us at 32 x 4K
+// contiguous, and the same within 2% at 4 x 128K.
+int local_splits(const AttnParams& p, bool paged) {
   const int pairs = p.B * p.Hkv;
-  const int ns = (4 * device_cus() + pairs - 1) / pairs;
+  const int per_cu = paged ? 2 : 1;
+  const int ns = (per_cu * device_cus() + pairs - 1) / pairs;
   return ns < kLocalSplitsMin ? kLocalSplitsMin : (ns > kLocalSplitsMax ? kLocalSplitsMax : ns);
 }
 
@@ -756,9 +763,12 @@ template <int G, bool PAGED, bool ROPE>
 int launch_local_t(const AttnParams& p_in, hipStream_t s) {
   static_assert(kLocalSplitsMax <= kLocalMaxSplits, "local splits exceed the workspace slots");
   AttnParams p = p_in;
-  p.local_splits = local_splits(p);
+  p.local_splits = local_splits(p, PAGED);
   dim3 grid(p.local_splits, p.Hkv, p.B);
-  hipLaunchKernelGGL((k_attn_local<G, PAGED, ROPE>), grid, dim3(kLocalWaves * 64), 0, s, p);
+  if (p.local_splits <= kLocalWideMax)
+    hipLaunchKernelGGL((k_attn_local<G, PAGED, ROPE, kLocalWavesWide>), grid, dim3(kLocalWavesWide * 64), 0, s, p);
+  else
+    hipLaunchKernelGGL((k_attn_local<G, PAGED, ROPE, kLocalWaves>), grid, dim3(kLocalWaves * 64), 0, s, p);
   return hipGetLastError() == hipSuccess ? ODA_OK : ODA_E_LAUNCH;
 }
 
