@@ -63,6 +63,11 @@ def parse():
                     help="skip the first-request timings (a fresh process per measurement: capture plus the "
                          "first K steps, ODA and always-full)")
     ap.add_argument("--first-request-cell", default="", help=argparse.SUPPRESS)  # child: oda | always-full
+    ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "BENCH_JSON"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; csv) of a bench run with "
+                         "--copy-calibration: HBM bytes per launch of k_attn_full and k_attn_local over the "
+                         "split-graph region, each counter scaled by what it reads for the plain 1 GiB copies; prints "
+                         "one JSON object (the entries of profiles/hbm_traffic.json) and a markdown table")
     ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
                     help="summarise a rocprofv3 --kernel-trace (csv) of a bench run: per-kernel durations over "
                          "the whole run and over the split-graph region its JSON line names (trace_window), and "
@@ -95,6 +100,8 @@ def main():
     args = parse()
     if args.trace_summary:
         return trace_summary(*args.trace_summary)
+    if args.pmc_summary:
+        return pmc_summary(*args.pmc_summary)
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the step is timed on one GPU's share "
                                    "of the batch, and runs over several GPUs are not provided", "n_gpus": args.gpus}))
@@ -457,8 +464,11 @@ def run(args, wl, stream, torch):
     traffic, traffic_note = measured_traffic(wl.name, bytes_per_launch)
     local_bytes = kv_local * Hkv * d * 2 * 2 * L
     both_gbs = (local_bytes + full_bytes) / ((local_ms + full_ms) * 1e-3) / 1e9
+    local_traffic, local_traffic_note = measured_traffic(wl.name, local_bytes / nlaunch, kernel="k_attn_local")
     out["attention_kernels"] = {
         "local_avg_launch_us": round(local_ms * 1e3 / nlaunch, 2),
+        "local_algorithmic_bytes_per_launch": int(local_bytes / nlaunch),
+        "local_traffic": local_traffic, "local_traffic_note": local_traffic_note,
         "local_gbs": round(local_bytes / (local_ms * 1e-3) / 1e9, 1),
         "local_frac": round(local_bytes / (local_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "full_gbs": round(full_bytes / (full_ms * 1e-3) / 1e9, 1),
@@ -604,21 +614,21 @@ def device_copy_gbs(torch, stream, n_bytes=1 << 30, reps=5):
                     "on this box, for reading roofline.frac"}
 
 
-def measured_traffic(workload, bytes_per_launch):
-    """HBM bytes per launch of k_attn_full on this workload from the
-    committed rocprofv3 PMC measurement (FETCH_SIZE + WRITE_SIZE, each
-    normalised on a 1 GiB copy), as its ratio to the algorithmic bytes of the
-    measured launches times this run's algorithmic bytes per launch; None
-    when this kernel and workload were not counted, or the kernel source
-    changed since."""
+def measured_traffic(workload, bytes_per_launch, kernel="k_attn_full"):
+    """HBM bytes per launch of `kernel` on this workload from the committed
+    rocprofv3 PMC measurement (FETCH_SIZE + WRITE_SIZE, each normalised on a
+    1 GiB copy), as its ratio to the algorithmic bytes of the measured
+    launches times this run's algorithmic bytes per launch; None when this
+    kernel and workload were not counted, or the kernel source changed
+    since."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None, "no counter measurement"
-    ent = rec.get("k_attn_full", {}).get(workload)
+    ent = rec.get(kernel, {}).get(workload)
     if ent is None:
-        return None, f"k_attn_full not counted on {workload}"
+        return None, f"{kernel} not counted on {workload}"
     if ent.get("kernel_source_sha256") != kernel_source_hash():
         return None, "kernel changed since the counters were taken"
     ratio = ent["hbm_bytes_per_launch"] / ent["algorithmic_bytes_per_launch"]
@@ -747,6 +757,70 @@ def trace_summary(trace_dir: str, bench_json: str) -> None:
     for name, (n, tot, mn, mx) in stats(rows)[:25]:
         out.append(f"| `{name}` | {n} | {tot:.1f} | {tot / n:.2f} | {mn:.2f} | {mx:.2f} |")
     print("\n".join(out))
+
+
+def _pmc_rows(run_dir: str, counter: str):
+    """Per-dispatch (kernel, value) of one counter from a rocprofv3 --pmc
+    csv run: the process with the most k_attn_full dispatches, in dispatch
+    order."""
+    import csv
+    import glob
+    per_file = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path, newline="") as f:
+            rows = [(int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"]))
+                    for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+        per_file[path] = rows
+    if not per_file:
+        raise SystemExit(f"no {counter} rows under {run_dir}")
+    path, rows = max(per_file.items(), key=lambda kv: sum("k_attn_full" in r[1] for r in kv[1]))
+    rows.sort()
+    return path, [(k, v) for _, k, v in rows]
+
+
+def pmc_summary(fetch_dir: str, write_dir: str, bench_json: str) -> None:
+    """HBM traffic per launch of the attention kernels over the split-graph
+    region of a bench run with --copy-calibration, from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled so that it reads the 1 GiB
+    (read + write) device copies' known bytes."""
+    with open(bench_json) as f:
+        rec = json.loads([l for l in f.read().splitlines() if l.strip().startswith("{")][-1])
+    win = rec["roofline"]["trace_window"]
+    K, L = rec["steps"], rec["config"]["layers"]
+    B, Hkv, d = rec["config"]["batch"], rec["config"]["kv_heads"], rec["config"]["head_dim"]
+    copy_bytes = rec["copy_calibration_bytes"] // 2        # bytes read (= bytes written) per copy
+    out = {"workload": rec["config"]["workload"], "kernel_source_sha256": kernel_source_hash()}
+    for counter, run_dir in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        path, rows = _pmc_rows(run_dir, counter)
+        copies = [v for k, v in rows if "copyBuffer" in k][-3:]
+        factor = copy_bytes / 1024.0 / (sum(copies) / len(copies))
+        out[counter] = {"copy_kib": round(sum(copies) / len(copies), 1), "factor": round(factor, 5)}
+        for kern in ("k_attn_full", "k_attn_local"):
+            first, n = win[kern]
+            vals = [v for k, v in rows if kern in k][first:first + n]
+            assert len(vals) == n, (kern, len(vals), n)
+            out[counter][kern + "_kib_raw"] = round(sum(vals) / n, 2)
+            out[counter][kern + "_bytes"] = sum(vals) / n * 1024.0 * factor
+    full_alg = rec["roofline"]["algorithmic_bytes_per_launch"]
+    local_alg = rec["attention_kernels"]["local_algorithmic_bytes_per_launch"]
+    ent = {}
+    for kern, alg in (("k_attn_full", full_alg), ("k_attn_local", local_alg)):
+        hbm = out["FETCH_SIZE"][kern + "_bytes"] + out["WRITE_SIZE"][kern + "_bytes"]
+        ent[kern] = {"kernel_source_sha256": out["kernel_source_sha256"], "hbm_bytes_per_launch": int(hbm),
+                     "algorithmic_bytes_per_launch": int(alg), "ratio": round(hbm / alg, 5) if alg else None,
+                     "launches": win[kern][1], "fetch_factor": out["FETCH_SIZE"]["factor"],
+                     "write_factor": out["WRITE_SIZE"]["factor"]}
+    print(json.dumps({"workload": out["workload"], "entries": ent}))
+    md = [f"| kernel | FETCH_SIZE raw (KiB/launch) | WRITE_SIZE raw (KiB/launch) | HBM bytes/launch | algorithmic | ratio |",
+          "|---|---|---|---|---|---|"]
+    for kern in ("k_attn_full", "k_attn_local"):
+        e = ent[kern]
+        md.append(f"| `{kern}` | {out['FETCH_SIZE'][kern + '_kib_raw']} | {out['WRITE_SIZE'][kern + '_kib_raw']} | "
+                  f"{e['hbm_bytes_per_launch']:,} | {e['algorithmic_bytes_per_launch']:,} | {e['ratio']} |")
+    md.append(f"\nCopy calibration: FETCH_SIZE reads {out['FETCH_SIZE']['copy_kib']} KiB and WRITE_SIZE "
+              f"{out['WRITE_SIZE']['copy_kib']} KiB per 1 GiB copy (factors {out['FETCH_SIZE']['factor']}, "
+              f"{out['WRITE_SIZE']['factor']}).")
+    print("\n".join(md))
 
 
 def host_cpu_model() -> str:
