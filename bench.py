@@ -531,16 +531,21 @@ def synth_head_params(hidden: int) -> int:
 def first_request(args, wl, theta):
     """The pages' first-request protocol (capture included), next to the warm
     one: each measurement runs in a fresh process (setup untimed), capturing
-    one graph that serves every step and timing capture plus the first K
-    steps; the same process then times the warm median of REPEATS replays of
-    K steps.  ODA with the run's theta, and always-full."""
+    one graph that serves every step and timing capture plus the first N
+    steps, N the workload's decode-step count (one request); the same
+    process then times the warm median of REPEATS replays of N steps.  ODA
+    with the run's theta, and always-full."""
     import subprocess
-    res = {"protocol": "fresh process per measurement; cold = capture + first K steps (host clock); warm = median "
-                       "of repeats of K replays of the same single graph; the step's inputs are selected on the "
-                       "device from a resident per-step table inside the graph"}
+    import synth
+    key = int(args.workload) if str(args.workload).isdigit() else args.workload
+    n = synth.workloads()[key].steps
+    res = {"protocol": f"fresh process per measurement; cold = capture + the first {n} steps (the workload's decode "
+                       "steps, one request; host clock); warm = median of repeats of the same steps replayed with "
+                       "the same single graph; the step's inputs are selected on the device from a resident "
+                       "per-step table inside the graph", "steps": n}
     for mode in ("oda", "always-full"):
         cmd = [sys.executable, os.path.abspath(__file__), "--workload", str(args.workload), "--steps",
-               str(args.steps), "--warmup", str(args.warmup), "--repeats", str(args.repeats),
+               str(n), "--warmup", str(args.warmup), "--repeats", str(args.repeats),
                "--first-request-cell", f"{mode}:{theta!r}"]
         cp = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
         if cp.returncode != 0:
