@@ -15,10 +15,14 @@
 // lanes hold the rows' weights in registers (16-byte loads, all issued at
 // once), then sweep every batch row against them, so the weights are read
 // from HBM exactly once whatever the batch; the batch inputs come from L2.
-// The dot products are reduced inside the wave (DPP row sums + readlane),
-// with no LDS and no barrier.  RMSNorm scales are folded in after the dot
-// product (W (gamma*x) / rms(x)), the sum of squares gathered in the same
-// pass; the interaction vector is formed on the fly from the tower outputs.
+// The batch inputs of a layer (a few KB per sequence) are copied once per
+// workgroup into LDS with direct-to-LDS loads issued right after the
+// weights, so every batch row arrives in one memory round trip instead of
+// one per row; biases and residual operands are loaded before any store.
+// The dot products are reduced inside the wave (DPP row sums + readlane).
+// RMSNorm scales are folded in after the dot product (W (gamma*x) / rms(x)),
+// the sum of squares gathered in the same pass; the interaction vector is
+// formed on the fly from the tower outputs.
 #include "head_internal.h"
 
 namespace oda {
@@ -41,6 +45,30 @@ __device__ __forceinline__ float4 ldbf4(const uint16_t* p) {
   return make_float4(bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y));
 }
 
+// Copies the first n 16-byte chunks of `src` into `dst` (LDS) with
+// direct-to-LDS loads, chunk c by thread c % kThreads: the LDS address of a
+// wave's load is its first lane's chunk, each lane writing 16 bytes after the
+// previous lane's.  The caller waits (stage_wait) before reading.
+template <int MAXC>
+__device__ __forceinline__ void stage_lds(const void* src, int n, void* dst) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const uint4* g = static_cast<const uint4*>(src);
+  uint4* l = static_cast<uint4*>(dst);
+#pragma unroll
+  for (int j = 0; j < MAXC; ++j) {
+    const int c = j * kThreads + tid;
+    if (c < n) __builtin_amdgcn_global_load_lds(g + c, l + (c - lane), 16, 0, 0);
+  }
+}
+// Every load of the workgroup has landed (the staged rows included), then
+// the staged LDS is visible to all waves.
+__device__ __forceinline__ void stage_wait() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ------------------------------------------------------------------ towers
 struct TowerArgs {
   const float* w;  // blob
@@ -55,6 +83,8 @@ struct TowerArgs {
 template <int KI, int R, int NBM>
 __global__ void __launch_bounds__(kThreads) k_tower(TowerArgs A) {
   constexpr int D = KI * 256;
+  constexpr int CPR = D / 8;  // 16-byte chunks of one bf16 input row
+  __shared__ uint4 s_x[NBM * CPR];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int tw = blockIdx.y;
   const int n0 = (blockIdx.x * kWaves + wave) * R;
@@ -68,8 +98,14 @@ __global__ void __launch_bounds__(kThreads) k_tower(TowerArgs A) {
   float4 g[KI];
 #pragma unroll
   for (int i = 0; i < KI; ++i) g[i] = ld4(gam + 256 * i);
+  const float* cb = A.w + A.off_c[tw] + n0;
+  float cbv[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) cbv[r] = cb[r];
+  stage_lds<(NBM * CPR + kThreads - 1) / kThreads>(A.x[tw], A.B * CPR, s_x);
+  stage_wait();
+  const uint2* sx = reinterpret_cast<const uint2*>(s_x);
   float acc[R][NBM], ss[NBM];
-  const uint16_t* x = A.x[tw] + lane * 4;
 #pragma unroll
   for (int b = 0; b < NBM; ++b) {
     ss[b] = 0.0f;
@@ -78,7 +114,8 @@ __global__ void __launch_bounds__(kThreads) k_tower(TowerArgs A) {
     if (b < A.B) {
 #pragma unroll
       for (int i = 0; i < KI; ++i) {
-        const float4 xv = ldbf4(x + (size_t)b * D + 256 * i);
+        const uint2 raw = sx[(b * D + 256 * i) / 4 + lane];
+        const float4 xv = make_float4(bf16lo(raw.x), bf16hi(raw.x), bf16lo(raw.y), bf16hi(raw.y));
         const float4 in = mul4(xv, g[i]);
         ss[b] += dot4(xv, xv);
 #pragma unroll
@@ -86,7 +123,6 @@ __global__ void __launch_bounds__(kThreads) k_tower(TowerArgs A) {
       }
     }
   }
-  const float* cb = A.w + A.off_c[tw] + n0;
 #pragma unroll
   for (int b = 0; b < NBM; ++b) {
     if (b < A.B) {
@@ -94,7 +130,7 @@ __global__ void __launch_bounds__(kThreads) k_tower(TowerArgs A) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const float v = wave_sum64(acc[r][b]);
-        if (lane == 0) A.out[((size_t)tw * A.B + b) * kTower + n0 + r] = silu(v * inv + cb[r]);
+        if (lane == 0) A.out[((size_t)tw * A.B + b) * kTower + n0 + r] = silu(v * inv + cbv[r]);
       }
     }
   }
@@ -129,6 +165,7 @@ __device__ __forceinline__ float4 seg_value(int seg, const float4 a, const float
 // segment values of that chunk.  grid (T / 4)
 template <int NBM>
 __global__ void __launch_bounds__(kThreads) k_interact(InteractArgs A) {
+  __shared__ float4 s_t[3 * NBM * kTower / 4];  // towers [3][B][T]
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = blockIdx.x * kWaves + wave;
   const float* W = A.W + (size_t)n * (9 * kTower) + lane * 4;
@@ -137,30 +174,33 @@ __global__ void __launch_bounds__(kThreads) k_interact(InteractArgs A) {
   for (int q = 0; q < 4; ++q)
 #pragma unroll
     for (int s = 0; s < 9; ++s) w[q][s] = ld4(W + s * kTower + q * 256);
+  const float cI = A.bias[n];
+  stage_lds<(3 * NBM * kTower / 4 + kThreads - 1) / kThreads>(A.towers, 3 * A.B * kTower / 4, s_t);
+  stage_wait();
+  const float* st = reinterpret_cast<const float*>(s_t);
+  const int B = A.B;
   float acc[NBM];
 #pragma unroll
   for (int b = 0; b < NBM; ++b) {
     acc[b] = 0.0f;
-    if (b < A.B) {
+    if (b < B) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int e = q * 256 + lane * 4;
-        const float4 av = ld4(A.towers + (size_t)b * kTower + e);
-        const float4 bv = ld4(A.towers + ((size_t)A.B + b) * kTower + e);
-        const float4 cv = ld4(A.towers + ((size_t)2 * A.B + b) * kTower + e);
+        const int e = q * 64 + lane;  // float4 index of element q*256 + 4*lane
+        const float4 av = s_t[b * (kTower / 4) + e];
+        const float4 bv = s_t[(B + b) * (kTower / 4) + e];
+        const float4 cv = s_t[(2 * B + b) * (kTower / 4) + e];
 #pragma unroll
         for (int s = 0; s < 9; ++s) acc[b] += dot4(w[q][s], seg_value(s, av, bv, cv));
       }
     }
   }
-  const float cI = A.bias[n];
 #pragma unroll
   for (int b = 0; b < NBM; ++b) {
-    if (b < A.B) {
+    if (b < B) {
       const float v = wave_sum64(acc[b]);
       if (lane == 0) {
-        const float resid = A.towers[(size_t)b * kTower + n] + A.towers[((size_t)A.B + b) * kTower + n] +
-                            A.towers[((size_t)2 * A.B + b) * kTower + n];
+        const float resid = st[b * kTower + n] + st[(B + b) * kTower + n] + st[(2 * B + b) * kTower + n];
         A.out[(size_t)b * kTower + n] = v + cI + resid;
       }
     }
@@ -182,6 +222,7 @@ struct GateUpArgs {
 template <int R, int NBM>
 __global__ void __launch_bounds__(kThreads) k_gateup(GateUpArgs A) {
   constexpr int KI = kTower / 256;
+  __shared__ float4 s_u[NBM * kTower / 4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n0 = (blockIdx.x * kWaves + wave) * R;
   float4 wg[R][KI], wu[R][KI], g[KI];
@@ -194,6 +235,8 @@ __global__ void __launch_bounds__(kThreads) k_gateup(GateUpArgs A) {
     }
 #pragma unroll
   for (int i = 0; i < KI; ++i) g[i] = ld4(A.gamma + 256 * i + lane * 4);
+  stage_lds<(NBM * kTower / 4 + kThreads - 1) / kThreads>(A.u, A.B * kTower / 4, s_u);
+  stage_wait();
   float ag[R][NBM], au[R][NBM], ss[NBM];
 #pragma unroll
   for (int b = 0; b < NBM; ++b) {
@@ -203,7 +246,7 @@ __global__ void __launch_bounds__(kThreads) k_gateup(GateUpArgs A) {
     if (b < A.B) {
 #pragma unroll
       for (int i = 0; i < KI; ++i) {
-        const float4 xv = ld4(A.u + (size_t)b * kTower + 256 * i + lane * 4);
+        const float4 xv = s_u[b * (kTower / 4) + 64 * i + lane];
         const float4 in = mul4(xv, g[i]);
         ss[b] += dot4(xv, xv);
 #pragma unroll
@@ -240,28 +283,31 @@ struct DownArgs {
 template <int NBM>
 __global__ void __launch_bounds__(kThreads) k_down(DownArgs A) {
   constexpr int KI = kFfn / 256;
+  __shared__ float4 s_h[NBM * kFfn / 4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = blockIdx.x * kWaves + wave;
   float4 w[KI];
 #pragma unroll
   for (int i = 0; i < KI; ++i) w[i] = ld4(A.Wd + (size_t)n * kFfn + 256 * i + lane * 4);
+  // residual inputs of this row, one per batch row (lane b)
+  const float resid = lane < A.B ? A.u[(size_t)lane * kTower + n] : 0.0f;
+  stage_lds<(NBM * kFfn / 4 + kThreads - 1) / kThreads>(A.hdn, A.B * kFfn / 4, s_h);
+  stage_wait();
   float acc[NBM];
 #pragma unroll
   for (int b = 0; b < NBM; ++b) {
     acc[b] = 0.0f;
     if (b < A.B) {
 #pragma unroll
-      for (int i = 0; i < KI; ++i) acc[b] += dot4(w[i], ld4(A.hdn + (size_t)b * kFfn + 256 * i + lane * 4));
+      for (int i = 0; i < KI; ++i) acc[b] += dot4(w[i], s_h[b * (kFfn / 4) + 64 * i + lane]);
     }
   }
 #pragma unroll
   for (int b = 0; b < NBM; ++b) {
     if (b < A.B) {
       const float v = wave_sum64(acc[b]);
-      if (lane == 0) {
-        const size_t o = (size_t)b * kTower + n;
-        A.out[o] = A.u[o] + v;
-      }
+      const float r = __shfl(resid, b, 64);
+      if (lane == 0) A.out[(size_t)b * kTower + n] = r + v;
     }
   }
 }
@@ -370,36 +416,42 @@ __global__ void __launch_bounds__(kThreads) k_out_rule(OutArgs A) {
   __shared__ float s_q[kMaxBatch];
   __shared__ int s_start[kMaxBatch + 1];
   __shared__ int s_count[kMaxBatch];
+  __shared__ float4 s_u[kMaxBatch * kTower / 4];
   constexpr int KI = kTower / 256;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int B = A.B;
   float4 wg[KI];
 #pragma unroll
   for (int i = 0; i < KI; ++i) wg[i] = mul4(ld4(A.w + 256 * i + lane * 4), ld4(A.gamma + 256 * i + lane * 4));
-  for (int b = wave; b < A.B; b += kWaves) {
+  const float c = A.c[0];
+  // the rule's operands, loaded before the scores exist (wave 0, lane b)
+  const int fo = wave == 0 && lane < B && A.force != nullptr ? (int)A.force[lane] : -1;
+  const int pos = wave == 0 && lane < B ? A.pos[lane] : 0;
+  stage_lds<(kMaxBatch * kTower / 4 + kThreads - 1) / kThreads>(A.u, B * kTower / 4, s_u);
+  stage_wait();
+  for (int b = wave; b < B; b += kWaves) {
     float d = 0.0f, ss = 0.0f;
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
-      const float4 x = ld4(A.u + (size_t)b * kTower + 256 * i + lane * 4);
+      const float4 x = s_u[b * (kTower / 4) + 64 * i + lane];
       d += dot4(wg[i], x);
       ss += dot4(x, x);
     }
     d = wave_sum64(d);
     ss = wave_sum64(ss);
-    if (lane == 0) s_q[b] = d * rsqrtf(ss / (float)kTower + kEps) + A.c[0];
+    if (lane == 0) s_q[b] = d * rsqrtf(ss / (float)kTower + kEps) + c;
   }
   __syncthreads();
   if (wave != 0) return;
-  int f = 0, pos = 0;
-  if (lane < A.B) {
+  int f = 0;
+  if (lane < B) {
     const float q = s_q[lane];
     A.score[lane] = q;
-    const int fo = A.force != nullptr ? (int)A.force[lane] : -1;
     f = fo >= 0 ? (fo != 0) : ((q > A.theta) || !isfinite(q));
     A.flag[lane] = (uint8_t)f;
-    pos = A.pos[lane];
   }
-  const int cnt = split_count(f != 0, pos, lane, A.B, A.Hkv);
-  write_worklist(cnt, pos + 1, lane, A.B, s_start, s_count, A.worklist);
+  const int cnt = split_count(f != 0, pos, lane, B, A.Hkv);
+  write_worklist(cnt, pos + 1, lane, B, s_start, s_count, A.worklist);
 }
 
 __global__ void __launch_bounds__(64) k_worklist(const uint8_t* flag, const int32_t* pos, int32_t* worklist, int B,
@@ -901,10 +953,7 @@ int launch_recall_head(const HeadParams& p, const int64_t* offs, hipStream_t s) 
   switch (nbm_of(p.B)) {
     case 1: return launch_head_t<1>(p, offs, s);
     case 2: return launch_head_t<2>(p, offs, s);
-    case 4: return launch_head_t<4>(p, offs, s);
-    case 8: return launch_head_t<8>(p, offs, s);
-    case 16: return launch_head_t<16>(p, offs, s);
-    default: return launch_head_t<32>(p, offs, s);
+    default: return launch_head_t<4>(p, offs, s);
   }
 }
 
