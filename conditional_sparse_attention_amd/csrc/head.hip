@@ -713,6 +713,30 @@ __global__ void __launch_bounds__(NW * 64) k_dense(DenseArgs A) {
 #pragma unroll
       for (int sp = 0; sp < KSPLIT; ++sp)
         pv[o][h][sp] = part_get(pb + (size_t)sp * PSZ + h * (PMAIN / 2) + tid + o * NT);
+  // the epilogue's bias and residual operands, in the same batch of loads
+  float ea[NO], eb[NO], ec[NO], ed[NO];
+#pragma unroll
+  for (int o = 0; o < NO; ++o) {
+    const int i = tid + o * NT;
+    const int v = i >> 6, l = i & 63;
+    const int t = v / (NG * 4), cg = (v >> 2) % NG, r = v & 3;
+    const int col = 16 * cg + (l & 15);
+    const int n = rb * ROWS + 16 * t + 4 * (l >> 4) + r;
+    ea[o] = eb[o] = ec[o] = ed[o] = 0.0f;
+    if (col < B) {
+      if (MODE == kTowerMode) {
+        ea[o] = A.bias[z][n];
+      } else if (MODE == kInterMode) {
+        const float* ta = A.xf + (size_t)col * kTower + n;
+        ea[o] = ta[0];
+        eb[o] = ta[(size_t)B * kTower];
+        ec[o] = ta[(size_t)2 * B * kTower];
+        ed[o] = A.bias[0][n];
+      } else if (MODE == kDownMode) {
+        ea[o] = A.resid[(size_t)col * kTower + n];
+      }
+    }
+  }
   if (kNorm) {
     if (tid < NG * 16) {
       float sum = 0.0f;
@@ -734,11 +758,9 @@ __global__ void __launch_bounds__(NW * 64) k_dense(DenseArgs A) {
     for (int sp = 0; sp < KSPLIT; ++sp) y += pv[o][0][sp];
     if (col >= B) continue;
     if (MODE == kTowerMode) {
-      A.out[z][(size_t)col * kTower + n] = silu(y * s_inv[col] + A.bias[z][n]);
+      A.out[z][(size_t)col * kTower + n] = silu(y * s_inv[col] + ea[o]);
     } else if (MODE == kInterMode) {
-      const float* ta = A.xf + (size_t)col * kTower + n;
-      const float resid = ta[0] + ta[(size_t)B * kTower] + ta[(size_t)2 * B * kTower];
-      A.out[0][(size_t)col * kTower + n] = y + A.bias[0][n] + resid;
+      A.out[0][(size_t)col * kTower + n] = y + ed[o] + (ea[o] + eb[o] + ec[o]);
     } else if (MODE == kGateUpMode) {
       float yu = 0.0f;
 #pragma unroll
@@ -746,8 +768,7 @@ __global__ void __launch_bounds__(NW * 64) k_dense(DenseArgs A) {
       const float inv = s_inv[col];
       A.out[0][(size_t)col * kFfn + n] = silu(y * inv) * (yu * inv);
     } else {
-      const size_t oo = (size_t)col * kTower + n;
-      A.out[0][oo] = A.resid[oo] + y;
+      A.out[0][(size_t)col * kTower + n] = ea[o] + y;
     }
   }
   if (tid == 0) __hip_atomic_store(A.tickets + rbg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -953,7 +974,8 @@ int launch_recall_head(const HeadParams& p, const int64_t* offs, hipStream_t s) 
   switch (nbm_of(p.B)) {
     case 1: return launch_head_t<1>(p, offs, s);
     case 2: return launch_head_t<2>(p, offs, s);
-    default: return launch_head_t<4>(p, offs, s);
+    case 4: return launch_head_t<4>(p, offs, s);
+    default: return launch_head_t<8>(p, offs, s);
   }
 }
 

@@ -10,8 +10,10 @@ namespace oda {
 constexpr int kHeadTickets = 256;
 // Batches from here on take the dense (MFMA) head path.  The GEMV's cost
 // grows with every batch row it sweeps, the MFMA path's does not up to 16
-// columns; they cross between 4 and 5 sequences.
-constexpr int kHeadDenseMin = 5;
+// columns; measured at D = 1024 to 4096 they cross between 6 and 8 sequences
+// (GEMV 53.5 / 56.6 us against 61.3 / 61.5 us at 5 / 6 sequences, D = 2048;
+// 63.1 against 61.9 us at 8).
+constexpr int kHeadDenseMin = 7;
 struct HeadWs {
   float* towers;  // [3][B][T]  (a, b, c)
   float* u0;      // [B][T]
