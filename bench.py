@@ -492,7 +492,8 @@ def run(args, wl, stream, torch):
                        "duration_source": "HIP events on the launch stream around each step's graph of the L "
                                           "full-attention launches (empty launches included, with zero bytes)",
                        "attention_kernels_frac": out["attention_kernels"]["kv_frac_peak"],
-                       "trace_window": {"k_attn_full": [before * L, nlaunch], "k_attn_local": [before * L, nlaunch]}}
+                       "trace_window": {"k_attn_full": [before * L, nlaunch], "k_attn_local": [before * L, nlaunch],
+                                        "pid": os.getpid()}}
     if args.rate_sweep and wl.bernoulli_odd is None:
         out["rate_sweep"] = rate_sweep(args, S, graphs)
     del graphs
@@ -707,7 +708,7 @@ def trace_summary(trace_dir: str, bench_json: str) -> None:
     with open(bench_json) as f:
         line = [l for l in f.read().splitlines() if l.strip().startswith("{")][-1]
     rec = json.loads(line)
-    win = rec["roofline"]["trace_window"]
+    win = rec.get("roofline", {}).get("trace_window")
     per_file = {}
     for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
         with open(path, newline="") as f:
@@ -715,8 +716,10 @@ def trace_summary(trace_dir: str, bench_json: str) -> None:
         per_file[path] = rows
     if not per_file:
         raise SystemExit(f"no *kernel_trace.csv under {trace_dir}")
-    path, rows = max(per_file.items(), key=lambda kv: sum("k_attn_full" in r[0] for r in kv[1]))
-    rows.sort(key=lambda r: r[1])
+    pid = (win or {}).get("pid")
+    path = _bench_process_file(list(per_file), pid,
+                               lambda p: (sum("k_attn_full" in r[0] for r in per_file[p]), len(per_file[p])))
+    rows = sorted(per_file[path], key=lambda r: r[1])
 
     def stats(sel):
         agg = {}
@@ -734,6 +737,19 @@ def trace_summary(trace_dir: str, bench_json: str) -> None:
         ds = [r for r in rows if kernel in r[0]]
         return ds[first:first + n]
 
+    if win is None:
+        # a line without attention windows (decoder, hybrid, training): the
+        # whole process only
+        total = sum((t1 - t0) for _, t0, t1 in rows) / 1e3
+        out = [f"Trace file: `{os.path.relpath(path, trace_dir)}` ({len(rows)} dispatches, {total / 1e3:.1f} ms of "
+               f"kernel time). JSON line of the profiled run: `{rec['metric']}`, value {rec['value']} {rec['unit']}, "
+               f"{rec['steps']} steps, warm-up {rec['warmup']}.", "",
+               "| kernel | calls | total (us) | avg (us) | min (us) | max (us) | % of kernel time |",
+               "|---|---|---|---|---|---|---|"]
+        for name, (n, tot, mn, mx) in stats(rows)[:25]:
+            out.append(f"| `{name}` | {n} | {tot:.1f} | {tot / n:.2f} | {mn:.2f} | {mx:.2f} | {100 * tot / total:.1f} |")
+        print("\n".join(out))
+        return
     wl_full, wl_local = window("k_attn_full"), window("k_attn_local")
     t_lo, t_hi = wl_local[0][1], wl_full[-1][2]
     region = [r for r in rows if r[1] >= t_lo and r[2] <= t_hi]
@@ -764,7 +780,19 @@ def trace_summary(trace_dir: str, bench_json: str) -> None:
     print("\n".join(out))
 
 
-def _pmc_rows(run_dir: str, counter: str):
+def _bench_process_file(paths, pid, count_full):
+    """The trace file of the bench process: the one rocprofv3 named after the
+    pid the JSON line gives (<pid>_...csv); without a pid, the file with the
+    most k_attn_full dispatches."""
+    if pid is not None:
+        own = [p for p in paths if os.path.basename(p).startswith(f"{pid}_")]
+        if own:
+            return own[0]
+        raise SystemExit(f"no trace file of process {pid} among {len(paths)} files")
+    return max(paths, key=count_full)
+
+
+def _pmc_rows(run_dir: str, counter: str, pid=None):
     """Per-dispatch (kernel, value) of one counter from a rocprofv3 --pmc
     csv run: the process with the most k_attn_full dispatches, in dispatch
     order."""
@@ -778,8 +806,8 @@ def _pmc_rows(run_dir: str, counter: str):
         per_file[path] = rows
     if not per_file:
         raise SystemExit(f"no {counter} rows under {run_dir}")
-    path, rows = max(per_file.items(), key=lambda kv: sum("k_attn_full" in r[1] for r in kv[1]))
-    rows.sort()
+    path = _bench_process_file(list(per_file), pid, lambda p: sum("k_attn_full" in r[1] for r in per_file[p]))
+    rows = sorted(per_file[path])
     return path, [(k, v) for _, k, v in rows]
 
 
