@@ -664,9 +664,17 @@ def rate_sweep(args, S, graphs):
         slope, icpt = np.polyfit(x, y, 1)
         pred = slope * x + icpt
         r2 = 1 - np.sum((y - pred) ** 2) / max(np.sum((y - y.mean()) ** 2), 1e-30)
+        # one unit of rate flags every sequence: the slope over B is the
+        # marginal cost of one flagged sequence-step, whose full-branch KV
+        # bytes are L * 4096 B per key of its mean length over the steps
+        t_mean = float(np.mean(wl.t0)) + (args.steps + 1) / 2.0
+        seq_bytes = wl.layers * t_mean * wl.hkv * wl.head_dim * 2 * 2
+        per_seq_ms = float(slope) / wl.batch
         return {"points": res, "timing": "per-step hip-graph replay, median of repeats",
                 "fit_ms_per_step": {"slope_per_unit_rate": round(float(slope), 4),
-                                    "intercept": round(float(icpt), 4), "r2": round(float(r2), 5)}}
+                                    "intercept": round(float(icpt), 4), "r2": round(float(r2), 5)},
+                "marginal_flagged_sequence": {"ms": round(per_seq_ms, 4), "kv_bytes": int(seq_bytes),
+                                              "gbs": round(seq_bytes / (per_seq_ms * 1e-3) / 1e9, 1)}}
     return {"points": res}
 
 
