@@ -196,12 +196,14 @@ def test_worklist_entry_point_bitexact():
             assert decode_items(w[1:1 + w[0]]) == want_worklist(flags, pos.astype(np.int64) + 1, hkv), (hkv, B)
 
 
-@pytest.mark.parametrize("B,hq", [(1, 16), (4, 16), (5, 8), (8, 16), (9, 8), (16, 32), (17, 16), (32, 8), (32, 32), (24, 16)])
+@pytest.mark.parametrize("B,hq", [(1, 16), (4, 16), (5, 8), (6, 32), (7, 16), (8, 16), (9, 8), (16, 32), (17, 16),
+                                  (32, 8), (32, 32), (24, 16)])
 def test_recall_head_batch_sizes(B, hq):
     """oda_recall_score alone, on both sides of the switch from the
-    bandwidth-shaped GEMV (up to 4 sequences) to the fp32 MFMA GEMMs (5 and
-    up: one 16-wide column group through 16, two from 17), at D = 1024, 2048
-    and 4096, with a perturbed head so every bias and gain term counts.
+    bandwidth-shaped GEMV (up to 6 sequences: batch widths 1, 2, 4 and 8) to
+    the fp32 MFMA GEMMs (7 and up: one 16-wide column group through 16, two
+    from 17), at D = 1024, 2048 and 4096, with a perturbed head so every bias
+    and gain term counts.
     Scores to 1e-4 (1 + |q|); flags bit-exact outside the tie band; the work
     list bit-exact against the oracle's for the GPU's flags."""
     from _harness import SCORE_TOL, TIE_BAND, decode_items, want_worklist
