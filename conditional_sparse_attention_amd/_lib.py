@@ -17,7 +17,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboda.so")
 
 ODA_OK = 0
-ODA_E_NULL, ODA_E_DIMS, ODA_E_UNSUPPORTED, ODA_E_WORKSPACE, ODA_E_LAYER, ODA_E_LAUNCH = -1, -2, -3, -4, -5, -6
+ODA_E_NULL, ODA_E_DIMS, ODA_E_UNSUPPORTED, ODA_E_WORKSPACE, ODA_E_LAYER, ODA_E_LAUNCH, ODA_E_ALIGN = \
+    -1, -2, -3, -4, -5, -6, -7
 ODA_KV_CONTIG, ODA_KV_PAGED = 0, 1
 ODA_ERR_CAPACITY, ODA_ERR_BLOCK, ODA_ERR_TOKEN, ODA_ERR_ROW = 1, 2, 4, 8
 ODA_DEC_LOCAL, ODA_DEC_FULL = 0, 1

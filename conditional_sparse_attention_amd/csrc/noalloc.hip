@@ -65,6 +65,7 @@ extern "C" int oda_local_attn_noalloc(const oda_dims* dims, int32_t layer, const
                                       oda_bf16* out, float* lse, int32_t* err, hipStream_t stream) {
   const int st = check_attn_operands(dims, layer, kv, pos, q, k_cur, v_cur, out);
   if (st != ODA_OK) return st;
+  if (!aligned_to(lse, 4) || !aligned_to(err, 4)) return ODA_E_ALIGN;
   size_t tick_off, part_off;
   const size_t need = scratch_need(dims, &tick_off, &part_off);
   // the ticket region cleared at set-up covers up to kMaxBatch * 1024 pairs

@@ -159,6 +159,9 @@ int check_attn_operands(const oda_dims* d, int32_t layer, const oda_kv* kv, cons
     return ODA_E_NULL;
   if (d->kv_layout == ODA_KV_PAGED && kv->block_tables == nullptr) return ODA_E_NULL;
   if (layer < 0 || layer >= d->num_layers) return ODA_E_LAYER;
+  if (!aligned_to(kv->k, 16) || !aligned_to(kv->v, 16) || !aligned_to(kv->block_tables, 4) || !aligned_to(pos, 4) ||
+      !aligned_to(q, 16) || !aligned_to(kc, 16) || !aligned_to(vc, 16) || !aligned_to(out, 16))
+    return ODA_E_ALIGN;
   return ODA_OK;
 }
 
@@ -168,6 +171,7 @@ static int check_attn_args(const oda_dims* d, int32_t layer, const oda_kv* kv, c
   const int st = check_attn_operands(d, layer, kv, pos, q, kc, vc, out);
   if (st != ODA_OK) return st;
   if (ws == nullptr) return ODA_E_NULL;
+  if (!aligned_to(ws, 16)) return ODA_E_ALIGN;
   *L = ws_layout(d);
   if (ws_bytes < L->total) return ODA_E_WORKSPACE;
   return ODA_OK;
@@ -208,6 +212,7 @@ const char* oda_status_str(int status) {
     case ODA_E_WORKSPACE: return "workspace smaller than oda_workspace_bytes()";
     case ODA_E_LAYER: return "layer index out of range";
     case ODA_E_LAUNCH: return "kernel launch failed";
+    case ODA_E_ALIGN: return "a device pointer is not aligned as the ABI requires";
     default: return "unknown status";
   }
 }
@@ -236,6 +241,7 @@ int oda_workspace_init(const oda_dims* dims, void* ws, size_t ws_bytes, hipStrea
   int st;
   if (!dims_valid(dims, &st)) return st;
   if (ws == nullptr) return ODA_E_NULL;
+  if (!aligned_to(ws, 16)) return ODA_E_ALIGN;
   const WsLayout L = ws_layout(dims);
   if (ws_bytes < L.total) return ODA_E_WORKSPACE;
   // header, work list and every ticket array lie in [0, part_local)
@@ -246,6 +252,7 @@ int oda_local_ranges(const oda_dims* dims, const int32_t* pos, int32_t* ranges, 
   int st;
   if (!dims_valid(dims, &st)) return st;
   if (pos == nullptr || ranges == nullptr) return ODA_E_NULL;
+  if (!aligned_to(pos, 4) || !aligned_to(ranges, 4)) return ODA_E_ALIGN;
   return launch_ranges(pos, ranges, dims->batch, dims->sink, dims->window, stream);
 }
 
@@ -255,6 +262,7 @@ int oda_local_attn(const oda_dims* dims, int32_t layer, const oda_kv* kv, const 
   WsLayout L;
   const int st = check_attn_args(dims, layer, kv, pos, q, k_cur, v_cur, out, ws, ws_bytes, &L);
   if (st != ODA_OK) return st;
+  if (!aligned_to(lse, 4)) return ODA_E_ALIGN;
   const AttnParams p = attn_params(dims, layer, kv, pos, q, k_cur, v_cur, out, lse, ws, L, false);
   return launch_local_attn(p, dims->num_q_heads / dims->num_kv_heads, dims->kv_layout == ODA_KV_PAGED, stream);
 }
@@ -265,6 +273,7 @@ int oda_full_attn_if(const oda_dims* dims, int32_t layer, const oda_kv* kv, cons
   WsLayout L;
   const int st = check_attn_args(dims, layer, kv, pos, q, k_cur, v_cur, out, ws, ws_bytes, &L);
   if (st != ODA_OK) return st;
+  if (!aligned_to(lse, 4)) return ODA_E_ALIGN;
   const AttnParams p = attn_params(dims, layer, kv, pos, q, k_cur, v_cur, out, lse, ws, L, true);
   return launch_full_attn(p, dims->num_q_heads / dims->num_kv_heads, dims->kv_layout == ODA_KV_PAGED, stream);
 }
@@ -277,6 +286,9 @@ int oda_recall_score(const oda_dims* dims, const float* head_w, const oda_bf16* 
   if (head_w == nullptr || h_prev == nullptr || emb == nullptr || h_local == nullptr || pos == nullptr ||
       score == nullptr || flag == nullptr || ws == nullptr)
     return ODA_E_NULL;
+  if (!aligned_to(head_w, 16) || !aligned_to(h_prev, 16) || !aligned_to(emb, 16) || !aligned_to(h_local, 16) ||
+      !aligned_to(pos, 4) || !aligned_to(score, 4) || !aligned_to(ws, 16))
+    return ODA_E_ALIGN;
   const WsLayout L = ws_layout(dims);
   if (ws_bytes < L.total) return ODA_E_WORKSPACE;
   int64_t offs[ODA_HEAD_NTENSORS + 1];
@@ -306,6 +318,7 @@ int oda_worklist(const oda_dims* dims, const uint8_t* flag, const int32_t* pos, 
   int st;
   if (!dims_valid(dims, &st)) return st;
   if (flag == nullptr || pos == nullptr || ws == nullptr) return ODA_E_NULL;
+  if (!aligned_to(pos, 4) || !aligned_to(ws, 16)) return ODA_E_ALIGN;
   const WsLayout L = ws_layout(dims);
   if (ws_bytes < L.total) return ODA_E_WORKSPACE;
   return launch_worklist(flag, pos, reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.worklist), dims->batch,
@@ -323,6 +336,10 @@ int oda_commit(const oda_dims* dims, const oda_kv* kv, int32_t* pos, const uint8
       out_last_L == nullptr || out_last_F == nullptr || h_prev == nullptr || ws == nullptr)
     return ODA_E_NULL;
   if (dims->kv_layout == ODA_KV_PAGED && kv->block_tables == nullptr) return ODA_E_NULL;
+  if (!aligned_to(kv->k, 16) || !aligned_to(kv->v, 16) || !aligned_to(kv->block_tables, 4) || !aligned_to(pos, 4) ||
+      !aligned_to(k_cur_L, 16) || !aligned_to(v_cur_L, 16) || !aligned_to(k_cur_F, 16) || !aligned_to(v_cur_F, 16) ||
+      !aligned_to(out_last_L, 16) || !aligned_to(out_last_F, 16) || !aligned_to(h_prev, 16) || !aligned_to(ws, 16))
+    return ODA_E_ALIGN;
   const WsLayout L = ws_layout(dims);
   if (ws_bytes < L.total) return ODA_E_WORKSPACE;
   CommitParams p;

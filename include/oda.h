@@ -23,6 +23,13 @@
  *    the compute-unit count (queried once, used to size grids).  Calls that
  *    share a workspace `ws` must be ordered (same stream); calls on
  *    different workspaces may run concurrently.
+ *  - Alignment: bf16 and float arrays (q, k_cur, v_cur, out, the caches,
+ *    head_w, h_prev, emb, h_local, the staged rows) and `ws` must be 16-byte
+ *    aligned, int32 arrays (pos, block tables, ranges, lse, score) 4-byte
+ *    aligned; the kernels read them with 16-byte vector and direct-to-LDS
+ *    loads.  hipMalloc and torch allocations are 256-byte aligned, and every
+ *    row of the layouts below starts on a 16-byte boundary.  A pointer that
+ *    breaks this is refused with ODA_E_ALIGN.
  *  - Return value: ODA_OK (0) or a negative ODA_E_* code.  On an error
  *    nothing has been launched and no memory has been touched.
  *  - Conditions that can only be seen on the device (a position beyond the
@@ -70,6 +77,7 @@ extern "C" {
 #define ODA_E_WORKSPACE (-4)   /* ws_bytes smaller than oda_workspace_bytes(dims) */
 #define ODA_E_LAYER (-5)       /* layer index outside [0, num_layers) */
 #define ODA_E_LAUNCH (-6)      /* the HIP runtime rejected a kernel launch */
+#define ODA_E_ALIGN (-7)       /* a device pointer is not aligned as the rules above require */
 
 /* kv_layout */
 #define ODA_KV_CONTIG 0

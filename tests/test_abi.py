@@ -86,6 +86,25 @@ def test_entry_points_reject_bad_arguments_without_launching():
     assert lib.oda_workspace_init(dp, None, ws_bytes, None) == C.ODA_E_NULL
     assert lib.oda_local_ranges(None, fake, fake, None) == C.ODA_E_NULL
     assert C.status_str(C.ODA_E_WORKSPACE).startswith("workspace")
+    # alignment: 16 bytes for bf16 / float arrays and the workspace, 4 for int32 and lse
+    odd = fake + 2
+    k2 = ctypes.byref(kv2)
+    assert lib.oda_local_attn(dp, 0, k2, fake, odd, fake, fake, fake, None, fake, ws_bytes, None) == C.ODA_E_ALIGN
+    assert lib.oda_full_attn_if(dp, 0, k2, fake, fake, fake, fake, odd, None, fake, ws_bytes, None) == C.ODA_E_ALIGN
+    assert lib.oda_local_attn(dp, 0, k2, *args, odd, fake, ws_bytes, None) == C.ODA_E_ALIGN
+    assert lib.oda_local_attn(dp, 0, k2, *args, None, fake + 8, ws_bytes, None) == C.ODA_E_ALIGN
+    assert lib.oda_local_attn(dp, 0, ctypes.byref(C.oda_kv(fake + 4, fake, None)), *args, None, fake, ws_bytes,
+                              None) == C.ODA_E_ALIGN
+    assert lib.oda_recall_score(dp, fake, odd, fake, fake, ctypes.c_float(0), None, fake, fake, fake, fake, ws_bytes,
+                                None) == C.ODA_E_ALIGN
+    assert lib.oda_recall_score(dp, fake, fake, fake, fake, ctypes.c_float(0), None, fake + 1, fake, fake, fake,
+                                ws_bytes, None) == C.ODA_E_ALIGN
+    assert lib.oda_commit(dp, k2, fake, fake, *([fake] * 6), odd, fake, ws_bytes, None) == C.ODA_E_ALIGN
+    assert lib.oda_worklist(dp, fake, fake, fake + 4, ws_bytes, None) == C.ODA_E_ALIGN
+    assert lib.oda_workspace_init(dp, fake + 4, ws_bytes, None) == C.ODA_E_ALIGN
+    assert lib.oda_local_ranges(dp, fake + 2, fake, None) == C.ODA_E_ALIGN
+    assert lib.oda_local_attn_noalloc(dp, 0, k2, *args, None, fake + 2, None) == C.ODA_E_ALIGN
+    assert "aligned" in C.status_str(C.ODA_E_ALIGN)
     # the variant without a workspace: the same argument checks, and dims
     # whose split partials exceed the library's fixed scratch are refused
     assert lib.oda_local_attn_noalloc(dp, 0, kp, *([None] * 7), None) == C.ODA_E_NULL
