@@ -8,6 +8,7 @@
 #include <mutex>
 
 #include "oda_internal.h"
+#include "abi_align.h"
 
 namespace oda {
 namespace {

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include "head_internal.h"
+#include "abi_align.h"
 
 namespace oda {
 

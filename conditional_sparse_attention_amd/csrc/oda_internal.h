@@ -148,9 +148,6 @@ AttnParams attn_params_at(const ::oda_dims* d, int32_t layer, const ::oda_kv* kv
                           float* part, int32_t* tickets, int32_t* header, const int32_t* worklist);
 // The argument checks every attention call makes (dims, non-NULL operands,
 // block tables of a paged cache, layer range); ODA_OK or an error code.
-// alignment the ABI requires of a device pointer (NULL passes: optional
-// arguments are checked for presence separately)
-inline bool aligned_to(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 int check_attn_operands(const ::oda_dims* d, int32_t layer, const ::oda_kv* kv, const int32_t* pos,
                         const uint16_t* q, const uint16_t* kc, const uint16_t* vc, const uint16_t* out);
 
