@@ -50,6 +50,7 @@ typedef __attribute__((address_space(1))) const v4u_t gv4_t;
 // bounds (see local_splits()).
 constexpr int kLocalSplitsMin = 1;
 constexpr int kLocalSplitsMax = 8;
+constexpr int kLocalSplitsMaxPaged = 16;  // the paged walk streams slower per workgroup
 // Waves per workgroup of the local kernel: kLocalWaves, or kLocalWavesWide
 // when a (sequence, KV head) is cut into at most kLocalWideMax splits (each
 // workgroup then streams a larger share alone).
@@ -665,7 +666,8 @@ __global__ void __launch_bounds__(NW * 64) k_attn_local(AttnParams P) {
   const int v_lo = split * chunk;
   const int v_hi = (v_lo + chunk) < n ? v_lo + chunk : n;
   float* part_bg = P.part + ((size_t)(b * P.Hkv + g) * kLocalMaxSplits) * G * kPartStride;
-  attn_unit<G, PAGED, NW, ODA_LOCAL_DEPTH, ODA_LOCAL_U, kLocalSplitsMax, ROPE>(P, b, g, split, ns, v_lo, v_hi, S, P.tickets + b * P.Hkv + g, part_bg, lds);
+  constexpr int kMaxS = PAGED ? kLocalSplitsMaxPaged : kLocalSplitsMax;
+  attn_unit<G, PAGED, NW, ODA_LOCAL_DEPTH, ODA_LOCAL_U, kMaxS, ROPE>(P, b, g, split, ns, v_lo, v_hi, S, P.tickets + b * P.Hkv + g, part_bg, lds);
 }
 
 // The persistent grid walks units u = (work-list item) * Hkv + KV head.
@@ -744,24 +746,30 @@ int device_cus() {
 // Workgroups per (sequence, KV head) in the local branch: enough for one per
 // compute unit over the whole batch, ceil(CUs / (B Hkv)), two per compute
 // unit for the paged layout (its block-table walk streams slower per
-// workgroup), within [kLocalSplitsMin, kLocalSplitsMax].  The local set is
-// small (at most sink + window keys), so past 8 splits the cross-workgroup
-// merge costs more than the extra streaming parallelism gains.  At 8 KV
-// heads, contiguous: 8 splits up to 4 sequences, 4 at 8, 2 at 16, 1 (no
-// merge at all) at 32; paged: 2 at 32.  Measured per launch against four
-// per compute unit (at least 4 splits): 16.2 / 17.2 us at 8 x 16K, 28.9 /
-// 33.0 us at 16 x 64K with group size 4, 43.4 / 48.8 us at 32 x 4K
-// contiguous, and the same within 2% at 4 x 128K.
+// workgroup), within [kLocalSplitsMin, kLocalSplitsMax] (contiguous) or
+// [kLocalSplitsMin, kLocalSplitsMaxPaged] (paged).  The local set is small
+// (at most sink + window keys): for a contiguous cache past 8 splits the
+// cross-workgroup merge costs more than the extra streaming parallelism
+// gains (16 splits: the same at 1 sequence, 10-13% slower at 2 and 3); the
+// paged walk gains up to 16 (per launch at 128K, 16 / 8 heads: 11.8 / 15.2 us
+// at 1 sequence, 13.5 / 15.9 at 2, 15.1 / 16.4 at 3, 16.2 / 16.8 at 4, 18.7
+// / 19.6 at 6).  At 8 KV heads, contiguous: 8 splits up to 4 sequences, 4 at
+// 8, 2 at 16, 1 (no merge at all) at 32; paged: 16 up to 4, 2 at 32.
+// Measured per launch against four per compute unit (at least 4 splits):
+// 16.2 / 17.2 us at 8 x 16K, 28.9 / 33.0 us at 16 x 64K with group size 4,
+// 43.4 / 48.8 us at 32 x 4K contiguous, and the same within 2% at 4 x 128K.
 int local_splits(const AttnParams& p, bool paged) {
   const int pairs = p.B * p.Hkv;
   const int per_cu = paged ? 2 : 1;
+  const int cap = paged ? kLocalSplitsMaxPaged : kLocalSplitsMax;
   const int ns = (per_cu * device_cus() + pairs - 1) / pairs;
-  return ns < kLocalSplitsMin ? kLocalSplitsMin : (ns > kLocalSplitsMax ? kLocalSplitsMax : ns);
+  return ns < kLocalSplitsMin ? kLocalSplitsMin : (ns > cap ? cap : ns);
 }
 
 template <int G, bool PAGED, bool ROPE>
 int launch_local_t(const AttnParams& p_in, hipStream_t s) {
-  static_assert(kLocalSplitsMax <= kLocalMaxSplits, "local splits exceed the workspace slots");
+  static_assert(kLocalSplitsMax <= kLocalMaxSplits && kLocalSplitsMaxPaged <= kLocalMaxSplits,
+                "local splits exceed the workspace slots");
   AttnParams p = p_in;
   p.local_splits = local_splits(p, PAGED);
   dim3 grid(p.local_splits, p.Hkv, p.B);
