@@ -33,6 +33,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kJB = 4;                                // 32-k blocks per wave pass (128 k)
 constexpr int kWaveK = kJB * 32;
 constexpr int kMaxCols = 32;
+constexpr int kMaxSlices = 16;                        // K slices of one GEMM launch, at most
 
 enum GemmMode { kQkv = 0, kOut = 1, kGateUp = 2, kDown = 3, kLogits = 4 };
 
@@ -236,14 +237,27 @@ __global__ void __launch_bounds__(NW * 64) k_gemm16(GemmArgs A) {
       s_last = __hip_atomic_fetch_add(A.tickets + rbg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nks - 1;
     __syncthreads();
     if (!s_last) return;
+    // every slice's partial in one batch of loads, then added in slice order
     for (int i = tid; i < PMAIN; i += NT) {
+      float v[kMaxSlices];
+#pragma unroll
+      for (int sp = 0; sp < kMaxSlices; ++sp)
+        if (sp < nks) v[sp] = part_get(pb + (size_t)sp * PSZ + i);
       float s = 0.0f;
-      for (int sp = 0; sp < nks; ++sp) s += part_get(pb + (size_t)sp * PSZ + i);
+#pragma unroll
+      for (int sp = 0; sp < kMaxSlices; ++sp)
+        if (sp < nks) s += v[sp];
       tile[i] = s;
     }
     if (kNorm && tid < NG * 16) {
+      float v[kMaxSlices];
+#pragma unroll
+      for (int sp = 0; sp < kMaxSlices; ++sp)
+        if (sp < nks) v[sp] = part_get(pb + (size_t)sp * PSZ + PMAIN + tid);
       float s = 0.0f;
-      for (int sp = 0; sp < nks; ++sp) s += part_get(pb + (size_t)sp * PSZ + PMAIN + tid);
+#pragma unroll
+      for (int sp = 0; sp < kMaxSlices; ++sp)
+        if (sp < nks) s += v[sp];
       s_ss[tid] = s;
     }
     if (tid == 0) __hip_atomic_store(A.tickets + rbg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -539,7 +553,8 @@ int launch_gemm_nw(const GemmArgs& a, GemmShape s, hipStream_t st) {
 
 template <int MODE, int TW>
 int launch_gemm(const GemmArgs& a, GemmShape s, hipStream_t st) {
-  if (s.tw != TW || a.K % (s.nks * s.nw * kWaveK) != 0 || a.K / s.nks < s.nw * kWaveK) return ODA_E_UNSUPPORTED;
+  if (s.tw != TW || s.nks > kMaxSlices || a.K % (s.nks * s.nw * kWaveK) != 0 || a.K / s.nks < s.nw * kWaveK)
+    return ODA_E_UNSUPPORTED;
   int rc;
   if constexpr (MODE == kLogits) {
     if (s.nw != 4) return ODA_E_UNSUPPORTED;
