@@ -327,46 +327,61 @@ struct OutArgs {
   int B, Hkv;
 };
 
+// The rule wave's per-sequence values are exchanged through LDS: lane
+// b < kMaxBatch writes its entry, then every lane reads the whole table with
+// wave-uniform addresses (broadcast reads, issued back to back), so each
+// reduction costs one LDS round trip instead of a chain of cross-lane
+// shuffles.  Lanes of one wave run their LDS accesses in order; the
+// wavefront-scope fence keeps the compiler from moving the reads above the
+// writes.
+struct RuleLds {
+  int t[kMaxBatch];    // t = pos + 1 of a flagged sequence, else 0
+  int4 p[kMaxBatch];   // (na, nb, ua, ub): both candidate cuts and their unit lengths
+  int2 w[kMaxBatch];   // (nsplit, unit length) of the chosen cut, 0 when unflagged
+};
+__device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
+
 // Lane b < B of one wave (B <= 32) holds sequence b's flag f and position:
 // its split count under the policy stated in oda.h, which depends on every
 // flagged lane (their number, their keys together, and the cost of the two
-// candidate cuts summed or maximised over the wave).
-__device__ __forceinline__ int64_t wave_sum_i64(int64_t x) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
-  return x;
-}
-__device__ __forceinline__ int wave_max_i32(int x) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    const int y = __shfl_xor(x, d, 64);
-    x = x > y ? x : y;
-  }
-  return x;
-}
-__device__ __forceinline__ int wave_min_i32(int x) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    const int y = __shfl_xor(x, d, 64);
-    x = x < y ? x : y;
-  }
-  return x;
-}
-__device__ __forceinline__ int split_count(bool f, int pos, int lane, int B, int hkv) {
+// candidate cuts summed or maximised over the batch).  Integer sums, maxima
+// and minima: the same in any order.
+__device__ __forceinline__ int split_count(bool f, int pos, int lane, int B, int hkv, RuleLds* L) {
   const bool on = f && lane < B;
   const int nflag = __popcll(__ballot(on));
   const int t = pos + 1;
-  const int64_t total = wave_sum_i64(on ? (int64_t)t : 0);
+  if (lane < kMaxBatch) L->t[lane] = on ? t : 0;
+  wave_lds_fence();
+  int64_t total = 0;
+#pragma unroll
+  for (int o = 0; o < kMaxBatch; o += 4) {
+    const int4 v = *reinterpret_cast<const int4*>(&L->t[o]);
+    total += (int64_t)v.x + v.y + v.z + v.w;
+  }
   const int na = on ? full_nsplit_round(t, nflag, hkv, total) : 0;
   const int nb = on ? full_nsplit_rounds(t, hkv, total) : 0;
-  const int64_t units_a = wave_sum_i64((int64_t)na * hkv);
-  const int64_t units_b = wave_sum_i64((int64_t)nb * hkv);
   const int ua = na > 0 ? (t + na - 1) / na : 0;
   const int ub = nb > 0 ? (t + nb - 1) / nb : 0;
-  const int long_a = wave_max_i32(ua), long_b = wave_max_i32(ub);
-  const int short_a = wave_min_i32(on ? ua : 0x7FFFFFFF), short_b = wave_min_i32(on ? ub : 0x7FFFFFFF);
-  const int64_t cost_a = full_split_cost(units_a, long_a, short_a, total, hkv);
-  const int64_t cost_b = full_split_cost(units_b, long_b, short_b, total, hkv);
+  if (lane < kMaxBatch) L->p[lane] = make_int4(na, nb, ua, ub);
+  wave_lds_fence();
+  int4 tab[kMaxBatch];
+#pragma unroll
+  for (int o = 0; o < kMaxBatch; ++o) tab[o] = L->p[o];  // all reads in flight together
+  int sa = 0, sb = 0;  // at most 32 x 32 splits
+  int long_a = 0, long_b = 0, short_a = 0x7FFFFFFF, short_b = 0x7FFFFFFF;
+#pragma unroll
+  for (int o = 0; o < kMaxBatch; ++o) {
+    const int4 v = tab[o];
+    sa += v.x;
+    sb += v.y;
+    long_a = max(long_a, v.z);
+    long_b = max(long_b, v.w);
+    // a flagged entry has both counts >= 1; unflagged entries hold zeros
+    short_a = min(short_a, v.x > 0 ? v.z : 0x7FFFFFFF);
+    short_b = min(short_b, v.y > 0 ? v.w : 0x7FFFFFFF);
+  }
+  const int64_t cost_a = full_split_cost((int64_t)sa * hkv, long_a, short_a, total, hkv);
+  const int64_t cost_b = full_split_cost((int64_t)sb * hkv, long_b, short_b, total, hkv);
   return cost_b < cost_a ? nb : na;
 }
 
@@ -374,39 +389,31 @@ __device__ __forceinline__ int split_count(bool f, int pos, int lane, int B, int
 // descending unit length ceil(t / nsplit) (ties by ascending b), each with
 // its items (b << 20) | (nsplit << 10) | split for split = 0 .. nsplit-1.
 // Lanes < B of one wave (B <= 32) hold cnt = nsplit (0 when unflagged) and
-// t = pos + 1.  Each lane ranks itself against every other lane, the counts
-// are placed in rank order in LDS, an exclusive scan over ranks gives the
-// start of each sequence's items.
-__device__ __forceinline__ void write_worklist(int cnt, int t, int lane, int B, int* s_start, int* s_count,
-                                               int32_t* worklist) {
+// t = pos + 1.  A flagged lane's items start after those of every flagged
+// sequence ordered before it, so each lane sums those counts over the
+// broadcast table and writes its items there; lane 0 writes the total.
+__device__ __forceinline__ void write_worklist(int cnt, int t, int lane, int B, RuleLds* L, int32_t* worklist) {
   const int unit = cnt > 0 ? (t + cnt - 1) / cnt : 0;
-  // every lane of the wave runs this loop (the shuffles need them all)
-  int rank = 0, rank_unflagged = 0;
-  for (int o = 0; o < kMaxBatch; ++o) {
-    const int c_o = __shfl(cnt, o, 64);
-    const int u_o = __shfl(unit, o, 64);
-    const bool flagged_o = o < B && c_o > 0;
-    if (flagged_o && (u_o > unit || (u_o == unit && o < lane))) ++rank;
-    if (o < B && !flagged_o && o < lane) ++rank_unflagged;
-  }
-  // unflagged lanes rank after every flagged one, in lane order
-  const int nflag = __popcll(__ballot(cnt > 0 && lane < B));
-  if (cnt == 0) rank = nflag + rank_unflagged;
-  if (lane < B) s_count[rank] = cnt;
-  __builtin_amdgcn_wave_barrier();
-  const int c_r = lane < B ? s_count[lane] : 0;  // count of the sequence ranked `lane`
-  int incl = c_r;
+  if (lane < kMaxBatch) L->w[lane] = make_int2(lane < B ? cnt : 0, unit);
+  wave_lds_fence();
+  int2 tab[kMaxBatch];
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int v = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += v;
+  for (int o = 0; o < kMaxBatch; o += 2) {  // all reads in flight together
+    const int4 v = *reinterpret_cast<const int4*>(&L->w[o]);
+    tab[o] = make_int2(v.x, v.y);
+    tab[o + 1] = make_int2(v.z, v.w);
   }
-  if (lane < B) s_start[lane] = incl - c_r;  // start of rank `lane`
-  if (lane == B - 1) worklist[0] = incl;
-  __builtin_amdgcn_wave_barrier();
+  int start = 0, total = 0;
+#pragma unroll
+  for (int o = 0; o < kMaxBatch; ++o) {
+    const int c = tab[o].x, u = tab[o].y;  // (nsplit, unit length) of sequence o
+    const bool before = c > 0 && (u > unit || (u == unit && o < lane));
+    total += c;
+    start += before ? c : 0;
+  }
+  if (lane == 0) worklist[0] = total;
   if (lane < B && cnt > 0) {
-    const int st = s_start[rank];
-    for (int s = 0; s < cnt; ++s) worklist[1 + st + s] = full_item(lane, cnt, s);
+    for (int s = 0; s < cnt; ++s) worklist[1 + start + s] = full_item(lane, cnt, s);
   }
 }
 
@@ -414,8 +421,7 @@ __device__ __forceinline__ void write_worklist(int cnt, int t, int lane, int B, 
 // rule and writes the compacted work list (exclusive scan of flag * nsplit).
 __global__ void __launch_bounds__(kThreads) k_out_rule(OutArgs A) {
   __shared__ float s_q[kMaxBatch];
-  __shared__ int s_start[kMaxBatch + 1];
-  __shared__ int s_count[kMaxBatch];
+  __shared__ RuleLds s_rule;
   __shared__ float4 s_u[kMaxBatch * kTower / 4];
   constexpr int KI = kTower / 256;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -450,19 +456,18 @@ __global__ void __launch_bounds__(kThreads) k_out_rule(OutArgs A) {
     f = fo >= 0 ? (fo != 0) : ((q > A.theta) || !isfinite(q));
     A.flag[lane] = (uint8_t)f;
   }
-  const int cnt = split_count(f != 0, pos, lane, B, A.Hkv);
-  write_worklist(cnt, pos + 1, lane, B, s_start, s_count, A.worklist);
+  const int cnt = split_count(f != 0, pos, lane, B, A.Hkv, &s_rule);
+  write_worklist(cnt, pos + 1, lane, B, &s_rule, A.worklist);
 }
 
 __global__ void __launch_bounds__(64) k_worklist(const uint8_t* flag, const int32_t* pos, int32_t* worklist, int B,
                                                  int hkv) {
-  __shared__ int s_start[kMaxBatch + 1];
-  __shared__ int s_count[kMaxBatch];
+  __shared__ RuleLds s_rule;
   const int lane = threadIdx.x;
   const bool f = lane < B && flag[lane] != 0;
   const int p = lane < B ? pos[lane] : 0;
-  const int cnt = split_count(f, p, lane, B, hkv);
-  write_worklist(cnt, p + 1, lane, B, s_start, s_count, worklist);
+  const int cnt = split_count(f, p, lane, B, hkv, &s_rule);
+  write_worklist(cnt, p + 1, lane, B, &s_rule, worklist);
 }
 
 // ------------------------------------------------ dense batches: fp32 MFMA
