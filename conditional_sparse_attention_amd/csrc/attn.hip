@@ -50,7 +50,7 @@ typedef __attribute__((address_space(1))) const v4u_t gv4_t;
 // bounds (see local_splits()).
 constexpr int kLocalSplitsMin = 1;
 constexpr int kLocalSplitsMax = 8;
-constexpr int kLocalSplitsMaxPaged = 16;  // the paged walk streams slower per workgroup
+constexpr int kLocalSplitsMaxPaged = 16;  // a paged walk still gains at one sequence
 // Waves per workgroup of the local kernel: kLocalWaves, or kLocalWavesWide
 // when a (sequence, KV head) is cut into at most kLocalWideMax splits (each
 // workgroup then streams a larger share alone).
@@ -111,15 +111,18 @@ struct State {
   float acc[G][8];
 };
 
-// Address of cache row p of (b, g); for the paged layout a block-table
-// entry outside the pool marks the row invalid (ok=false) and returns a
-// safe address.
+// Row index of cache row p of (b, g) (times kHeadDim: its element offset).
+// In the paged layout the block comes from the workgroup's copy of the
+// block-table entries in LDS (tab[i] = entry blk0 + i of the sequence's
+// row); an entry outside the pool marks the row invalid (ok = false) and
+// yields a safe address.
 template <bool PAGED>
-__device__ __forceinline__ size_t row_index(const AttnParams& P, int b, int g, int p, bool& ok) {
+__device__ __forceinline__ size_t row_index(const AttnParams& P, int b, int g, int p, const int32_t* tab, int blk0,
+                                            bool& ok) {
   if (!PAGED) {
     return ((size_t)(b * P.Hkv + g) * (size_t)P.t_cap + (size_t)p);
   } else {
-    int32_t blk = P.tables[(size_t)b * P.max_blocks + (p >> P.log2_block)];
+    int32_t blk = tab[(p >> P.log2_block) - blk0];
     if (blk < 0 || (int64_t)blk >= P.num_blocks) {
       ok = false;
       blk = 0;
@@ -190,8 +193,8 @@ __device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
 // group, clamped to p_hi - 1 and marked invalid beyond it.
 template <bool PAGED, int U>
 __device__ __forceinline__ void load_stage(const AttnParams& P, const uint16_t* Kbg, const uint16_t* Vbg, int b,
-                                           int g, int base, int p_hi, int r, int c, uint4 (&kk)[U], uint4 (&vv)[U],
-                                           bool (&ok)[U]) {
+                                           int g, int base, int p_hi, int r, int c, const int32_t* tab, int blk0,
+                                           uint4 (&kk)[U], uint4 (&vv)[U], bool (&ok)[U]) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int p = base + u * 4 + r;
@@ -202,7 +205,7 @@ __device__ __forceinline__ void load_stage(const AttnParams& P, const uint16_t* 
       off = (size_t)pp * kHeadDim;
     } else {
       bool bok = true;
-      off = row_index<true>(P, b, g, pp, bok) * kHeadDim;
+      off = row_index<true>(P, b, g, pp, tab, blk0, bok) * kHeadDim;
       if (!bok) {
         if (valid && c == 0) atomicOr(P.err, ODA_ERR_BLOCK);
         valid = false;
@@ -288,12 +291,23 @@ __device__ __forceinline__ void rope_q(const AttnParams& P, uint4 (&qv)[G], cons
   for (int h = 0; h < G; ++h) qv[h] = norm_rope8(qv[h], rl.gq, rl.cs, c, P.qk_eps);
 }
 
+// Shared memory of a workgroup, in floats: wg_merge needs NW*G*(128+2),
+// merge_partials NW*64*6; while the cache rows stream, the same memory holds
+// block-table entries of the paged layout.
+template <int G, int NW>
+constexpr int lds_floats() {
+  constexpr int a = NW * G * (kHeadDim + 2);
+  constexpr int b = 6 * NW * 64;
+  return a > b ? a : b;
+}
+
 // Rows [p_lo, p_hi) of the cache.  Wave w takes stages starting at
 // p_lo + (k*NW + w) * 4U.  A ring of DEPTH register stages keeps DEPTH-1
 // stages in flight while one is consumed; its refill is issued right after.
 template <int G, bool PAGED, int NW, int DEPTH, int U, bool ROPE>
-__device__ __forceinline__ void cache_rows(const AttnParams& P, uint4 (&qv)[G], bool& q_ready, const RopeLane& rl,
-                                           State<G>& st, int b, int g, int p_lo, int p_hi, int wave, int r, int c) {
+__device__ __forceinline__ void stream_rows(const AttnParams& P, uint4 (&qv)[G], bool& q_ready, const RopeLane& rl,
+                                            State<G>& st, int b, int g, int p_lo, int p_hi, int wave, int r, int c,
+                                            const int32_t* tab, int blk0) {
   constexpr int kStage = 4 * U;
   constexpr int kStride = NW * kStage;
   const uint16_t* Kbg = P.K;
@@ -315,7 +329,7 @@ __device__ __forceinline__ void cache_rows(const AttnParams& P, uint4 (&qv)[G], 
   const int nst = (p_hi - first + kStride - 1) / kStride;
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d)
-    load_stage<PAGED, U>(P, Kbg, Vbg, b, g, first + d * kStride, p_hi, r, c, kk[d], vv[d], ok[d]);
+    load_stage<PAGED, U>(P, Kbg, Vbg, b, g, first + d * kStride, p_hi, r, c, tab, blk0, kk[d], vv[d], ok[d]);
   // decoder mode: the raw q rows were loaded first; form q while the ring fills
   if constexpr (ROPE) {
     if (!q_ready) {
@@ -328,7 +342,8 @@ __device__ __forceinline__ void cache_rows(const AttnParams& P, uint4 (&qv)[G], 
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       block_update<G, U>(qv, st, kk[d], vv[d], ok[d], P.scale_log2);
-      load_stage<PAGED, U>(P, Kbg, Vbg, b, g, first + (k + d + DEPTH) * kStride, p_hi, r, c, kk[d], vv[d], ok[d]);
+      load_stage<PAGED, U>(P, Kbg, Vbg, b, g, first + (k + d + DEPTH) * kStride, p_hi, r, c, tab, blk0, kk[d], vv[d],
+                           ok[d]);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -336,6 +351,37 @@ __device__ __forceinline__ void cache_rows(const AttnParams& P, uint4 (&qv)[G], 
 #pragma unroll
   for (int d = 0; d + 1 < DEPTH; ++d)
     if (d < rem) block_update<G, U>(qv, st, kk[d], vv[d], ok[d], P.scale_log2);
+}
+
+// Rows [p_lo, p_hi) of the cache, called by every thread of the workgroup.
+// Paged layout: the block-table entries of the rows are first copied into
+// the workgroup's shared memory (as many blocks at a time as it holds), so
+// that a row's address needs no global load of its own: a table load would
+// have to wait behind every cache load already in flight (the vector memory
+// counter completes in order) and would drain the ring at each stage.
+template <int G, bool PAGED, int NW, int DEPTH, int U, bool ROPE>
+__device__ __forceinline__ void cache_rows(const AttnParams& P, uint4 (&qv)[G], bool& q_ready, const RopeLane& rl,
+                                           State<G>& st, int b, int g, int p_lo, int p_hi, int wave, int r, int c,
+                                           float* lds) {
+  if constexpr (!PAGED) {
+    stream_rows<G, PAGED, NW, DEPTH, U, ROPE>(P, qv, q_ready, rl, st, b, g, p_lo, p_hi, wave, r, c, nullptr, 0);
+  } else {
+    constexpr int kCap = lds_floats<G, NW>();  // table entries per window
+    int32_t* tab = reinterpret_cast<int32_t*>(lds);
+    const int lb = P.log2_block;
+    const int32_t* row = P.tables + (size_t)b * P.max_blocks;
+    for (int w_lo = p_lo; w_lo < p_hi;) {
+      const int blk0 = w_lo >> lb;
+      const int64_t w_end = ((int64_t)blk0 + kCap) << lb;
+      const int w_hi = w_end < (int64_t)p_hi ? (int)w_end : p_hi;
+      const int nblk = ((w_hi - 1) >> lb) - blk0 + 1;
+      for (int i = threadIdx.x; i < nblk; i += NW * 64) tab[i] = row[blk0 + i];
+      __syncthreads();
+      stream_rows<G, PAGED, NW, DEPTH, U, ROPE>(P, qv, q_ready, rl, st, b, g, w_lo, w_hi, wave, r, c, tab, blk0);
+      __syncthreads();  // every wave is done with this window's entries
+      w_lo = w_hi;
+    }
+  }
 }
 
 // The current token: one staged row, handled by wave 0 / row group 0.  In
@@ -592,12 +638,14 @@ __device__ void attn_unit(const AttnParams& P, int b, int g, int split, int nspl
   // first range [0, n0) -> positions equal virtual indices
   if (v_lo < S.n0) {
     const int hi = v_cache_hi < S.n0 ? v_cache_hi : S.n0;
-    if (hi > v_lo) cache_rows<G, PAGED, NW, DEPTH, U, ROPE>(P, qv, q_ready, rl, st, b, g, v_lo, hi, wave, r, c);
+    if (hi > v_lo) cache_rows<G, PAGED, NW, DEPTH, U, ROPE>(P, qv, q_ready, rl, st, b, g, v_lo, hi, wave, r, c, lds);
   }
   // second range: virtual n0 + k  ->  position s1 + k
   {
     const int lo = v_lo > S.n0 ? v_lo : S.n0;
-    if (v_cache_hi > lo) cache_rows<G, PAGED, NW, DEPTH, U, ROPE>(P, qv, q_ready, rl, st, b, g, S.s1 + (lo - S.n0), S.s1 + (v_cache_hi - S.n0), wave, r, c);
+    if (v_cache_hi > lo)
+      cache_rows<G, PAGED, NW, DEPTH, U, ROPE>(P, qv, q_ready, rl, st, b, g, S.s1 + (lo - S.n0),
+                                               S.s1 + (v_cache_hi - S.n0), wave, r, c, lds);
   }
   if constexpr (ROPE) {
     if (!q_ready) {  // this wave streamed no cache rows
@@ -637,14 +685,6 @@ __device__ void attn_unit(const AttnParams& P, int b, int g, int split, int nspl
     if (tid == 0) reset_ticket(ticket);
   }
   __syncthreads();
-}
-
-template <int G, int NW>
-constexpr int lds_floats() {
-  // wg_merge needs NW*G*(128+2) floats; merge_partials NW*64*6
-  constexpr int a = NW * G * (kHeadDim + 2);
-  constexpr int b = 6 * NW * 64;
-  return a > b ? a : b;
 }
 
 template <int G, bool PAGED, bool ROPE, int NW>
@@ -744,25 +784,24 @@ int device_cus() {
 }
 
 // Workgroups per (sequence, KV head) in the local branch: enough for one per
-// compute unit over the whole batch, ceil(CUs / (B Hkv)), two per compute
-// unit for the paged layout (its block-table walk streams slower per
-// workgroup), within [kLocalSplitsMin, kLocalSplitsMax] (contiguous) or
-// [kLocalSplitsMin, kLocalSplitsMaxPaged] (paged).  The local set is small
-// (at most sink + window keys): for a contiguous cache past 8 splits the
-// cross-workgroup merge costs more than the extra streaming parallelism
+// compute unit over the whole batch, ceil(CUs / (B Hkv)), within
+// [kLocalSplitsMin, kLocalSplitsMax] for a contiguous cache and
+// [kLocalSplitsMin, kLocalSplitsMaxPaged] for a paged one.  The local set is
+// small (at most sink + window keys): for a contiguous cache past 8 splits
+// the cross-workgroup merge costs more than the extra streaming parallelism
 // gains (16 splits: the same at 1 sequence, 10-13% slower at 2 and 3); the
-// paged walk gains up to 16 (per launch at 128K, 16 / 8 heads: 11.8 / 15.2 us
-// at 1 sequence, 13.5 / 15.9 at 2, 15.1 / 16.4 at 3, 16.2 / 16.8 at 4, 18.7
-// / 19.6 at 6).  At 8 KV heads, contiguous: 8 splits up to 4 sequences, 4 at
-// 8, 2 at 16, 1 (no merge at all) at 32; paged: 16 up to 4, 2 at 32.
-// Measured per launch against four per compute unit (at least 4 splits):
-// 16.2 / 17.2 us at 8 x 16K, 28.9 / 33.0 us at 16 x 64K with group size 4,
-// 43.4 / 48.8 us at 32 x 4K contiguous, and the same within 2% at 4 x 128K.
+// paged walk still gains from 16 at one sequence (9.9 against 11.1 us per
+// launch at 128K, 16 / 8 heads).  Per launch, paged, one workgroup per
+// compute unit against two: 12.6 / 15.2 us at 4 x 128K, 45.6 / 47.4 us at
+// 32 x 4K, 27.3 / 27.5 us at 16 x 16K.  Contiguous, against four per compute
+// unit: 16.2 / 17.2 us at 8 x 16K, 28.9 / 33.0 us at 16 x 64K with group
+// size 4, 43.4 / 48.8 us at 32 x 4K, the same within 2% at 4 x 128K.  At 8
+// KV heads: 8 splits (16 paged at one sequence) up to 4 sequences, 4 at 8,
+// 2 at 16, 1 (no merge at all) at 32.
 int local_splits(const AttnParams& p, bool paged) {
   const int pairs = p.B * p.Hkv;
-  const int per_cu = paged ? 2 : 1;
   const int cap = paged ? kLocalSplitsMaxPaged : kLocalSplitsMax;
-  const int ns = (per_cu * device_cus() + pairs - 1) / pairs;
+  const int ns = (device_cus() + pairs - 1) / pairs;
   return ns < kLocalSplitsMin ? kLocalSplitsMin : (ns > cap ? cap : ns);
 }
 
