@@ -73,16 +73,16 @@ constexpr int kLocalWideMax = 2;
 // Full kernel shape per group size: G = 2 (the 16/8-head models) runs 12
 // waves (3 per SIMD) with a 3-stage ring; G = 1 and G = 4 keep more state per
 // lane and run 8 waves with a 4-stage ring, which keeps a similar number of
-// bytes in flight per CU without spilling (FullDepth: one stage less for the
-// paged layout).
-template <int G>
+// bytes in flight per CU without spilling.  The paged layout holds more per
+// row in flight (a block and an address), so its rings are a stage shorter
+// (G = 2: 2 stages; a 3-stage ring spills at 12 waves and measured slower at
+// 8), and G = 2 runs 8 waves there: 1-4% faster per launch than 12 (e.g.
+// 27.1 / 28.2 us at 8 flagged 4K sequences of 32, 88.4 / 89.7 us at one
+// flagged 128K sequence).
+template <int G, bool PAGED>
 struct FullWaves {
-  static constexpr int value = G == 2 ? ODA_FULL_WAVES_SMALL_G : 8;
+  static constexpr int value = G == 2 ? (PAGED ? 8 : ODA_FULL_WAVES_SMALL_G) : 8;
 };
-// The paged layout keeps a block-table row and an address per stage and row
-// in flight as well; a shallower ring there avoids spilling (G = 2: 2 stages,
-// 7% faster per launch than 3 with spills on a paged 4K batch of 32; G = 1
-// and 4: 3 stages).
 template <int G, bool PAGED>
 struct FullDepth {
   static constexpr int value = PAGED ? (G == 2 ? 2 : 3) : (G == 2 ? ODA_FULL_DEPTH : 4);
@@ -717,8 +717,8 @@ __global__ void __launch_bounds__(NW * 64) k_attn_local(AttnParams P) {
 // the current one.  Once every workgroup has found the list exhausted, the
 // last one to finish clears the counters, so each launch starts from zero.
 template <int G, bool PAGED>
-__global__ void __launch_bounds__(FullWaves<G>::value * 64) k_attn_full(AttnParams P) {
-  constexpr int NW = FullWaves<G>::value;
+__global__ void __launch_bounds__((FullWaves<G, PAGED>::value * 64)) k_attn_full(AttnParams P) {
+  constexpr int NW = FullWaves<G, PAGED>::value;
   __shared__ float lds[lds_floats<G, NW>()];
   __shared__ int s_next;
   int count = P.worklist[0];
@@ -828,7 +828,7 @@ int full_grid(const AttnParams& p) {
 template <int G, bool PAGED>
 int launch_full_t(const AttnParams& p, hipStream_t s) {
   dim3 grid(full_grid(p));
-  hipLaunchKernelGGL((k_attn_full<G, PAGED>), grid, dim3(FullWaves<G>::value * 64), 0, s, p);
+  hipLaunchKernelGGL((k_attn_full<G, PAGED>), grid, dim3(FullWaves<G, PAGED>::value * 64), 0, s, p);
   return hipGetLastError() == hipSuccess ? ODA_OK : ODA_E_LAUNCH;
 }
 
