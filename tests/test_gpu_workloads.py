@@ -95,3 +95,23 @@ def test_workload5_4k_all_flagged_whole_sequence_units():
     run_workload("5-4k", steps,
                  lambda wl, j: [(27, 31, 3)],
                  lambda wl, j: [(27, 0, 1), (13, 17, 4), (27, 31, 7)])
+
+
+def test_paged_units_longer_than_one_table_window():
+    """A paged cache of 2-row blocks with all 32 sequences flagged at 20K
+    positions: the policy makes each (sequence, KV head) one unit of 20,001
+    keys (10,001 blocks), more block-table entries than the full kernel's
+    shared-memory copy holds at once (3,072 with 8 waves), so each unit is
+    streamed in four windows of entries, the last one ragged."""
+    B = 32
+    t0 = np.full(B, 20000, dtype=np.int64)
+    wl = synth.Workload("paged-20k-b32-block2", 2, 16, 8, 128, B, t0, 2, seed=61, head_seed=161, layout="paged",
+                        block_size=2)
+    bp = BigProblem(wl, head_perturb=True)
+    rec = bp.run_step(0, 0.0, _force(B, full=range(B)))
+    assert [ns for (_, ns, _) in rec["worklist"]] == [1] * B
+    n_loc, n_full = bp.check(rec, [(1, 3, 2), (0, 30, 7)], [(1, 0, 0), (1, 31, 5), (0, 17, 3)])
+    assert n_loc >= 2 and n_full >= 3
+    print(f"{wl.name}: {n_loc} local and {n_full} full outputs compared", flush=True)
+    del bp
+    torch.cuda.empty_cache()
