@@ -328,21 +328,34 @@ def metric_label(wl) -> str:
 
 
 def calibrated_theta(S, K, torch):
-    """theta for the workload's rate from an all-local pass over the K steps
-    (theta = +inf), or the workload's fixed theta; the state is reset."""
-    from conditional_sparse_attention_amd.step import tune_theta
+    """theta for the workload's rate, or the workload's fixed theta; the
+    state is reset.  An all-local pass over the K steps (theta = +inf) gives
+    a first threshold, then passes of the ODA step itself re-tune it until
+    its own trajectory sends round(rate * B * K) decisions to the full
+    branch (match_rate).  Returns (theta, calibrated, passes, record)."""
+    from conditional_sparse_attention_amd.step import match_rate, tune_theta
     wl = S.wl
     if wl.rate is None:
-        return float(wl.theta), False
-    S.set_theta(math.inf)
+        return float(wl.theta), False, 0, None
+    B = wl.batch
+    scores = torch.zeros((K, B), dtype=torch.float32, device="cuda")
+    flags = torch.zeros((K, B), dtype=torch.uint8, device="cuda")
+
+    def run_pass(theta):
+        S.set_theta(theta)
+        S.reset()
+        for j in range(K):
+            S.plans[j].run()
+            scores[j].copy_(S.state.score)
+            flags[j].copy_(S.state.flag)
+        torch.cuda.synchronize()
+        return scores.cpu().numpy(), flags.cpu().numpy()
+
+    theta0 = tune_theta(run_pass(math.inf)[0], wl.rate)
+    theta, n, k, passes = match_rate(run_pass, theta0, wl.rate)
     S.reset()
-    scores = torch.zeros((K, wl.batch), dtype=torch.float32, device="cuda")
-    for j in range(K):
-        S.plans[j].run()
-        scores[j].copy_(S.state.score)
-    torch.cuda.synchronize()
-    S.reset()
-    return tune_theta(scores.cpu().numpy(), wl.rate), True
+    return theta, True, 1 + passes, {"all_local_theta": theta0, "trajectory_passes": passes,
+                                     "full_decisions": n, "target_full_decisions": k}
 
 
 def run(args, wl, stream, torch):
@@ -358,7 +371,7 @@ def run(args, wl, stream, torch):
     K = args.steps
 
     # ---- calibration: all-local scores -> theta for the target rate
-    theta, calibrated = calibrated_theta(S, K, torch)
+    theta, calibrated, tune_passes, tuning = calibrated_theta(S, K, torch)
     S.set_theta(theta)
 
     # ---- warm-up
@@ -447,6 +460,7 @@ def run(args, wl, stream, torch):
         "config": {"workload": wl.name, "layers": L, "batch": B, "context": ctx, "q_heads": Hq,
                    "kv_heads": Hkv, "head_dim": d, "kv_layout": wl.layout, "recall_rate_target": wl.rate,
                    "recall_rate_realised": realised, "theta": theta, "theta_calibrated": calibrated,
+                   "theta_tuning": tuning,
                    "tokens_per_s": round(steps_per_s * B, 1),
                    "repeats": args.repeats, "timing": "per-step hip-graph replay, median of repeats",
                    "split_graph_steps_per_s": round(1000.0 * K / split_ms, 2)},
@@ -484,7 +498,7 @@ def run(args, wl, stream, torch):
                                   "streamed once / time"}
     # dispatch windows of the split region, in this process's launch order,
     # so a kernel trace of the same command can be cut to the same launches
-    before = (K if calibrated else 0) + args.warmup + args.repeats * K
+    before = tune_passes * K + args.warmup + args.repeats * K
     out["roofline"] = {"bound": "hbm", "kernel": "k_attn_full (oda_full_attn_if)", "achieved": round(achieved, 1),
                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                        "traffic": traffic, "traffic_note": traffic_note, "avg_launch_us": round(avg_us, 2),
@@ -1139,27 +1153,27 @@ def decoder_bench(args, wl, stream, torch):
     """The workload's batch and contexts with the decoder backbone: theta
     tuned on an all-local pass to the workload's rate, then warm graph
     replay, against the always-full baseline."""
+    from conditional_sparse_attention_amd.step import match_rate, tune_theta
     K = args.steps
     S = DecSession(wl.t0, max(K, args.warmup, 1), stream, theta=math.inf)
-    S.reset()
     scores = torch.zeros((K, wl.batch), dtype=torch.float32, device="cuda")
-    for j in range(K):
-        S.step()
-        scores[j].copy_(S.bufs.score)
-    torch.cuda.synchronize()
-    sc = np.sort(scores.cpu().numpy().reshape(-1))[::-1]
-    rate = wl.rate if wl.rate is not None else 0.0
-    k = int(round(rate * sc.size))
-    theta = float((sc[k - 1] + sc[k]) / 2) if 0 < k < sc.size else (math.inf if k == 0 else -math.inf)
-    S.plan.set_theta(theta)
-    # realised rate on an eager pass with this theta
-    S.reset()
     flags = torch.zeros((K, wl.batch), dtype=torch.uint8, device="cuda")
-    for j in range(K):
-        S.step()
-        flags[j].copy_(S.bufs.flag)
-    torch.cuda.synchronize()
-    realised = float(flags.float().mean().item())
+
+    def run_pass(theta):
+        S.plan.set_theta(theta)
+        S.reset()
+        for j in range(K):
+            S.step()
+            scores[j].copy_(S.bufs.score)
+            flags[j].copy_(S.bufs.flag)
+        torch.cuda.synchronize()
+        return scores.cpu().numpy(), flags.cpu().numpy()
+
+    # theta from an all-local pass, then re-tuned on the ODA step's own trajectory
+    rate = wl.rate if wl.rate is not None else 0.0
+    theta, n_full, _, passes = match_rate(run_pass, tune_theta(run_pass(math.inf)[0], rate), rate)
+    S.plan.set_theta(theta)
+    realised = n_full / flags.numel()
     ms = S.warm_ms(K, args.warmup, args.repeats)
     ms_af = S.warm_ms(K, args.warmup, args.repeats, always_full=True)
     sh = S.sh
@@ -1171,6 +1185,7 @@ def decoder_bench(args, wl, stream, torch):
         "config": {"workload": f"{wl.name} + {sh.name} decoder", "layers": sh.layers, "batch": wl.batch,
                    "context": int(wl.t0[0]), "hidden": sh.hidden, "mlp": sh.inter, "vocab": sh.vocab,
                    "recall_rate_target": rate, "recall_rate_realised": realised, "theta": theta,
+                   "theta_tuning_passes": 1 + passes,
                    "tokens_per_s": round(1e3 / ms * wl.batch, 1), "timing": "hip-graph replay, median of repeats"},
         "always_full": {"steps_per_s": round(1e3 / ms_af, 2), "ms_per_step": round(ms_af, 4),
                         "oda_speedup": round(ms_af / ms, 3)},
@@ -1340,26 +1355,28 @@ def hybrid_bench(args, stream, torch):
     """Hybrid backbone (6 attention + 18 recurrent layers, 8 sequences at
     32K): theta tuned on an all-local pass to the pages' hybrid call rate,
     then one graph per step, against always-full."""
+    from conditional_sparse_attention_amd.step import match_rate, tune_theta
     K = args.steps
     H = HybridSession(max(K, args.warmup, 1), stream, theta=math.inf)
     S = H.S
-    H.reset()
     scores = torch.zeros((K, H.wl.batch), dtype=torch.float32, device="cuda")
-    for j in range(K):
-        H.plans[j].run()
-        scores[j].copy_(S.state.score)
-    torch.cuda.synchronize()
-    sc = np.sort(scores.cpu().numpy().reshape(-1))[::-1]
-    k = int(round(H.wl.rate * sc.size))
-    theta = float((sc[k - 1] + sc[k]) / 2) if 0 < k < sc.size else (math.inf if k == 0 else -math.inf)
+    flags = torch.zeros((K, H.wl.batch), dtype=torch.uint8, device="cuda")
+
+    def run_pass(theta):
+        H.set_theta(theta)
+        H.reset()
+        for j in range(K):
+            H.plans[j].run()
+            scores[j].copy_(S.state.score)
+            flags[j].copy_(S.state.flag)
+        torch.cuda.synchronize()
+        return scores.cpu().numpy(), flags.cpu().numpy()
+
+    # theta from an all-local pass, then re-tuned on the ODA step's own trajectory
+    theta, n_full, _, passes = match_rate(run_pass, tune_theta(run_pass(math.inf)[0], H.wl.rate), H.wl.rate)
     H.set_theta(theta)
     H.reset()
-    flags = torch.zeros((K, H.wl.batch), dtype=torch.uint8, device="cuda")
-    for j in range(K):
-        H.plans[j].run()
-        flags[j].copy_(S.state.flag)
-    torch.cuda.synchronize()
-    realised = float(flags.float().mean().item())
+    realised = n_full / flags.numel()
     assert S.error_bits() == 0, "device error bits set"
     ms = H.warm_ms(K, args.repeats)
     ms_af = H.warm_ms(K, args.repeats, always_full=True)
@@ -1374,6 +1391,7 @@ def hybrid_bench(args, stream, torch):
                    "recurrent_layers": sh.layers, "batch": wl.batch, "context": int(wl.t0[0]),
                    "gdn_heads": sh.heads, "head_dim": sh.d, "conv_width": sh.conv_width,
                    "recall_rate_target": wl.rate, "recall_rate_realised": realised, "theta": theta,
+                   "theta_tuning_passes": 1 + passes,
                    "tokens_per_s": round(1e3 / ms * wl.batch, 1), "timing": "hip-graph per step, median of repeats"},
         "always_full": {"steps_per_s": round(1e3 / ms_af, 2), "ms_per_step": round(ms_af, 4),
                         "oda_speedup": round(ms_af / ms, 3)},

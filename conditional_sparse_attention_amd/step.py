@@ -124,3 +124,47 @@ def tune_theta(scores, rate: float) -> float:
     if k >= sc.size:
         return -math.inf
     return float((sc[k - 1] + sc[k]) / 2)
+
+
+def match_rate(run_pass, theta0: float, rate: float, max_passes: int = 12):
+    """Threshold whose own trajectory sends round(rate * n) of its n
+    decisions to the full branch.  theta0 comes from an all-local
+    calibration pass (tune_theta); once sequences take the full branch their
+    hidden states and caches change, so the later scores, and the realised
+    count, drift away from it.  run_pass(theta) runs the steps from the same
+    start state with threshold theta and returns (recall scores, flags), one
+    entry per decision.  Each further pass takes the threshold that would
+    have hit the count on the previous pass's own scores, kept strictly
+    between the thresholds found so far to send too many and too few (their
+    midpoint when it falls outside).  Returns (theta, realised count, target
+    count, passes run), theta being the first of the passes closest to the
+    target."""
+    import math
+
+    import numpy as np
+
+    theta, lo, hi = float(theta0), -math.inf, math.inf
+    best, passes = None, 0
+    while True:
+        scores, flags = run_pass(theta)
+        passes += 1
+        n = int(np.count_nonzero(flags))
+        k = int(round(rate * np.asarray(flags).size))
+        if best is None or abs(n - k) < abs(best[1] - k):
+            best = (theta, n, k)
+        if n == k or passes >= max_passes:
+            break
+        if n > k:
+            lo = max(lo, theta)
+        else:
+            hi = min(hi, theta)
+        cand = tune_theta(scores, rate)
+        inside = (cand > lo or cand == lo == -math.inf) and (cand < hi or cand == hi == math.inf)
+        if not inside:
+            if not (math.isfinite(lo) and math.isfinite(hi)):
+                break
+            cand = (lo + hi) / 2
+        if cand == theta:
+            break
+        theta = cand
+    return best[0], best[1], best[2], passes

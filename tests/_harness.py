@@ -342,13 +342,21 @@ class BigProblem:
 
     def calibrate_theta(self, steps: int, rate: float) -> float:
         """The benchmark's threshold for a target call rate: the steps run
-        all-local (theta = +inf), the threshold sends round(rate * B * steps)
-        of their scores to the full branch; then the state is reset."""
-        from conditional_sparse_attention_amd.step import tune_theta
+        all-local (theta = +inf) and the threshold sends round(rate * B *
+        steps) of their scores to the full branch; passes of the ODA step
+        then re-tune it on its own trajectory (step.match_rate); the state
+        is reset."""
+        from conditional_sparse_attention_amd.step import match_rate, tune_theta
         B = self.wl.batch
-        scores = [self.run_step(j, math.inf, np.full(B, -1, np.int8))["score"] for j in range(steps)]
+
+        def run_pass(theta):
+            self.reset()
+            recs = [self.run_step(j, theta, np.full(B, -1, np.int8)) for j in range(steps)]
+            return np.stack([r["score"] for r in recs]), np.stack([r["flag"] for r in recs])
+
+        theta = match_rate(run_pass, tune_theta(run_pass(math.inf)[0], rate), rate)[0]
         self.reset()
-        return tune_theta(np.concatenate(scores), rate)
+        return theta
 
     def run_step(self, j: int, theta: float, force) -> dict:
         pr, wl = self.pr, self.wl

@@ -5,9 +5,10 @@ policy and comparing actions, outputs and committed state
 ([On-Demand Attention notes §3.3, last paragraph; §4]).  Here the policy is
 the benchmark's: the workload's random Xavier head, every decision taken by
 the head, and the threshold tuned to the workload's call rate on an
-all-local calibration pass over the same steps (41.6% for the 16K batch of
-8, 12.5% for the 128K batch of 4 with its far needles, 47% for the
-Qwen3-8B-shaped 64K batch of 16).  The GPU trajectory drives; for each of
+all-local calibration pass over the same steps and then re-tuned on the ODA
+step's own trajectory until it sends that share of the decisions to the
+full branch (41.6% for the 16K batch of 8, 12.5% for the 128K batch of 4
+with its far needles, 47% for the Qwen3-8B-shaped 64K batch of 16).  The GPU trajectory drives; for each of
 8 steps the oracle checks
 
   * every recall score, every flag outside the tie band, the work list, the
@@ -63,9 +64,11 @@ def test_tuned_rate(trajectory):
     key, wl, bp, recs, flags = trajectory
     fl = np.array(flags)
     n = int(fl.sum())
-    print(f"{wl.name}: {n} of {fl.size} decisions full (target {wl.rate})", flush=True)
-    # the trajectory exercises both branches
+    k = round(wl.rate * fl.size)
+    print(f"{wl.name}: {n} of {fl.size} decisions full (target {wl.rate}: {k})", flush=True)
+    # the trajectory exercises both branches, at the rate the threshold was tuned to
     assert 0 < n < fl.size
+    assert abs(n - k) <= 1 + k // 20
 
 
 def test_tuned_local_outputs(trajectory):
