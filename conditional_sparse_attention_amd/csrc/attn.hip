@@ -71,21 +71,23 @@ constexpr int kLocalWideMax = 2;
 #define ODA_FULL_U 2
 #endif
 // Full kernel shape per group size: G = 2 (the 16/8-head models) runs 12
-// waves (3 per SIMD) with a 3-stage ring; G = 1 and G = 4 keep more state per
-// lane and run 8 waves with a 4-stage ring, which keeps a similar number of
-// bytes in flight per CU without spilling.  The paged layout holds more per
-// row in flight (a block and an address), so its rings are a stage shorter
-// (G = 2: 2 stages; a 3-stage ring spills at 12 waves and measured slower at
-// 8), and G = 2 runs 8 waves there: 1-4% faster per launch than 12 (e.g.
-// 27.1 / 28.2 us at 8 flagged 4K sequences of 32, 88.4 / 89.7 us at one
-// flagged 128K sequence).
+// waves (3 per SIMD) with a 3-stage ring; G = 4 keeps twice the query and
+// accumulator state per lane and runs 12 waves with a 2-stage ring (165
+// registers: 4.6-5.9% faster per launch than 8 waves with 4 stages at 8
+// flagged 64K sequences, e.g. 355.9 / 372.9 us at 16 x 64K, the same at 2-4
+// flagged; 3 stages spill at 12 waves); G = 1 runs 8 waves with a 4-stage
+// ring.  The paged layout holds more per row in flight (a block and an
+// address), so its rings are a stage shorter (G = 2: 2 stages; a 3-stage
+// ring spills at 12 waves and measured slower at 8), and G = 2 runs 8 waves
+// there: 1-4% faster per launch than 12 (e.g. 27.1 / 28.2 us at 8 flagged 4K
+// sequences of 32, 88.4 / 89.7 us at one flagged 128K sequence).
 template <int G, bool PAGED>
 struct FullWaves {
-  static constexpr int value = G == 2 ? (PAGED ? 8 : ODA_FULL_WAVES_SMALL_G) : 8;
+  static constexpr int value = G == 2 ? (PAGED ? 8 : ODA_FULL_WAVES_SMALL_G) : (G == 4 && !PAGED ? 12 : 8);
 };
 template <int G, bool PAGED>
 struct FullDepth {
-  static constexpr int value = PAGED ? (G == 2 ? 2 : 3) : (G == 2 ? ODA_FULL_DEPTH : 4);
+  static constexpr int value = PAGED ? (G == 2 ? 2 : 3) : (G == 2 ? ODA_FULL_DEPTH : (G == 4 ? 2 : 4));
 };
 
 __device__ __forceinline__ float dot8_bf16(const uint4 a, const uint4 b) {
